@@ -1,0 +1,272 @@
+"""CPU oracle for attention over a reduced-precision (FP16 or int8 "q8") K/V cache.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The product
+path (``quantized_kv_cache_q8_amd`` and its HIP library) never does, and this
+module imports nothing from it.
+
+Plain, slow, obviously correct NumPy.  Attention is computed in float64 on the
+dequantised cache values; the quantiser is computed in float32 (the precision in
+which the GPU kernel takes the same integer decisions).
+
+Sources (web pages; cited by title and section):
+  [P1] PR #3084 "FP16 K/V cache by default, int8 with --kv-q8 (262144 fits a
+       16 GiB card)": sections Summary, What changed, Extra Notes.
+  [P3] PR #711 "kv: --kv k8v4 streams with --kv-resident": sections What, How.
+
+Readings where the pages are silent (all listed in the design doc):
+  * fp16(.) is IEEE round-to-nearest-even; rint is round-half-to-even.
+  * ``x / scale`` divides by the *stored* fp16 scale widened to fp32, with a
+    true IEEE fp32 division (not a reciprocal multiply).
+  * a group whose scale is zero stores code 0 (x/0 is otherwise undefined).
+  * group g of a head row holds dims [64g, 64g+64) of one token, K and V separately.
+  * query head q reads kv head q // G, G = n_q_heads / n_kv_heads.
+  * the prompt chunk rounds its queries to fp16 before Q K^T, as the GEMMs read
+    halves; row i of a chunk at position pos0 attends keys [0, pos0 + i].
+
+Parity pins: every function here is checked by ``tests/test_oracle_*.py``
+against closed forms, invariants, brute force with exact rational arithmetic and
+independent library routines (torch's CPU scaled-dot-product attention).  No
+function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+GROUP = 64          # dims per fp16 scale  [P1, Summary]
+QMAX = 127          # symmetric int8 range [P1, What changed]
+FMT_F16, FMT_Q8 = 0, 1
+
+
+# ----------------------------------------------------------------------------
+# Storage cost
+# ----------------------------------------------------------------------------
+def cache_bytes(fmt: int, kvh: int, cap: int, hd: int, part: int) -> int:
+    """Bytes of one K (or one V) array of one layer.
+
+    part 0: values (fp16, 2 B each) or int8 codes (1 B each); part 1: the fp16
+    scales of the q8 format (one 2-B scale per 64 values, [P1, Summary]); the
+    FP16 format has no scales.
+    """
+    n = kvh * cap * hd
+    if part == 0:
+        return 2 * n if fmt == FMT_F16 else n
+    return 0 if fmt == FMT_F16 else 2 * (n // GROUP)
+
+
+# ----------------------------------------------------------------------------
+# O1 / O2: writing a cell (quantise-on-write, FP16 store)
+# ----------------------------------------------------------------------------
+def quantize_q8(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Quantise-on-write of [P1, What changed]: per 64-dim group of a head row,
+    scale = fp16(max|x| / 127) and code = clamp(rint(x / scale), -127, 127).
+
+    x: float32 [..., HD], HD a multiple of 64.
+    returns (codes int8 [..., HD], scales float16 [..., HD // 64]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    hd = x.shape[-1]
+    assert hd % GROUP == 0
+    g = x.reshape(*x.shape[:-1], hd // GROUP, GROUP)
+    amax = np.abs(g).max(axis=-1)                        # exact in float32
+    s16 = (amax / np.float32(QMAX)).astype(np.float16)   # fp32 division, then RNE to fp16
+    s32 = s16.astype(np.float32)[..., None]              # the stored scale, widened
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = g / s32                                      # IEEE fp32 division
+    r = np.where(s32 == 0, np.float32(0), r)             # all-zero (or underflowed) group
+    codes = np.clip(np.rint(r), -QMAX, QMAX).astype(np.int8)
+    return codes.reshape(x.shape), s16
+
+
+def store_f16(x: np.ndarray) -> np.ndarray:
+    """FP16 cache write of [P1, Summary]: IEEE round-to-nearest-even to binary16."""
+    return np.asarray(x, dtype=np.float32).astype(np.float16)
+
+
+# ----------------------------------------------------------------------------
+# Cache (one layer, one session): the data structure of [P1, Summary / What changed]
+# ----------------------------------------------------------------------------
+class Cache:
+    """One session's cache for one layer.
+
+    F16: k, v float16 [kvh][cap][hd].
+    Q8 : k, v int8 [kvh][cap][hd] plus k_scale, v_scale float16 [kvh][cap][hd/64]
+         (scale arrays kept beside the code arrays, [P1, What changed]; codes and
+         scales are separate runs of bytes, [P3, How]).
+    """
+
+    def __init__(self, fmt: int, kvh: int, cap: int, hd: int):
+        self.fmt, self.kvh, self.cap, self.hd = fmt, kvh, cap, hd
+        if fmt == FMT_F16:
+            self.k = np.zeros((kvh, cap, hd), np.float16)
+            self.v = np.zeros((kvh, cap, hd), np.float16)
+            self.k_scale = self.v_scale = None
+        else:
+            self.k = np.zeros((kvh, cap, hd), np.int8)
+            self.v = np.zeros((kvh, cap, hd), np.int8)
+            self.k_scale = np.zeros((kvh, cap, hd // GROUP), np.float16)
+            self.v_scale = np.zeros((kvh, cap, hd // GROUP), np.float16)
+
+    def append(self, pos: int, xk: np.ndarray, xv: np.ndarray) -> bool:
+        """Write n_tok new cells at rows [pos, pos + n_tok).  xk, xv: float32
+        [n_tok][kvh][hd].  Returns False, writing nothing, when the rows do not fit."""
+        n = xk.shape[0]
+        if pos < 0 or pos + n > self.cap:
+            return False
+        for src, dst, dsc in ((xk, "k", "k_scale"), (xv, "v", "v_scale")):
+            rows = np.transpose(np.asarray(src, np.float32), (1, 0, 2))  # [kvh][n][hd]
+            if self.fmt == FMT_F16:
+                getattr(self, dst)[:, pos:pos + n] = store_f16(rows)
+            else:
+                c, s = quantize_q8(rows)
+                getattr(self, dst)[:, pos:pos + n] = c
+                getattr(self, dsc)[:, pos:pos + n] = s
+        return True
+
+    # O3: what the decode reads -- exact dequantised values in float64
+    def dequant(self, which: str, length: int) -> np.ndarray:
+        """float64 [kvh][length][hd].  q8: code * scale, which is exact (a 7-bit
+        integer times an 11-bit significand); F16: the stored halves."""
+        vals = getattr(self, which)[:, :length]
+        if self.fmt == FMT_F16:
+            return vals.astype(np.float64)
+        sc = getattr(self, which + "_scale")[:, :length].astype(np.float64)
+        return vals.astype(np.float64) * np.repeat(sc, GROUP, axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# O4: compaction to the FP16 [kvh][P][HD] copy the prompt GEMMs read
+# ----------------------------------------------------------------------------
+def compact_f16(cache: Cache, P: int) -> tuple[np.ndarray, np.ndarray]:
+    """[P1, Extra Notes]: the prompt chunk's GEMMs read an FP16 [kvh][P][HD] copy
+    of the cache.  F16: rows 0..P-1 copied (a stride change only).  q8:
+    fp16(float(code) * float(scale)), one rounding of an exact fp32 product."""
+    out = []
+    for which in ("k", "v"):
+        vals = getattr(cache, which)[:, :P]
+        if cache.fmt == FMT_F16:
+            out.append(vals.copy())
+        else:
+            sc = getattr(cache, which + "_scale")[:, :P].astype(np.float32)
+            prod = vals.astype(np.float32) * np.repeat(sc, GROUP, axis=-1)
+            out.append(prod.astype(np.float16))
+    return out[0], out[1]
+
+
+# ----------------------------------------------------------------------------
+# O5: decode attention, the plain definition
+# ----------------------------------------------------------------------------
+def decode_attn(q: np.ndarray, K: np.ndarray, V: np.ndarray, length: int,
+                sm_scale: float) -> np.ndarray:
+    """Attention of one new token over the first ``length`` cached cells.
+
+    q: [nqh][hd] (float32 values); K, V: float64 [kvh][>=length][hd] dequantised
+    cache; returns float64 [nqh][hd].  length == 0 returns zeros.
+    """
+    nqh, hd = q.shape
+    kvh = K.shape[0]
+    G = nqh // kvh
+    out = np.zeros((nqh, hd))
+    if length == 0:
+        return out
+    sm = float(np.float32(sm_scale))
+    for qh in range(nqh):
+        h = qh // G
+        z = sm * (K[h, :length] @ q[qh].astype(np.float64))
+        w = np.exp(z - z.max())
+        out[qh] = (w @ V[h, :length]) / w.sum()
+    return out
+
+
+# ----------------------------------------------------------------------------
+# O6: the same result by split-K partials and a log-sum-exp merge
+# ----------------------------------------------------------------------------
+def decode_partials(q, K, V, length, sm_scale, T):
+    """Per split j (tokens [jT, min((j+1)T, length))): normalised partial output
+    o_j and lse_j = m_j + ln(l_j).  An empty split has lse = -inf and o = 0.
+    Returns (o float64 [nqh][S][hd], lse float64 [nqh][S]), S = ceil(length / T)."""
+    nqh, hd = q.shape
+    kvh = K.shape[0]
+    G = nqh // kvh
+    S = max(1, -(-length // T))
+    o = np.zeros((nqh, S, hd))
+    lse = np.full((nqh, S), -np.inf)
+    sm = float(np.float32(sm_scale))
+    for qh in range(nqh):
+        h = qh // G
+        for j in range(S):
+            a, b = j * T, min((j + 1) * T, length)
+            if a >= b:
+                continue
+            z = sm * (K[h, a:b] @ q[qh].astype(np.float64))
+            m = z.max()
+            w = np.exp(z - m)
+            l = w.sum()
+            o[qh, j] = (w @ V[h, a:b]) / l
+            lse[qh, j] = m + math.log(l)
+    return o, lse
+
+
+def merge_partials(o: np.ndarray, lse: np.ndarray) -> np.ndarray:
+    """out = sum_j exp(lse_j - L) o_j with L = log sum_j exp(lse_j); empty splits
+    (lse = -inf) weigh zero; all-empty gives zeros."""
+    nqh, S, hd = o.shape
+    out = np.zeros((nqh, hd))
+    for qh in range(nqh):
+        m = lse[qh].max()
+        if m == -np.inf:
+            continue
+        w = np.exp(lse[qh] - m)
+        L = m + math.log(w.sum())
+        out[qh] = (np.exp(lse[qh] - L)[:, None] * o[qh]).sum(axis=0)
+    return out
+
+
+def decode_attn_splitk(q, K, V, length, sm_scale, T):
+    return merge_partials(*decode_partials(q, K, V, length, sm_scale, T))
+
+
+# ----------------------------------------------------------------------------
+# O7: prompt-chunk attention, the plain definition
+# ----------------------------------------------------------------------------
+def prefill_attn(q: np.ndarray, K16: np.ndarray, V16: np.ndarray, pos0: int,
+                 sm_scale: float, rows=None) -> np.ndarray:
+    """Causal attention of a prompt chunk over the FP16 compacted copy.
+
+    q: float32 [n_tok][nqh][hd] (rounded to fp16 here, as the GEMMs read halves);
+    K16, V16: float16 [kvh][P][hd] with P >= pos0 + n_tok.  Row i (absolute
+    position pos0 + i) attends keys [0, pos0 + i].  ``rows`` selects a subset of
+    chunk rows (all by default).  Returns float64 [len(rows)][nqh][hd].
+    """
+    n_tok, nqh, hd = q.shape
+    kvh = K16.shape[0]
+    G = nqh // kvh
+    rows = np.arange(n_tok) if rows is None else np.asarray(rows)
+    sm = float(np.float32(sm_scale))
+    Q16 = np.asarray(q, np.float32).astype(np.float16).astype(np.float64)
+    out = np.zeros((len(rows), nqh, hd))
+    for qh in range(nqh):
+        h = qh // G
+        for r, i in enumerate(rows):
+            n_keys = pos0 + int(i) + 1
+            Kh = K16[h, :n_keys].astype(np.float64)
+            z = sm * (Kh @ Q16[i, qh])
+            w = np.exp(z - z.max())
+            out[r, qh] = (w @ V16[h, :n_keys].astype(np.float64)) / w.sum()
+    return out
+
+
+# ----------------------------------------------------------------------------
+# O8: brute force on tiny inputs (scalar loops, math.exp / math.fsum)
+# ----------------------------------------------------------------------------
+def brute_attention_row(qv, Krows, Vrows, sm_scale):
+    """One query vector against explicit key/value row lists, scalar Python."""
+    sm = float(np.float32(sm_scale))
+    z = [sm * math.fsum(float(a) * float(b) for a, b in zip(qv, kr)) for kr in Krows]
+    m = max(z)
+    w = [math.exp(t - m) for t in z]
+    l = math.fsum(w)
+    hd = len(Vrows[0])
+    return [math.fsum(w[t] * float(Vrows[t][d]) for t in range(len(w))) / l for d in range(hd)]

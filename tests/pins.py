@@ -1,0 +1,388 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Each ``pin_*`` takes the oracle function(s) under test as arguments and raises
+AssertionError on a mismatch, so that the same pins run against the oracle
+(tests/test_oracle_*.py) and against planted mistakes
+(tests/test_oracle_mutations.py), which must each fail at least one pin.
+
+What pins what:
+  * quantiser: hand-derived worked examples; brute force with exact rational
+    arithmetic (fp32 division and fp16 rounding written from the IEEE
+    definition); |code| <= 127 and max |code| = 127 for normal scales; the
+    reconstruction bound |code*s - x| <= s*(1/2 + 2^-17); sign symmetry;
+    power-of-two scaling; an exhaustive sweep over every positive finite fp16
+    scale; stored cases where a reciprocal multiply differs.
+  * byte accounting: the 12.0 / 6.0 / 3.1 GiB of PR #3084, section Summary.
+  * decode: torch's CPU scaled_dot_product_attention in float64 (a library
+    routine); len = 1, q = 0, constant V, V*2, token permutation; scalar brute
+    force; the FP16 cache equals fp32 attention on fp16-rounded K/V.
+  * split-K: the log-sum-exp merge equals single-pass softmax for any split
+    size, with and without padded empty splits.
+  * prefill: torch's causal SDPA over the whole sequence (rows pos0..);
+    a one-token chunk equals decode; future keys do not affect a row; brute force.
+  * compaction: the exact rational product rounded once to fp16.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from _exact import f16, quant_group_exact
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _group(vals):
+    x = np.zeros(64, np.float32)
+    x[: len(vals)] = np.asarray(vals, np.float32)
+    return x
+
+
+# ----------------------------------------------------------------------------
+# quantiser
+# ----------------------------------------------------------------------------
+def pin_quant_worked_examples(quant):
+    gold = _load("quant_worked_examples.json")
+    x = np.stack([_group(g["x"]) for g in gold["groups"]])      # [n][64], one group each
+    codes, scales = quant(x)
+    for i, g in enumerate(gold["groups"]):
+        want = np.zeros(64, np.int8)
+        want[: len(g["codes"])] = g["codes"]
+        assert int(scales[i].view(np.uint16)[0]) == int(g["scale_bits"], 16), g["label"]
+        assert np.array_equal(codes[i], want), g["label"]
+    # two groups in one head row keep separate scales (group = 64 contiguous dims)
+    row = np.concatenate([_group(gold["groups"][0]["x"]), _group(gold["groups"][1]["x"])])
+    c, s = quant(row[None])
+    assert s.shape[-1] == 2
+    assert [int(b) for b in s.view(np.uint16)[0]] == [0x3C00, 0x4000]
+    assert np.array_equal(c[0, :64], codes[0]) and np.array_equal(c[0, 64:], codes[1])
+
+
+def _random_groups(seed, n):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((n, 64), dtype=np.float32)
+    x *= np.exp2(r.integers(-20, 12, size=(n, 1))).astype(np.float32)   # normal and subnormal scales
+    x[r.random((n, 64)) < 0.05] *= np.float32(20)                        # outliers
+    x[:3] = 0
+    x[1, 5] = np.float32(-1e-30)       # scale underflows to 0
+    x[2, :] = np.float32(7.0)          # constant group
+    return x
+
+
+def pin_quant_brute_force(quant, n=300, n_exhaustive=8):
+    x = _random_groups(1, n)
+    codes, scales = quant(x)
+    for i in range(n):
+        s, c = quant_group_exact(x[i], brute=(i < n_exhaustive))
+        assert Fraction(float(scales[i, 0])) == s, (i, float(scales[i, 0]), float(s))
+        assert codes[i].tolist() == c, i
+
+
+def pin_quant_invariants(quant):
+    x = _random_groups(2, 4000)
+    codes, scales = quant(x)
+    c = codes.astype(np.int32)
+    s = scales[:, 0].astype(np.float64)
+    assert np.abs(c).max() <= 127
+    normal = s >= 2.0 ** -14
+    assert normal.sum() > 1000
+    assert (np.abs(c[normal]).max(-1) == 127).all()
+    err = np.abs(c * s[:, None] - x.astype(np.float64))
+    assert (err[normal] <= s[normal, None] * (0.5 + 2.0 ** -17)).all()
+    # sign symmetry
+    cn, sn = quant(-x)
+    assert np.array_equal(cn, -codes) and np.array_equal(sn.view(np.uint16), scales.view(np.uint16))
+    # power-of-two scaling while the scale stays a normal fp16 value
+    sel = (s >= 2.0 ** -12) & (s <= 2.0 ** 10)
+    c2, s2 = quant(x[sel] * np.float32(4))
+    assert np.array_equal(c2, codes[sel])
+    assert np.array_equal(s2.astype(np.float64), 4 * scales[sel].astype(np.float64))
+
+
+def pin_quant_scale_sweep(quant):
+    """Every positive finite fp16 value h: groups with amax = fl32(127 h) and its
+    fp32 neighbours, holding +amax, -amax, amax/3 and a small value."""
+    h = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float32)
+    h = h[:-1]                                      # fp32 neighbours of 127*65504 would overflow fp16
+    amax = (h * np.float32(127)).astype(np.float32)
+    amaxes = np.concatenate([amax, np.nextafter(amax, np.float32(np.inf)),
+                             np.nextafter(amax, np.float32(0))])
+    x = np.zeros((amaxes.size, 64), np.float32)
+    x[:, 0] = amaxes
+    x[:, 1] = -amaxes
+    x[:, 2] = amaxes / np.float32(3)
+    x[:, 3] = amaxes * np.float32(0.0123)
+    codes, scales = quant(x)
+    assert np.abs(codes.astype(np.int32)).max() <= 127
+    s = scales[:, 0].astype(np.float64)
+    normal = s >= 2.0 ** -14
+    assert (codes[normal, 0] == 127).all() and (codes[normal, 1] == -127).all()
+    # exact check of the scale and the four codes on a strided subset of the sweep
+    for i in range(0, amaxes.size, 41):
+        se, ce = quant_group_exact(x[i, :4].tolist() + [0.0])
+        assert Fraction(float(scales[i, 0])) == se, i
+        assert codes[i, :4].tolist() == ce[:4], i
+
+
+def pin_quant_recip_traps(quant):
+    gold = _load("recip_trap_cases.json")
+    x = np.array([[int(b, 16) for b in g] for g in gold["groups_f32_bits"]], np.uint32).view(np.float32)
+    assert len(x) >= 4
+    codes, scales = quant(x)
+    for i in range(len(x)):
+        s, c = quant_group_exact(x[i])
+        assert Fraction(float(scales[i, 0])) == s
+        assert codes[i].tolist() == c, i
+
+
+QUANT_PINS = [pin_quant_worked_examples, pin_quant_brute_force, pin_quant_invariants,
+              pin_quant_scale_sweep, pin_quant_recip_traps]
+
+
+# ----------------------------------------------------------------------------
+# byte accounting
+# ----------------------------------------------------------------------------
+def pin_cache_bytes_pages(cache_bytes, FMT_F16, FMT_Q8):
+    gold = _load("cache_bytes_pr3084.json")
+    cells = gold["cells"]
+    gib = float(2 ** 30)
+    # 12.0 GiB of fp32 at 262144 cells fixes the values per cell: 12288
+    vals_per_cell = round(gold["gib_fp32"] * gib / cells / 4)
+    assert vals_per_cell * cells * 4 == gold["gib_fp32"] * gib
+    # any factorisation layers * 2 (K, V) * kvh * hd of that count; here 6 * 2 * 8 * 128
+    layers, kvh, hd = 6, 8, 128
+    assert layers * 2 * kvh * hd == vals_per_cell
+
+    def total(fmt):
+        return layers * 2 * (cache_bytes(fmt, kvh, cells, hd, 0) + cache_bytes(fmt, kvh, cells, hd, 1))
+
+    assert total(FMT_F16) == gold["gib_fp16"] * gib
+    assert round(total(FMT_Q8) / gib, gold["printed_decimals"]) == gold["gib_q8"]
+    assert cache_bytes(FMT_F16, kvh, cells, hd, 1) == 0
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+def _sdpa_decode(q, K, V, length, sm_scale, dtype=torch.float64):
+    """torch's CPU SDPA, one query position, GQA by kv-head repetition."""
+    if length == 0:
+        return np.zeros(q.shape)
+    qt = torch.from_numpy(np.asarray(q, np.float64)).to(dtype)[None, :, None, :]     # [1][nqh][1][hd]
+    kt = torch.from_numpy(np.asarray(K[:, :length], np.float64)).to(dtype)[None]      # [1][kvh][L][hd]
+    vt = torch.from_numpy(np.asarray(V[:, :length], np.float64)).to(dtype)[None]
+    o = F.scaled_dot_product_attention(qt, kt, vt, scale=float(np.float32(sm_scale)), enable_gqa=True)
+    return o[0, :, 0, :].double().numpy()
+
+
+def _decode_case(seed, kvh, G, hd, L, outliers=True):
+    r = np.random.default_rng(seed)
+    K = r.standard_normal((kvh, L, hd))
+    V = r.standard_normal((kvh, L, hd))
+    if outliers:
+        K[:, :, 3] *= 20
+        V[:, :, 7] *= 20
+    q = r.standard_normal((kvh * G, hd)).astype(np.float32)
+    return q, K, V
+
+
+def pin_decode_sdpa(decode):
+    for seed, (kvh, G, hd, L, length) in enumerate(
+            [(2, 2, 128, 70, 70), (1, 4, 64, 33, 17), (3, 1, 128, 9, 9), (2, 4, 128, 300, 257)]):
+        q, K, V = _decode_case(seed, kvh, G, hd, L)
+        sm = 1 / math.sqrt(hd)
+        got = decode(q, K, V, length, sm)
+        ref = _sdpa_decode(q, K, V, length, sm)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), np.abs(got - ref).max()
+
+
+def pin_decode_closed_forms(decode):
+    q, K, V = _decode_case(10, 2, 2, 128, 40)
+    sm = 0.125
+    # one cached cell: the output is that cell's V row, exactly
+    out = decode(q, K, V, 1, sm)
+    assert np.array_equal(out, np.repeat(V[:, 0], 2, axis=0))
+    # zero query: uniform weights, the mean of the V rows
+    out = decode(np.zeros_like(q), K, V, 40, sm)
+    assert np.allclose(out, np.repeat(V.mean(axis=1), 2, axis=0), rtol=1e-13, atol=1e-13)
+    # constant V
+    Vc = np.full_like(V, 3.25)
+    assert np.allclose(decode(q, K, Vc, 40, sm), 3.25, rtol=1e-14, atol=0)
+    # V * 2 => out * 2 (exact in binary arithmetic)
+    assert np.array_equal(decode(q, K, 2 * V, 40, sm), 2 * decode(q, K, V, 40, sm))
+    # token permutation invariance
+    perm = np.random.default_rng(3).permutation(40)
+    a = decode(q, K, V, 40, sm)
+    b = decode(q, K[:, perm], V[:, perm], 40, sm)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
+    # empty cache gives zeros
+    assert not decode(q, K, V, 0, sm).any()
+    # cells beyond length are ignored
+    K2, V2 = K.copy(), V.copy()
+    K2[:, 30:] = 1e3
+    V2[:, 30:] = -1e3
+    assert np.array_equal(decode(q, K, V, 30, sm), decode(q, K2, V2, 30, sm))
+
+
+def pin_decode_brute(decode, brute_row):
+    q, K, V = _decode_case(20, 2, 2, 8, 12)
+    sm = 0.3
+    for length in (1, 5, 12):
+        out = decode(q, K, V, length, sm)
+        for qh in range(4):
+            h = qh // 2
+            ref = brute_row(q[qh], K[h, :length], V[h, :length], sm)
+            assert np.allclose(out[qh], ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_f16_cache_equals_fp32_attention(decode, Cache, FMT_F16):
+    """An FP16 cache gives the attention that fp32 arithmetic gives on K/V
+    rounded to fp16 (torch CPU SDPA in float32)."""
+    kvh, G, hd, L = 2, 4, 128, 500
+    r = np.random.default_rng(30)
+    xk = r.standard_normal((L, kvh, hd), dtype=np.float32)
+    xv = r.standard_normal((L, kvh, hd), dtype=np.float32)
+    xk[:, :, 11] *= 20
+    cache = Cache(FMT_F16, kvh, 512, hd)
+    assert cache.append(0, xk, xv)
+    q = r.standard_normal((kvh * G, hd), dtype=np.float32)
+    got = decode(q, cache.dequant("k", L), cache.dequant("v", L), L, 1 / math.sqrt(hd))
+    k16 = np.transpose(xk.astype(np.float16), (1, 0, 2))
+    v16 = np.transpose(xv.astype(np.float16), (1, 0, 2))
+    ref = _sdpa_decode(q, k16.astype(np.float32), v16.astype(np.float32), L, 1 / math.sqrt(hd),
+                       dtype=torch.float32)
+    assert np.allclose(got, ref, rtol=2e-5, atol=2e-5), np.abs(got - ref).max()
+
+
+DECODE_PINS = [pin_decode_sdpa, pin_decode_closed_forms]
+
+
+# ----------------------------------------------------------------------------
+# split-K + merge
+# ----------------------------------------------------------------------------
+def pin_splitk_identity(decode, partials, merge):
+    q, K, V = _decode_case(40, 2, 4, 64, 97)
+    sm = 0.2
+    ref = decode(q, K, V, 97, sm)
+    for T in (1, 3, 16, 32, 96, 97, 200):
+        o, lse = partials(q, K, V, 97, sm, T)
+        assert o.shape[1] == -(-97 // T)
+        got = merge(o, lse)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), T
+    # padded empty splits (lse = -inf, o = 0) weigh nothing
+    o, lse = partials(q, K, V, 97, sm, 16)
+    pad = 5
+    o2 = np.concatenate([o, np.zeros((o.shape[0], pad, o.shape[2]))], axis=1)
+    l2 = np.concatenate([lse, np.full((lse.shape[0], pad), -np.inf)], axis=1)
+    assert np.allclose(merge(o2, l2), ref, rtol=1e-12, atol=1e-12)
+    # a merge of a single split is that split's partial
+    o, lse = partials(q, K, V, 97, sm, 97)
+    assert np.allclose(merge(o, lse), o[:, 0], rtol=1e-14, atol=1e-14)
+    # partial lse is the log of the split's softmax denominator
+    o, lse = partials(q, K, V, 10, sm, 10)
+    for qh in range(o.shape[0]):
+        z = float(np.float32(sm)) * (K[qh // 4, :10] @ q[qh].astype(np.float64))
+        assert abs(lse[qh, 0] - math.log(math.fsum(math.exp(t) for t in z))) < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# prefill
+# ----------------------------------------------------------------------------
+def _prefill_case(seed, kvh, G, hd, pos0, n_tok):
+    r = np.random.default_rng(seed)
+    P = pos0 + n_tok
+    K16 = r.standard_normal((kvh, P, hd)).astype(np.float16)
+    V16 = r.standard_normal((kvh, P, hd)).astype(np.float16)
+    K16[:, :, 5] *= 8
+    q = r.standard_normal((n_tok, kvh * G, hd)).astype(np.float32)
+    return q, K16, V16
+
+
+def pin_prefill_sdpa_causal(prefill):
+    """Full-sequence causal SDPA (top-left aligned, no hand-made mask) with the
+    chunk's queries at positions pos0..P-1; the rows before pos0 are fillers."""
+    for seed, (kvh, G, hd, pos0, n_tok) in enumerate([(2, 2, 64, 37, 11), (1, 4, 128, 0, 9),
+                                                      (2, 1, 128, 64, 64)]):
+        q, K16, V16 = _prefill_case(seed, kvh, G, hd, pos0, n_tok)
+        sm = 1 / math.sqrt(hd)
+        got = prefill(q, K16, V16, pos0, sm)
+        P = pos0 + n_tok
+        Qfull = np.zeros((P, kvh * G, hd))
+        Qfull[pos0:] = q.astype(np.float16).astype(np.float64)
+        qt = torch.from_numpy(np.transpose(Qfull, (1, 0, 2)))[None]
+        kt = torch.from_numpy(K16.astype(np.float64))[None]
+        vt = torch.from_numpy(V16.astype(np.float64))[None]
+        o = F.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=float(np.float32(sm)),
+                                           enable_gqa=True)
+        ref = np.transpose(o[0].numpy(), (1, 0, 2))[pos0:]
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12), np.abs(got - ref).max()
+
+
+def pin_prefill_invariants(prefill, decode):
+    kvh, G, hd, pos0, n_tok = 2, 2, 64, 20, 6
+    q, K16, V16 = _prefill_case(50, kvh, G, hd, pos0, n_tok)
+    sm = 0.125
+    full = prefill(q, K16, V16, pos0, sm)
+    # each row equals decode of the fp16-rounded query over keys [0, pos0 + i]
+    for i in range(n_tok):
+        q16 = q[i].astype(np.float16).astype(np.float32)
+        d = decode(q16, K16.astype(np.float64), V16.astype(np.float64), pos0 + i + 1, sm)
+        assert np.allclose(full[i], d, rtol=1e-12, atol=1e-12), i
+    # future keys do not move a row
+    i = 2
+    K2, V2 = K16.copy(), V16.copy()
+    K2[:, pos0 + i + 1:] = 100
+    V2[:, pos0 + i + 1:] = -100
+    assert np.array_equal(prefill(q, K2, V2, pos0, sm, rows=[i]), full[[i]])
+    # a row subset equals the same rows of the full result
+    assert np.array_equal(prefill(q, K16, V16, pos0, sm, rows=[0, 5]), full[[0, 5]])
+
+
+def pin_prefill_brute(prefill, brute_row):
+    kvh, G, hd, pos0, n_tok = 1, 2, 8, 3, 4
+    q, K16, V16 = _prefill_case(60, kvh, G, hd, pos0, n_tok)
+    sm = 0.4
+    out = prefill(q, K16, V16, pos0, sm)
+    q16 = q.astype(np.float16).astype(np.float64)
+    for i in range(n_tok):
+        for qh in range(2):
+            n = pos0 + i + 1
+            ref = brute_row(q16[i, qh], K16[0, :n].astype(np.float64), V16[0, :n].astype(np.float64), sm)
+            assert np.allclose(out[i, qh], ref, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# compaction
+# ----------------------------------------------------------------------------
+def pin_compact_exact(compact, Cache, FMT_F16, FMT_Q8):
+    kvh, hd, cap, n = 2, 128, 64, 40
+    r = np.random.default_rng(70)
+    xk = r.standard_normal((n, kvh, hd), dtype=np.float32) * np.float32(30)
+    xv = r.standard_normal((n, kvh, hd), dtype=np.float32) * np.float32(1e-3)
+    for fmt in (FMT_F16, FMT_Q8):
+        c = Cache(fmt, kvh, cap, hd)
+        assert c.append(0, xk, xv)
+        k16, v16 = compact(c, n)
+        assert k16.shape == (kvh, n, hd) and k16.dtype == np.float16
+        if fmt == FMT_F16:
+            assert np.array_equal(k16.view(np.uint16), c.k[:, :n].view(np.uint16))
+            assert np.array_equal(v16.view(np.uint16), c.v[:, :n].view(np.uint16))
+            continue
+        for which, out in (("k", k16), ("v", v16)):
+            codes = getattr(c, which)
+            sc = getattr(c, which + "_scale")
+            for (h, t, d) in [(0, 0, 0), (1, 39, 127), (0, 17, 64), (1, 3, 63), (0, 25, 100)] + \
+                    [tuple(r.integers(0, m) for m in (kvh, n, hd)) for _ in range(200)]:
+                exact = Fraction(int(codes[h, t, d])) * Fraction(float(sc[h, t, d // 64]))
+                assert Fraction(float(out[h, t, d])) == f16(exact), (which, h, t, d)
