@@ -1,0 +1,346 @@
+#!/usr/bin/env python3
+"""Benchmark of the reduced-precision K/V-cache attention path on one MI355X.
+
+Workload (full context): 48 layers, each 8 kv heads x 32 query heads x head_dim
+128 at 262144 cells, batch 1, once with an FP16 cache (1 GiB/layer) and once with
+the int8 cache (codes + fp16 scale per 64 dims, 0.516 GiB/layer).  Seeded
+synthetic K/V (standard normal, 4 outlier channels x20 per kv head); layer 0 is
+filled by kv_append from host-generated values, the other layers are device copies
+of it (distinct addresses, so no cache level holds more than a sliver of them).
+
+One step = for each format, for each of the 48 layers: kv_append of one new token
+(quantise-on-write or FP16 store) and kv_decode_attn over the cache.  The timed
+region holds exactly `--steps` steps between two device synchronisations; the
+metric is the decode's algorithmic K/V bytes per step / step time.  Each
+kv_decode_attn call is also bracketed by HIP events on the launch stream for the
+per-kernel roofline.  Side measurements (not in the step): bulk append rate, and
+the 4096-token prompt chunk at position 131072 of an int8 cache.
+
+Prints progress to stderr and ONE JSON line to stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn KV read GB/s (% HBM peak) at 262144 ctx, fp16 & int8; append cells/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix, vendor figure
+KVH, NQH, HD, CTX, LAYERS = 8, 32, 128, 262144, 48
+F16, Q8 = 0, 1
+BYTES_PER_CELL_HEAD = {F16: 2 * HD * 2, Q8: 2 * (HD + 2 * (HD // 64))}   # K+V per (cell, kv head)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_bytes(fmt, length):
+    return length * KVH * BYTES_PER_CELL_HEAD[fmt]
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "quantized_kv_cache_q8_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, src_hash):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/), only if the
+    kernel source has not changed since."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+def build_model(kq, torch, seed, cap, warm_len):
+    """48 layers x 2 formats, each layer one session (cap cells), layer 0 filled
+    with kv_append from seeded host data, layers 1.. device copies."""
+    import kvsynth
+    log("generating layer K/V on the host")
+    xk = kvsynth.kv_tokens(seed, 0, CTX, KVH, HD, "K", outliers=True)
+    xv = kvsynth.kv_tokens(seed, 0, CTX, KVH, HD, "V", outliers=True)
+    dk = torch.from_numpy(xk[None]).cuda()
+    dv = torch.from_numpy(xv[None]).cuda()
+    del xk, xv
+    model = {}
+    append_rate = {}
+    for fmt in (F16, Q8):
+        sh = kq.make_shape(fmt, KVH, NQH, HD)
+        base = kq.Session(fmt, KVH, cap)
+        tab0 = kq.session_table([base.entry()])
+        lens0 = torch.zeros(1, dtype=torch.int32, device="cuda")
+        # bulk append of the whole context, timed (first call warms the code object)
+        kq.kv_append(sh, tab0, lens0, 1, 1024, dk[:, :1024].contiguous(), dv[:, :1024].contiguous())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        kq.kv_append(sh, tab0, lens0, 1, CTX, dk, dv)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        rw = CTX * KVH * 2 * HD * 4 + kq.kv_cache_bytes(fmt, KVH, CTX, HD, 0) * 2 + \
+            kq.kv_cache_bytes(fmt, KVH, CTX, HD, 1) * 2
+        append_rate["f16" if fmt == F16 else "int8"] = {
+            "cells_per_s": CTX / (ms * 1e-3), "us": ms * 1e3, "GB_s": rw / (ms * 1e-3) / 1e9,
+            "frac_hbm": rw / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "cells": CTX,
+            "bytes_per_cell": rw // CTX}
+        log(f"fmt={fmt}: bulk append {CTX} cells in {ms:.3f} ms")
+        layers = [base]
+        for i in range(1, LAYERS):
+            s = kq.Session(fmt, KVH, cap, fill=None)
+            for a, b in zip(s.tensors(), base.tensors()):
+                a.copy_(b)
+            layers.append(s)
+        tabs = [kq.session_table([s.entry()]) for s in layers]
+        model[fmt] = dict(shape=sh, layers=layers, tabs=tabs)
+        torch.cuda.synchronize()
+        log(f"fmt={fmt}: {LAYERS} layers ready")
+    del dk, dv
+    torch.cuda.empty_cache()
+    return model, append_rate
+
+
+def run_steps(kq, torch, model, n_steps, len0, q, xk_new, xv_new, ws, events=None):
+    """n_steps decode steps starting with len0 cached cells; returns the final length."""
+    # lens_w: where the new token goes (cells before it); lens_d: cells the decode reads
+    lens_w = torch.full((1,), len0, dtype=torch.int32, device="cuda")
+    lens_d = torch.full((1,), len0 + 1, dtype=torch.int32, device="cuda")
+    out = torch.empty((1, NQH, HD), device="cuda")
+    length = len0
+    for step in range(n_steps):
+        for fmt, m in model.items():
+            sh = m["shape"]
+            for li in range(LAYERS):
+                tab = m["tabs"][li]
+                kq.kv_append(sh, tab, lens_w, 1, 1, xk_new[li], xv_new[li])
+                if events is not None:
+                    e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    e[0].record()
+                kq.kv_decode_attn(sh, tab, lens_d, 1, length + 1, q[li], 1 / math.sqrt(HD), out,
+                                  ws[fmt])
+                if events is not None:
+                    e[1].record()
+                    events[fmt].append(e)
+        lens_w += 1
+        lens_d += 1
+        length += 1
+    return length
+
+
+def prefill_side(kq, torch, seed, steps, warmup):
+    """4096-token chunk at position 131072 of an int8 cache: compaction and MFMA attention."""
+    import kvsynth
+    pos0, n_tok = 131072, 4096
+    P = pos0 + n_tok
+    log("prefill: filling 135168 int8 cells")
+    sh = kq.make_shape(Q8, KVH, NQH, HD)
+    s = kq.Session(Q8, KVH, P)
+    tab = kq.session_table([s.entry()])
+    lens = torch.zeros(1, dtype=torch.int32, device="cuda")
+    chunk = 32768
+    for t0 in range(0, P, chunk):
+        n = min(chunk, P - t0)
+        xk = kvsynth.kv_tokens(seed, 0, n, KVH, HD, "K", True, sub=1000 + t0)
+        xv = kvsynth.kv_tokens(seed, 0, n, KVH, HD, "V", True, sub=1000 + t0)
+        lens.fill_(t0)
+        kq.kv_append(sh, tab, lens, 1, n, torch.from_numpy(xk[None]).cuda(),
+                     torch.from_numpy(xv[None]).cuda())
+    q = torch.from_numpy(kvsynth.queries(seed, 0, n_tok, NQH, HD, stream=kvsynth.S_Q_PREFILL)).cuda()
+    out = torch.empty((n_tok, NQH, HD), device="cuda")
+    ws = torch.empty(kq.kv_prefill_workspace_bytes(sh, P), dtype=torch.uint8, device="cuda")
+    half = ws.numel() // 2
+    k16 = ws[:half].view(torch.int16)
+    v16 = ws[half:].view(torch.int16)
+    sm = 1 / math.sqrt(HD)
+    for _ in range(warmup):
+        kq.kv_prefill_attn(sh, s.entry(), pos0, n_tok, q, sm, out, ws)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        kq.kv_compact_f16(sh, s.entry(), P, k16, v16)
+        e[1].record()
+        kq.kv_prefill_attn(sh, s.entry(), pos0, n_tok, q, sm, out, ws)
+        e[2].record()
+        ev.append(e)
+    torch.cuda.synchronize()
+    comp_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    total_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    attn_ms = max(total_ms - comp_ms, 1e-9)
+    pairs = sum(pos0 + i + 1 for i in range(n_tok))
+    flop = 4.0 * HD * pairs * NQH
+    comp_bytes = P * KVH * (2 * (HD + 4) + 2 * HD * 2)
+    assert torch.isfinite(out).all().item()
+    return {
+        "workload": "int8 cache, 4096-token chunk at position 131072, 8 kv / 32 q heads",
+        "tokens_per_s": n_tok / (total_ms * 1e-3), "ms_total": total_ms,
+        "compaction_ms": comp_ms, "compaction_GB_s": comp_bytes / (comp_ms * 1e-3) / 1e9,
+        "attention_ms": attn_ms, "attention_TFLOP_s": flop / (attn_ms * 1e-3) / 1e12,
+        "mfma_frac": flop / (attn_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+        "flop": flop}
+
+
+def cpu_baseline_leg(seed):
+    """The oracle, as it stands, on a bounded sample of the workload: 2 of the 8 kv
+    heads of one layer at 262144 cells, both formats (cache write + decode)."""
+    import kvsynth
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    kv_s = 2
+    xk = kvsynth.kv_tokens(seed, 0, CTX, KVH, HD, "K", outliers=True)[:, :kv_s].copy()
+    xv = kvsynth.kv_tokens(seed, 0, CTX, KVH, HD, "V", outliers=True)[:, :kv_s].copy()
+    q = kvsynth.queries(seed, 0, 1, NQH, HD)[0][: kv_s * (NQH // KVH)]
+    res = {}
+    total_bytes, total_s = 0, 0.0
+    for fmt in (F16, Q8):
+        t0 = time.perf_counter()
+        c = oracle.Cache(fmt, kv_s, CTX, HD)
+        c.append(0, xk, xv)
+        t1 = time.perf_counter()
+        K = c.dequant("k", CTX)
+        V = c.dequant("v", CTX)
+        oracle.decode_attn(q, K, V, CTX, 1 / math.sqrt(HD))
+        t2 = time.perf_counter()
+        nbytes = CTX * kv_s * BYTES_PER_CELL_HEAD[fmt]
+        res["f16" if fmt == F16 else "int8"] = {
+            "decode_GB_s": nbytes / (t2 - t1) / 1e9, "decode_s": t2 - t1,
+            "append_cells_per_s": CTX * kv_s / KVH / (t1 - t0)}
+        total_bytes += nbytes
+        total_s += t2 - t1
+    cores = len(os.sched_getaffinity(0))
+    return {"value": total_bytes / total_s / 1e9, "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": f"one layer, 2 of 8 kv heads (8 query heads), 262144 cells, FP16 and int8: "
+                      f"cache write then fp64 decode; value = decode K/V bytes / decode time; "
+                      f"numpy elementwise work on 1 thread, BLAS on {blas_threads} of {cores} cores",
+            "host_cores": cores, "per_format": res}
+
+
+# ----------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=44)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path has no multi-GPU mode (--gpus {args.gpus} "
+              "requested). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import quantized_kv_cache_q8_amd as kq
+
+    n_steps, n_warm = args.steps, args.warmup
+    cap = ((CTX + 63) // 64) * 64
+    len0 = CTX - (n_steps + n_warm)          # the last step decodes over exactly 262144 cells
+    model, append_rate = build_model(kq, torch, args.seed, cap, len0)
+
+    import kvsynth
+    q = [torch.from_numpy(kvsynth.queries(args.seed, li, 1, NQH, HD)).cuda() for li in range(LAYERS)]
+    xk_new = [torch.from_numpy(kvsynth.kv_tokens(args.seed, li, 1, KVH, HD, "K", True,
+                                                 stream=kvsynth.S_K_NEW)[None]).cuda()
+              for li in range(LAYERS)]
+    xv_new = [torch.from_numpy(kvsynth.kv_tokens(args.seed, li, 1, KVH, HD, "V", True,
+                                                 stream=kvsynth.S_V_NEW)[None]).cuda()
+              for li in range(LAYERS)]
+    ws = {fmt: torch.empty(kq.kv_decode_workspace_bytes(model[fmt]["shape"], 1, CTX),
+                           dtype=torch.uint8, device="cuda") for fmt in model}
+
+    log(f"warmup {n_warm} steps")
+    length = run_steps(kq, torch, model, n_warm, len0, q, xk_new, xv_new, ws)
+    torch.cuda.synchronize()
+    log(f"timing {n_steps} steps")
+    events = {F16: [], Q8: []}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    end_len = run_steps(kq, torch, model, n_steps, length, q, xk_new, xv_new, ws, events)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert end_len == CTX
+    step_s = (t1 - t0) / n_steps
+    bytes_total = sum(decode_bytes(fmt, length + s + 1) * LAYERS for fmt in (F16, Q8)
+                      for s in range(n_steps))
+    value = bytes_total / (t1 - t0) / 1e9
+
+    roof = {}
+    for fmt in (F16, Q8):
+        durs = [a.elapsed_time(b) * 1e-3 for a, b in events[fmt]]
+        avg = float(np.mean(durs))
+        per_launch = float(np.mean([decode_bytes(fmt, length + s + 1) for s in range(n_steps)]))
+        ach = per_launch / avg / 1e9
+        key = "decode_f16" if fmt == F16 else "decode_int8"
+        roof[fmt] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS,
+                     "traffic": load_traffic(key, source_hash("decode.hip")),
+                     "kernel": "k_decode_split + k_decode_merge (one kv_decode_attn call)",
+                     "avg_us": avg * 1e6, "algorithmic_bytes_per_launch": per_launch,
+                     "tokens_per_s_48_layers": 1.0 / (avg * LAYERS)}
+        log(f"fmt={fmt}: {avg * 1e6:.1f} us/layer, {ach:.0f} GB/s ({ach / HBM_PEAK_GBS:.1%})")
+    dominant = F16 if roof[F16]["avg_us"] >= roof[Q8]["avg_us"] else Q8
+
+    prefill = None
+    if not args.no_prefill:
+        del model
+        torch.cuda.empty_cache()
+        prefill = prefill_side(kq, torch, 55, steps=5, warmup=1)
+        log(f"prefill: {prefill['attention_ms']:.2f} ms attention, "
+            f"{prefill['attention_TFLOP_s']:.0f} TFLOP/s ({prefill['mfma_frac']:.1%})")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline_leg(args.seed)
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": n_steps,
+        "warmup": n_warm, "ms_per_step": step_s * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "full-context decode: 48 layers x (8 kv heads, 32 query heads, "
+                               "head_dim 128), 262144 cells, batch 1, FP16 cache and int8 cache; "
+                               "a step appends one token per layer and decodes, both formats",
+                   "layers": LAYERS, "kv_heads": KVH, "q_heads": NQH, "head_dim": HD,
+                   "context": CTX, "batch": 1, "formats": ["f16", "int8"]},
+        "frac_hbm": value / HBM_PEAK_GBS,
+        "roofline": roof[dominant],
+        "roofline_int8" if dominant == F16 else "roofline_f16": roof[Q8 if dominant == F16 else F16],
+        "cpu_baseline": cpu,
+        "append_bulk": append_rate,
+        "prefill": prefill,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

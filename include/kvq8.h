@@ -1,0 +1,152 @@
+/*
+ * kvq8.h -- attention over a reduced-precision K/V cache on MI355X (gfx950).
+ *
+ * C ABI.  Every pointer named d_* is a DEVICE pointer, every h_* a HOST pointer.
+ * Every call that takes a `stream` (a hipStream_t passed as void*, NULL for the
+ * null stream) only enqueues work on it and returns; nothing allocates, frees or
+ * synchronises, and no call keeps state between calls (reentrant, thread-safe).
+ * The caller owns every buffer: caches, session tables, lengths, workspaces.
+ *
+ * Error behaviour: every argument a host can check is checked before anything is
+ * enqueued; on error the call returns a negative KV_ERR_* code and enqueues
+ * nothing.  What only the device can see (a session table entry, a length) is
+ * checked by the kernels: the offending session is skipped (no byte of its cache
+ * is written; its decode output is written as zeros) and a KV_DEV_* bit is OR-ed
+ * into *d_status when d_status is not NULL (the caller zeroes it).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] PR #3084 "FP16 K/V cache by default, int8 with --kv-q8 (262144 fits a
+ *        16 GiB card)" -- sections Summary, What changed, Extra Notes.
+ *   [P2] Issue #67 "Path F format v3: persist per-head INT8 KV scales".
+ *   [P3] PR #711 "kv: --kv k8v4 streams with --kv-resident" -- sections What, How.
+ */
+#ifndef KVQ8_H
+#define KVQ8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Cache formats [P1, Summary]: FP16 values, or int8 codes with one FP16 scale per
+ * 64 dims.  An explicit enum, checked against which scale pointers are present,
+ * rather than inferring the format from pointer presence (the silent-skip trap
+ * described in [P3, How]). */
+typedef enum { KV_FMT_F16 = 0, KV_FMT_Q8 = 1 } kv_fmt;
+
+#define KV_GROUP 64 /* dims per FP16 scale [P1, Summary] */
+
+typedef struct {
+  int32_t fmt;        /* kv_fmt */
+  int32_t n_kv_heads; /* >= 1 */
+  int32_t n_q_heads;  /* n_kv_heads * G, G in {1, 2, 4, 8}; query head q reads kv head q / G */
+  int32_t head_dim;   /* 128 */
+} kv_shape;
+
+/* One session's cache for one layer.  Layout [P1, Extra Notes: [kvh][ctx][HD]]:
+ *   F16: k, v  = fp16 bits, [n_kv_heads][cap][head_dim]; k_scale = v_scale = NULL.
+ *   Q8 : k, v  = int8 codes, [n_kv_heads][cap][head_dim];
+ *        k_scale, v_scale = fp16 bits, [n_kv_heads][cap][head_dim / 64]; scale g of
+ *        a row covers dims [64g, 64g + 64).  Codes and scales are separate arrays
+ *        ([P1, What changed]; separate byte runs in [P3, How]).
+ * All four pointers 16-byte aligned; cap a multiple of 64.  An array of these
+ * lives in device memory for the batched calls. */
+typedef struct {
+  void* k;
+  void* v;
+  uint16_t* k_scale;
+  uint16_t* v_scale;
+  int32_t cap;
+  int32_t reserved; /* 0 */
+} kv_session;
+
+enum {
+  KV_OK = 0,
+  KV_ERR_ARG = -1,         /* null pointer, non-positive size, n_q_heads % n_kv_heads != 0 */
+  KV_ERR_FMT = -2,         /* unknown format, or scale pointers inconsistent with it */
+  KV_ERR_ALIGN = -3,       /* pointer not 16-byte aligned, or cap % 64 != 0 */
+  KV_ERR_UNSUPPORTED = -4, /* head_dim != 128, or G not in {1, 2, 4, 8} */
+  KV_ERR_WORKSPACE = -5,   /* workspace null or smaller than the *_workspace_bytes value */
+  KV_ERR_RANGE = -6,       /* rows outside [0, cap) (host-checkable cases) */
+  KV_ERR_HIP = -7          /* a kernel launch failed */
+};
+
+/* bits OR-ed into *d_status by kernels */
+enum {
+  KV_DEV_RANGE = 1,      /* len < 0, len + n_tok > cap (append), len > max_len or cap (decode) */
+  KV_DEV_BAD_SESSION = 2 /* table entry with null/unaligned pointers, scales inconsistent with
+                            the format, or cap not a positive multiple of 64 */
+};
+
+/* Bytes of one K (or one V) array of one layer: part 0 the values/codes, part 1
+ * the scales (0 for F16).  Per value: 2 B (F16), or 1 B + 2 B per 64 (Q8), which
+ * reproduces the 6.0 / 3.1 GiB at 262144 cells of [P1, Summary].  Returns 0 for
+ * invalid arguments. */
+size_t kv_cache_bytes(int fmt, int n_kv_heads, int cap, int head_dim, int part);
+
+/* Write n_tok new cells per session: quantise-on-write (Q8) or FP16 store (F16).
+ * [P1, What changed]: scale = fp16(max|x| / 127) per 64-dim group of a head row,
+ * with IEEE fp32 division and round-to-nearest-even; code = clamp(rint(x / s),
+ * -127, 127) dividing (IEEE fp32) by the stored fp16 scale; a zero scale stores
+ * code 0.  F16 stores fp16_rne(x).
+ *   d_tab   : kv_session [n_sess] (device)
+ *   d_len   : int32 [n_sess] (device): session b's cells go to rows
+ *             [d_len[b], d_len[b] + n_tok).  NOT modified (the caller advances it).
+ *   d_k_new, d_v_new : fp32 [n_sess][n_tok][n_kv_heads][head_dim] (device)
+ *   d_status: int32 (device) or NULL; KV_DEV_* bits.  A session whose rows do not
+ *             fit is skipped whole. */
+int kv_append(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d_len,
+              int n_sess, int n_tok, const float* d_k_new, const float* d_v_new,
+              int32_t* d_status, void* stream);
+
+/* Workspace for kv_decode_attn: split-K partials.  Depends only on its arguments. */
+size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_len);
+
+/* Split-K decode attention of one new token per session over the cache, reading
+ * the cache format directly ([P1, What changed / Extra Notes]).  For query head q
+ * of session b, kv head h = q / G:
+ *   out[b][q] = sum_t softmax_t(sm_scale * q . K[h][t]) V[h][t],  t < d_len[b],
+ * with K, V the dequantised cache values (code * scale, exact in fp32, or the
+ * fp16 values), fp32 arithmetic.  Partials of each split of the context are
+ * merged by log-sum-exp.  d_len[b] == 0 gives a zero row.
+ *   d_q   : fp32 [n_sess][n_q_heads][head_dim];  d_out : fp32 [n_sess][n_q_heads][head_dim]
+ *   max_len : host upper bound of every d_len[b] (sizes the grid); a session over it
+ *             is flagged KV_DEV_RANGE and gets a zero row.
+ *   d_ws, ws_bytes : at least kv_decode_workspace_bytes(h_shape, n_sess, max_len).
+ * Deterministic: the same inputs give bitwise the same output. */
+int kv_decode_attn(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d_len,
+                   int n_sess, int max_len, const float* d_q, float sm_scale, float* d_out,
+                   void* d_ws, size_t ws_bytes, int32_t* d_status, void* stream);
+
+/* Compaction [P1, Extra Notes]: the FP16 [kvh][P][HD] copy of cache rows [0, P) that
+ * the prompt chunk's Q K^T and P V products read.  F16: a copy (stride cap -> P).
+ * Q8: fp16_rne(float(code) * float(scale)) -- one rounding of an exact product.
+ *   h_sess : one session (host struct holding device pointers), P <= h_sess->cap
+ *   d_k16, d_v16 : fp16 bits [n_kv_heads][P][head_dim] (device), 16-byte aligned. */
+int kv_compact_f16(const kv_shape* h_shape, const kv_session* h_sess, int P,
+                   uint16_t* d_k16, uint16_t* d_v16, void* stream);
+
+/* Workspace for kv_prefill_attn: the compacted copy (Q8), 0 bytes for F16. */
+size_t kv_prefill_workspace_bytes(const kv_shape* h_shape, int P);
+
+/* Causal attention of a prompt chunk over the cache, computed on an FP16 copy with
+ * fp16 Q and fp32 accumulation on the matrix cores ([P1, Extra Notes]).  The chunk
+ * must already be appended at rows [pos0, pos0 + n_tok).  Row i (position pos0 + i)
+ * of query head q attends keys [0, pos0 + i] of kv head q / G:
+ *   out[i][q] = sum_t softmax_t(sm_scale * fp16(q_i) . K16[t]) V16[t]
+ * with the softmax weights rounded to fp16 before the P V product.
+ *   d_q  : fp32 [n_tok][n_q_heads][head_dim];  d_out : fp32 [n_tok][n_q_heads][head_dim]
+ *   d_ws : at least kv_prefill_workspace_bytes(h_shape, pos0 + n_tok) (may be NULL if 0). */
+int kv_prefill_attn(const kv_shape* h_shape, const kv_session* h_sess, int pos0, int n_tok,
+                    const float* d_q, float sm_scale, float* d_out, void* d_ws, size_t ws_bytes,
+                    void* stream);
+
+/* Static text for a KV_* status code. */
+const char* kv_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ8_H */

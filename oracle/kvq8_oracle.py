@@ -246,15 +246,18 @@ def prefill_attn(q: np.ndarray, K16: np.ndarray, V16: np.ndarray, pos0: int,
     rows = np.arange(n_tok) if rows is None else np.asarray(rows)
     sm = float(np.float32(sm_scale))
     Q16 = np.asarray(q, np.float32).astype(np.float16).astype(np.float64)
+    n_max = pos0 + int(rows.max()) + 1
+    keys = np.arange(n_max)
+    allowed = keys[None, :] <= (pos0 + rows)[:, None]          # row i attends keys [0, pos0 + i]
     out = np.zeros((len(rows), nqh, hd))
-    for qh in range(nqh):
-        h = qh // G
-        for r, i in enumerate(rows):
-            n_keys = pos0 + int(i) + 1
-            Kh = K16[h, :n_keys].astype(np.float64)
-            z = sm * (Kh @ Q16[i, qh])
-            w = np.exp(z - z.max())
-            out[r, qh] = (w @ V16[h, :n_keys].astype(np.float64)) / w.sum()
+    for h in range(kvh):
+        Kh = K16[h, :n_max].astype(np.float64)
+        Vh = V16[h, :n_max].astype(np.float64)
+        for qh in range(h * G, (h + 1) * G):
+            Z = sm * (Q16[rows, qh] @ Kh.T)                      # [rows][keys]
+            Z = np.where(allowed, Z, -np.inf)
+            W = np.exp(Z - Z.max(axis=1, keepdims=True))
+            out[:, qh] = (W @ Vh) / W.sum(axis=1, keepdims=True)
     return out
 
 

@@ -1,0 +1,208 @@
+"""Python binding of libkvq8 (reduced-precision K/V-cache attention, MI355X / gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP library; these
+wrappers check dtypes, contiguity and devices of torch tensors, pass their device
+pointers and the current HIP stream, and raise KvError on a negative status.
+The names are those of the C ABI in include/kvq8.h.
+
+If libkvq8.so is not built, importing this package raises ImportError: there is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq8.so")
+
+KV_FMT_F16, KV_FMT_Q8 = 0, 1
+KV_GROUP = 64
+KV_OK, KV_ERR_ARG, KV_ERR_FMT, KV_ERR_ALIGN, KV_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
+KV_ERR_WORKSPACE, KV_ERR_RANGE, KV_ERR_HIP = -5, -6, -7
+KV_DEV_RANGE, KV_DEV_BAD_SESSION = 1, 2
+
+EXPORTED = ["kv_cache_bytes", "kv_append", "kv_decode_workspace_bytes", "kv_decode_attn",
+            "kv_compact_f16", "kv_prefill_workspace_bytes", "kv_prefill_attn", "kv_status_str"]
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run quantized_kv_cache_q8_amd.build.build() "
+                      "(or __graft_entry__.build()) first")
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class kv_shape(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+class kv_session(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_scale", ctypes.c_void_p), ("cap", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+assert ctypes.sizeof(kv_session) == 40
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+_sig = {
+    "kv_cache_bytes": (_SZ, [_I, _I, _I, _I, _I]),
+    "kv_append": (_I, [ctypes.POINTER(kv_shape), _P, _P, _I, _I, _P, _P, _P, _P]),
+    "kv_decode_workspace_bytes": (_SZ, [ctypes.POINTER(kv_shape), _I, _I]),
+    "kv_decode_attn": (_I, [ctypes.POINTER(kv_shape), _P, _P, _I, _I, _P, ctypes.c_float, _P, _P,
+                            _SZ, _P, _P]),
+    "kv_compact_f16": (_I, [ctypes.POINTER(kv_shape), ctypes.POINTER(kv_session), _I, _P, _P, _P]),
+    "kv_prefill_workspace_bytes": (_SZ, [ctypes.POINTER(kv_shape), _I]),
+    "kv_prefill_attn": (_I, [ctypes.POINTER(kv_shape), ctypes.POINTER(kv_session), _I, _I, _P,
+                             ctypes.c_float, _P, _P, _SZ, _P]),
+    "kv_status_str": (ctypes.c_char_p, [_I]),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class KvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status} ({kv_status_str(status)})")
+        self.status = status
+
+
+def kv_status_str(status: int) -> str:
+    return _lib.kv_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != KV_OK:
+        raise KvError(status, where)
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    """Device pointer of a contiguous CUDA/HIP tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_shape(fmt: int, n_kv_heads: int, n_q_heads: int, head_dim: int = 128) -> kv_shape:
+    return kv_shape(int(fmt), int(n_kv_heads), int(n_q_heads), int(head_dim))
+
+
+def kv_cache_bytes(fmt: int, n_kv_heads: int, cap: int, head_dim: int, part: int) -> int:
+    return int(_lib.kv_cache_bytes(fmt, n_kv_heads, cap, head_dim, part))
+
+
+# ----------------------------------------------------------------------------
+# caller-owned buffers (torch device memory)
+# ----------------------------------------------------------------------------
+class Session:
+    """One session's cache arrays for one layer, allocated with torch.
+
+    F16: k, v int16 tensors holding fp16 bits [kvh][cap][hd]; Q8: k, v int8 codes
+    [kvh][cap][hd] and k_scale, v_scale int16 (fp16 bits) [kvh][cap][hd/64]."""
+
+    def __init__(self, fmt: int, n_kv_heads: int, cap: int, head_dim: int = 128,
+                 device="cuda", fill: int | None = None):
+        self.fmt, self.kvh, self.cap, self.hd = fmt, n_kv_heads, cap, head_dim
+        shp = (n_kv_heads, cap, head_dim)
+        if fmt == KV_FMT_F16:
+            self.k = torch.empty(shp, dtype=torch.int16, device=device)
+            self.v = torch.empty(shp, dtype=torch.int16, device=device)
+            self.k_scale = self.v_scale = None
+        else:
+            self.k = torch.empty(shp, dtype=torch.int8, device=device)
+            self.v = torch.empty(shp, dtype=torch.int8, device=device)
+            sshp = (n_kv_heads, cap, head_dim // KV_GROUP)
+            self.k_scale = torch.empty(sshp, dtype=torch.int16, device=device)
+            self.v_scale = torch.empty(sshp, dtype=torch.int16, device=device)
+        for t in self.tensors():
+            if fill is None:
+                t.zero_()
+            else:
+                t.view(torch.uint8).fill_(fill)
+
+    def tensors(self):
+        return [t for t in (self.k, self.v, self.k_scale, self.v_scale) if t is not None]
+
+    def entry(self) -> kv_session:
+        return kv_session(_ptr(self.k), _ptr(self.v), _ptr(self.k_scale), _ptr(self.v_scale),
+                          self.cap, 0)
+
+
+def session_table(entries, device="cuda") -> torch.Tensor:
+    """Device array of kv_session structs (a uint8 tensor of 40 * n bytes)."""
+    n = len(entries)
+    arr = (kv_session * n)(*entries)
+    host = torch.frombuffer(bytearray(bytes(arr)), dtype=torch.uint8)
+    return host.to(device)
+
+
+# ----------------------------------------------------------------------------
+# the C ABI, tensor in / tensor out
+# ----------------------------------------------------------------------------
+def kv_append(shape: kv_shape, tab: torch.Tensor, lens: torch.Tensor, n_sess: int, n_tok: int,
+              k_new: torch.Tensor, v_new: torch.Tensor, status: torch.Tensor | None = None,
+              stream=None) -> None:
+    _check(_lib.kv_append(ctypes.byref(shape), _ptr(tab, torch.uint8, "tab"),
+                          _ptr(lens, torch.int32, "lens"), n_sess, n_tok,
+                          _ptr(k_new, torch.float32, "k_new"), _ptr(v_new, torch.float32, "v_new"),
+                          _ptr(status, torch.int32, "status"), _stream(stream)), "kv_append")
+
+
+def kv_decode_workspace_bytes(shape: kv_shape, n_sess: int, max_len: int) -> int:
+    return int(_lib.kv_decode_workspace_bytes(ctypes.byref(shape), n_sess, max_len))
+
+
+def kv_decode_attn(shape: kv_shape, tab: torch.Tensor, lens: torch.Tensor, n_sess: int,
+                   max_len: int, q: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                   ws: torch.Tensor, status: torch.Tensor | None = None, stream=None) -> None:
+    _check(_lib.kv_decode_attn(ctypes.byref(shape), _ptr(tab, torch.uint8, "tab"),
+                               _ptr(lens, torch.int32, "lens"), n_sess, max_len,
+                               _ptr(q, torch.float32, "q"), float(sm_scale),
+                               _ptr(out, torch.float32, "out"), _ptr(ws, None, "ws"),
+                               ws.numel() * ws.element_size(), _ptr(status, torch.int32, "status"),
+                               _stream(stream)), "kv_decode_attn")
+
+
+def kv_compact_f16(shape: kv_shape, sess: kv_session, P: int, k16: torch.Tensor,
+                   v16: torch.Tensor, stream=None) -> None:
+    _check(_lib.kv_compact_f16(ctypes.byref(shape), ctypes.byref(sess), P,
+                               _ptr(k16, torch.int16, "k16"), _ptr(v16, torch.int16, "v16"),
+                               _stream(stream)), "kv_compact_f16")
+
+
+def kv_prefill_workspace_bytes(shape: kv_shape, P: int) -> int:
+    return int(_lib.kv_prefill_workspace_bytes(ctypes.byref(shape), P))
+
+
+def kv_prefill_attn(shape: kv_shape, sess: kv_session, pos0: int, n_tok: int, q: torch.Tensor,
+                    sm_scale: float, out: torch.Tensor, ws: torch.Tensor | None,
+                    stream=None) -> None:
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(_lib.kv_prefill_attn(ctypes.byref(shape), ctypes.byref(sess), pos0, n_tok,
+                                _ptr(q, torch.float32, "q"), float(sm_scale),
+                                _ptr(out, torch.float32, "out"), _ptr(ws, None, "ws"), nbytes,
+                                _stream(stream)), "kv_prefill_attn")
+
+
+def raw_lib() -> ctypes.CDLL:
+    """The loaded C library (for calls with raw pointers)."""
+    return _lib

@@ -1,0 +1,163 @@
+// The C ABI of libkvq8: argument validation (before any HIP call) and launches.
+// Declarations and their contracts are in include/kvq8.h.
+#include <cmath>
+
+#include "kvq8_internal.h"
+
+using namespace kvq8;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+int check_shape(const kv_shape* s) {
+  if (s == nullptr) return KV_ERR_ARG;
+  if (s->fmt != KV_FMT_F16 && s->fmt != KV_FMT_Q8) return KV_ERR_FMT;
+  if (s->n_kv_heads < 1 || s->n_q_heads < 1 || s->n_q_heads % s->n_kv_heads != 0) return KV_ERR_ARG;
+  if (s->head_dim != HD) return KV_ERR_UNSUPPORTED;
+  const int G = s->n_q_heads / s->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return KV_ERR_UNSUPPORTED;
+  return KV_OK;
+}
+
+// host copy of one session entry (prefill / compaction take one on the host)
+int check_session(const kv_shape* s, const kv_session* e) {
+  if (e == nullptr || e->k == nullptr || e->v == nullptr) return KV_ERR_ARG;
+  if (s->fmt == KV_FMT_Q8) {
+    if (e->k_scale == nullptr || e->v_scale == nullptr) return KV_ERR_FMT;
+  } else if (e->k_scale != nullptr || e->v_scale != nullptr) {
+    return KV_ERR_FMT;
+  }
+  if (!aligned16(e->k) || !aligned16(e->v) || !aligned16(e->k_scale) || !aligned16(e->v_scale))
+    return KV_ERR_ALIGN;
+  if (e->cap <= 0 || (e->cap & 63)) return KV_ERR_ALIGN;
+  return KV_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KV_OK : KV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t kv_cache_bytes(int fmt, int n_kv_heads, int cap, int head_dim, int part) {
+  if ((fmt != KV_FMT_F16 && fmt != KV_FMT_Q8) || n_kv_heads < 0 || cap < 0 || head_dim <= 0 ||
+      head_dim % KV_GROUP != 0 || (part != 0 && part != 1))
+    return 0;
+  const size_t n = (size_t)n_kv_heads * (size_t)cap * (size_t)head_dim;
+  if (part == 0) return fmt == KV_FMT_F16 ? 2 * n : n;
+  return fmt == KV_FMT_F16 ? 0 : 2 * (n / KV_GROUP);
+}
+
+int kv_append(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d_len, int n_sess,
+              int n_tok, const float* d_k_new, const float* d_v_new, int32_t* d_status,
+              void* stream) {
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  if (d_tab == nullptr || d_len == nullptr || d_k_new == nullptr || d_v_new == nullptr)
+    return KV_ERR_ARG;
+  if (n_sess < 1 || n_tok < 0) return KV_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_tab) & 7) || !aligned4(d_len) || !aligned16(d_k_new) ||
+      !aligned16(d_v_new) || !aligned4(d_status))
+    return KV_ERR_ALIGN;
+  if (n_tok == 0) return KV_OK;
+  return hip_status(launch_append(h_shape->fmt, h_shape->n_kv_heads, d_tab, d_len, n_sess, n_tok,
+                                  d_k_new, d_v_new, d_status, static_cast<hipStream_t>(stream)));
+}
+
+size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_len) {
+  if (check_shape(h_shape) || n_sess < 1 || max_len < 0) return 0;
+  const DecodePlan p = decode_plan(h_shape->n_kv_heads, h_shape->n_q_heads, n_sess, max_len);
+  return p.ws_o_bytes + p.ws_lse_bytes;
+}
+
+int kv_decode_attn(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d_len,
+                   int n_sess, int max_len, const float* d_q, float sm_scale, float* d_out,
+                   void* d_ws, size_t ws_bytes, int32_t* d_status, void* stream) {
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  if (d_tab == nullptr || d_len == nullptr || d_q == nullptr || d_out == nullptr) return KV_ERR_ARG;
+  if (n_sess < 1 || max_len < 0 || !std::isfinite(sm_scale)) return KV_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_tab) & 7) || !aligned4(d_len) || !aligned16(d_q) ||
+      !aligned16(d_out) || !aligned16(d_ws) || !aligned4(d_status))
+    return KV_ERR_ALIGN;
+  const DecodePlan p = decode_plan(h_shape->n_kv_heads, h_shape->n_q_heads, n_sess, max_len);
+  if (d_ws == nullptr || ws_bytes < p.ws_o_bytes + p.ws_lse_bytes) return KV_ERR_WORKSPACE;
+  return hip_status(launch_decode(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, d_tab,
+                                  d_len, n_sess, max_len, d_q, sm_scale, d_out, d_ws, p, d_status,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int kv_compact_f16(const kv_shape* h_shape, const kv_session* h_sess, int P, uint16_t* d_k16,
+                   uint16_t* d_v16, void* stream) {
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  rc = check_session(h_shape, h_sess);
+  if (rc) return rc;
+  if (d_k16 == nullptr || d_v16 == nullptr || P < 1) return KV_ERR_ARG;
+  if (!aligned16(d_k16) || !aligned16(d_v16)) return KV_ERR_ALIGN;
+  if (P > h_sess->cap) return KV_ERR_RANGE;
+  return hip_status(launch_compact(h_shape->fmt, h_shape->n_kv_heads, *h_sess, P, d_k16, d_v16,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t kv_prefill_workspace_bytes(const kv_shape* h_shape, int P) {
+  if (check_shape(h_shape) || P < 0) return 0;
+  if (h_shape->fmt == KV_FMT_F16) return 0;
+  const size_t half = ((size_t)h_shape->n_kv_heads * (size_t)P * HD * 2 + 255) & ~(size_t)255;
+  return 2 * half;
+}
+
+int kv_prefill_attn(const kv_shape* h_shape, const kv_session* h_sess, int pos0, int n_tok,
+                    const float* d_q, float sm_scale, float* d_out, void* d_ws, size_t ws_bytes,
+                    void* stream) {
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  rc = check_session(h_shape, h_sess);
+  if (rc) return rc;
+  if (d_q == nullptr || d_out == nullptr || pos0 < 0 || n_tok < 0 || !std::isfinite(sm_scale))
+    return KV_ERR_ARG;
+  if (!aligned16(d_q) || !aligned16(d_out) || !aligned16(d_ws)) return KV_ERR_ALIGN;
+  if ((long long)pos0 + n_tok > h_sess->cap) return KV_ERR_RANGE;
+  if (n_tok == 0) return KV_OK;
+  const int P = pos0 + n_tok;
+  const size_t need = kv_prefill_workspace_bytes(h_shape, P);
+  if (need > 0 && (d_ws == nullptr || ws_bytes < need)) return KV_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int kvh = h_shape->n_kv_heads;
+  const uint16_t *k16, *v16;
+  long row_stride;  // rows between kv heads
+  if (h_shape->fmt == KV_FMT_Q8) {
+    uint16_t* wk = static_cast<uint16_t*>(d_ws);
+    uint16_t* wv = reinterpret_cast<uint16_t*>(static_cast<char*>(d_ws) + need / 2);
+    rc = hip_status(launch_compact(KV_FMT_Q8, kvh, *h_sess, P, wk, wv, st));
+    if (rc) return rc;
+    k16 = wk;
+    v16 = wv;
+    row_stride = P;
+  } else {
+    // an FP16 cache is already the fp16 [kvh][cap][HD] layout: read it in place
+    k16 = static_cast<const uint16_t*>(h_sess->k);
+    v16 = static_cast<const uint16_t*>(h_sess->v);
+    row_stride = h_sess->cap;
+  }
+  return hip_status(launch_prefill(kvh, h_shape->n_q_heads, k16, v16, row_stride, pos0, n_tok, d_q,
+                                   sm_scale, d_out, st));
+}
+
+const char* kv_status_str(int status) {
+  switch (status) {
+    case KV_OK: return "ok";
+    case KV_ERR_ARG: return "invalid argument (null pointer, size or head counts)";
+    case KV_ERR_FMT: return "unknown cache format, or scale pointers inconsistent with it";
+    case KV_ERR_ALIGN: return "pointer not 16-byte aligned, or cap not a multiple of 64";
+    case KV_ERR_UNSUPPORTED: return "unsupported head_dim or query/kv head ratio";
+    case KV_ERR_WORKSPACE: return "workspace missing or too small";
+    case KV_ERR_RANGE: return "rows outside the session's capacity";
+    case KV_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,265 @@
+// Causal attention of a prompt chunk over the FP16 [kvh][P][HD] copy of the cache,
+// on the matrix cores (PR #3084 "FP16 K/V cache by default, int8 with --kv-q8",
+// section Extra Notes: the prompt chunk's Q K^T and P V products read fp16 halves).
+//
+// Workgroup = (kv head h, block of BQ = 256/G queries); its 256 rows are the
+// (query, head) pairs of the G query heads sharing kv head h, so one K/V tile in
+// LDS serves all of them.  Wave w owns rows [64w, 64w + 64) as 4 blocks of 16.
+//
+// Per 64-key tile, with v_mfma_f32_16x16x32_f16 (fp16 in, fp32 accumulate):
+//   S^T[key][row] = K Q^T    A = K rows from LDS, B = the wave's Q rows (registers)
+//   online softmax per row in fp32 (each lane owns whole rows: row = lane % 16 of
+//   each 16-row block; the 16 keys of a lane are reduced in registers, then across
+//   the 4 lane groups)
+//   O^T[dim][row] += V^T P^T  A = V^T from LDS, B = P^T straight from the S^T
+//   accumulators (fp16), using one consistent assignment of keys to MFMA k-slots
+//   for both operands, so no data moves between lanes.
+// K is staged row-major with a 272-byte row pitch, V transposed with a 144-byte
+// pitch, both free of LDS bank conflicts on the fragment reads.  The next tile's
+// global loads are in flight while the current tile computes.
+// Workgroups are numbered so that consecutive ones take different kv heads: the
+// hardware deals workgroups round-robin to the 8 XCDs, so with 8 kv heads each
+// XCD's L2 serves the K/V of one head to every query block of that head.
+#include "kvq8_internal.h"
+
+namespace kvq8 {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int PF_THREADS = 256;
+constexpr int BK = 64;     // keys per tile
+constexpr int KSTR = 136;  // K row pitch in halves (272 B)
+constexpr int VSTR = 72;   // V^T row pitch in halves (144 B)
+constexpr float LOG2E_F = 1.4426950408889634f;
+
+__device__ __forceinline__ floatx4 mfma(const half8& a, const half8& b, const floatx4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {  // low halves of a, b
+  return (a & 0xFFFFu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {  // high halves of a, b
+  return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+template <int G>
+__global__ __launch_bounds__(PF_THREADS) void k_prefill(
+    const uint16_t* __restrict__ k16, const uint16_t* __restrict__ v16, long stride, int kvh,
+    int pos0, int n_tok, const float* __restrict__ q, float qscale, float* __restrict__ out,
+    int n_qblk) {
+  constexpr int BQ = PF_THREADS / G;  // queries per workgroup
+  const int h = blockIdx.x % kvh;
+  const int qb = n_qblk - 1 - (int)(blockIdx.x / kvh);  // longest rows first
+  const int q0 = qb * BQ;
+  const int nqh = kvh * G;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int P = pos0 + n_tok;
+  const int q_last = min(q0 + BQ, n_tok) - 1;
+  const int n_tiles = (pos0 + q_last + 1 + BK - 1) / BK;
+
+  __shared__ __attribute__((aligned(16))) _Float16 Ks[BK * KSTR];
+  __shared__ __attribute__((aligned(16))) _Float16 Vt[128 * VSTR];
+
+  // ---- Q rows of this wave, fp16 (RNE), as B fragments of S^T = K Q^T ----------
+  half8 qf[4][4];
+  int lim[4];  // last key a row may attend
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int R = 64 * wave + 16 * rb + l16;
+    const int i = q0 + R / G, g = R % G;
+    lim[rb] = min(pos0 + i, P - 1);
+    const float* src = q + ((long)i * nqh + h * G + g) * HD;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      half8 f;
+      if (i < n_tok) {
+        const float4 a = *reinterpret_cast<const float4*>(src + 32 * ks + 8 * g4);
+        const float4 b = *reinterpret_cast<const float4*>(src + 32 * ks + 8 * g4 + 4);
+        f[0] = (_Float16)a.x; f[1] = (_Float16)a.y; f[2] = (_Float16)a.z; f[3] = (_Float16)a.w;
+        f[4] = (_Float16)b.x; f[5] = (_Float16)b.y; f[6] = (_Float16)b.z; f[7] = (_Float16)b.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = (_Float16)0.0f;
+      }
+      qf[rb][ks] = f;
+    }
+  }
+  const int wave_lim_min = min(pos0 + q0 + (64 * wave) / G, P - 1);
+
+  floatx4 o[4][8];  // O^T[dim = 16db + 4*g4 + j][row = 16rb + l16]
+  float m[4], l[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    m[rb] = -INFINITY;
+    l[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[rb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // ---- staging: K tile row-major, V tile transposed --------------------------
+  uint4 kreg[4], vreg[4];
+  const int kq = tid & 15, dq = tid >> 4;  // V: keys 4kq..4kq+3, dims 8dq..8dq+7
+  auto gload = [&](int tile) {
+    const int k0 = tile * BK;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + PF_THREADS * u;
+      const int key = k0 + (c >> 4);
+      kreg[u] = key < P ? *reinterpret_cast<const uint4*>(k16 + ((long)h * stride + key) * HD +
+                                                          (c & 15) * 8)
+                        : make_uint4(0, 0, 0, 0);
+      const int vkey = k0 + 4 * kq + u;
+      vreg[u] = vkey < P ? *reinterpret_cast<const uint4*>(v16 + ((long)h * stride + vkey) * HD +
+                                                           8 * dq)
+                         : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + PF_THREADS * u;
+      *reinterpret_cast<uint4*>(&Ks[(c >> 4) * KSTR + (c & 15) * 8]) = kreg[u];
+    }
+    const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
+    const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
+    const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
+    const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {  // dims 2e and 2e+1 of the octet
+      const uint2 lo = make_uint2(pack_lo(w0[e], w1[e]), pack_lo(w2[e], w3[e]));
+      const uint2 hi = make_uint2(pack_hi(w0[e], w1[e]), pack_hi(w2[e], w3[e]));
+      *reinterpret_cast<uint2*>(&Vt[(8 * dq + 2 * e) * VSTR + 4 * kq]) = lo;
+      *reinterpret_cast<uint2*>(&Vt[(8 * dq + 2 * e + 1) * VSTR + 4 * kq]) = hi;
+    }
+  };
+
+  gload(0);
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    __syncthreads();  // every wave is done reading the previous tile
+    lstore();
+    __syncthreads();
+    if (tile + 1 < n_tiles) gload(tile + 1);
+    const int k0 = tile * BK;
+
+    // ---- S^T = K Q^T --------------------------------------------------------
+    floatx4 s[4][4];  // [kb][rb]: S^T[key = k0 + 16kb + 4*g4 + j][row = 16rb + l16]
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) s[kb][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const half8 a = *reinterpret_cast<const half8*>(&Ks[(16 * kb + l16) * KSTR + 32 * ks + 8 * g4]);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) s[kb][rb] = mfma(a, qf[rb][ks], s[kb][rb]);
+      }
+    }
+
+    // ---- online softmax (log2 units) -----------------------------------------
+    const bool need_mask = k0 + BK - 1 > wave_lim_min;
+    half8 pf[4][2];  // P^T fragments, k-slot (g4, e) -> key 4*g4 + e (e < 4), 16 + 4*g4 + e - 4
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v = s[kb][rb][j] * qscale;
+          if (need_mask && k0 + 16 * kb + 4 * g4 + j > lim[rb]) v = -INFINITY;
+          s[kb][rb][j] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[rb], mx);
+      const float alpha = exp2f(m[rb] - mnew);
+      m[rb] = mnew;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = exp2f(s[kb][rb][j] - mnew);
+          s[kb][rb][j] = p;
+          ls += p;
+        }
+      l[rb] = l[rb] * alpha + ls;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[rb][db] *= alpha;
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        half8 f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          f[j] = (_Float16)s[2 * ks2][rb][j];
+          f[4 + j] = (_Float16)s[2 * ks2 + 1][rb][j];
+        }
+        pf[rb][ks2] = f;
+      }
+    }
+
+    // ---- O^T += V^T P^T -------------------------------------------------------
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const _Float16* vp = &Vt[(16 * db + l16) * VSTR + 32 * ks2 + 4 * g4];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
+        const half8 a = __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) o[rb][db] = mfma(a, pf[rb][ks2], o[rb][db]);
+      }
+    }
+  }
+
+  // ---- normalise and store ----------------------------------------------------
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    float L = l[rb];
+    L += shfl_xor(L, 16);
+    L += shfl_xor(L, 32);
+    const int R = 64 * wave + 16 * rb + l16;
+    const int i = q0 + R / G, g = R % G;
+    if (i >= n_tok) continue;
+    float* dst = out + ((long)i * nqh + h * G + g) * HD;
+    const float inv = 1.0f / L;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const floatx4 v = o[rb][db] * inv;
+      *reinterpret_cast<float4*>(dst + 16 * db + 4 * g4) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(int kvh, int nqh, const uint16_t* k16, const uint16_t* v16,
+                          long row_stride, int pos0, int n_tok, const float* d_q,
+                          float sm_scale, float* d_out, hipStream_t st) {
+  const int G = nqh / kvh;
+  const int BQ = PF_THREADS / G;
+  const int n_qblk = (n_tok + BQ - 1) / BQ;
+  const long long blocks = (long long)n_qblk * kvh;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  const float qs = sm_scale * LOG2E_F;
+  dim3 grid((unsigned)blocks), block(PF_THREADS);
+  switch (G) {
+    case 1: hipLaunchKernelGGL(k_prefill<1>, grid, block, 0, st, k16, v16, row_stride, kvh, pos0, n_tok, d_q, qs, d_out, n_qblk); break;
+    case 2: hipLaunchKernelGGL(k_prefill<2>, grid, block, 0, st, k16, v16, row_stride, kvh, pos0, n_tok, d_q, qs, d_out, n_qblk); break;
+    case 4: hipLaunchKernelGGL(k_prefill<4>, grid, block, 0, st, k16, v16, row_stride, kvh, pos0, n_tok, d_q, qs, d_out, n_qblk); break;
+    case 8: hipLaunchKernelGGL(k_prefill<8>, grid, block, 0, st, k16, v16, row_stride, kvh, pos0, n_tok, d_q, qs, d_out, n_qblk); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvq8

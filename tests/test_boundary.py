@@ -1,0 +1,190 @@
+"""The C ABI on the host: symbols, byte accounting, and argument validation.
+
+No call here reaches a kernel launch: every argument error is detected before
+any HIP call, so these run without a GPU (a launch attempt would surface as
+KV_ERR_HIP and fail the test).  Pointers are fake, aligned, never dereferenced.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import oracle
+import quantized_kv_cache_q8_amd as kq
+
+HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "kvq8.h")
+L = kq.raw_lib()
+A = 0x7F0000000000          # fake, 256-byte aligned device addresses
+B = A + 0x100000
+C = A + 0x200000
+D = A + 0x300000
+F16, Q8 = kq.KV_FMT_F16, kq.KV_FMT_Q8
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(kq.EXPORTED), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_struct_layout():
+    assert ctypes.sizeof(kq.kv_session) == 40
+    assert ctypes.sizeof(kq.kv_shape) == 16
+
+
+def test_cache_bytes_matches_oracle():
+    for fmt in (F16, Q8):
+        for kvh, cap, hd in [(8, 262144, 128), (2, 1024, 128), (3, 64, 256), (1, 0, 64)]:
+            for part in (0, 1):
+                assert kq.kv_cache_bytes(fmt, kvh, cap, hd, part) == \
+                    oracle.cache_bytes(fmt, kvh, cap, hd, part)
+    assert kq.kv_cache_bytes(2, 8, 64, 128, 0) == 0
+    assert kq.kv_cache_bytes(Q8, 8, 64, 100, 0) == 0
+    assert kq.kv_cache_bytes(Q8, 8, 64, 128, 2) == 0
+
+
+def test_status_strings():
+    for s in range(-7, 1):
+        assert kq.kv_status_str(s) and kq.kv_status_str(s) != "unknown status"
+    assert kq.kv_status_str(-99) == "unknown status"
+
+
+def shape(fmt=Q8, kvh=8, nqh=32, hd=128):
+    return kq.make_shape(fmt, kvh, nqh, hd)
+
+
+_DEFAULT = object()
+
+
+def sess(fmt=Q8, cap=1024, k=A, v=B, ks=_DEFAULT, vs=_DEFAULT):
+    """Session entry; scale pointers default to C / D for Q8 and NULL for F16."""
+    if ks is _DEFAULT:
+        ks = C if fmt == Q8 else None
+    if vs is _DEFAULT:
+        vs = D if fmt == Q8 else None
+    return kq.kv_session(k, v, ks, vs, cap, 0)
+
+
+def append(sh, tab=A, lens=B, n_sess=1, n_tok=1, k=C, v=D, status=None):
+    return L.kv_append(ctypes.byref(sh) if sh is not None else None, tab, lens, n_sess, n_tok, k, v,
+                       status, None)
+
+
+def test_append_validation():
+    assert append(None) == kq.KV_ERR_ARG
+    assert append(shape(fmt=5)) == kq.KV_ERR_FMT
+    assert append(shape(nqh=30)) == kq.KV_ERR_ARG
+    assert append(shape(kvh=0)) == kq.KV_ERR_ARG
+    assert append(shape(hd=64)) == kq.KV_ERR_UNSUPPORTED
+    assert append(shape(kvh=2, nqh=6)) == kq.KV_ERR_UNSUPPORTED     # G = 3
+    assert append(shape(kvh=1, nqh=16)) == kq.KV_ERR_UNSUPPORTED    # G = 16
+    assert append(shape(), tab=None) == kq.KV_ERR_ARG
+    assert append(shape(), lens=None) == kq.KV_ERR_ARG
+    assert append(shape(), k=None) == kq.KV_ERR_ARG
+    assert append(shape(), n_sess=0) == kq.KV_ERR_ARG
+    assert append(shape(), n_tok=-1) == kq.KV_ERR_ARG
+    assert append(shape(), k=C + 4) == kq.KV_ERR_ALIGN
+    assert append(shape(), tab=A + 4) == kq.KV_ERR_ALIGN
+    assert append(shape(), lens=B + 2) == kq.KV_ERR_ALIGN
+    assert append(shape(), status=A + 1) == kq.KV_ERR_ALIGN
+    assert append(shape(), n_tok=0) == kq.KV_OK          # nothing to do, nothing launched
+
+
+def decode(sh, ws_bytes=None, tab=A, lens=B, n_sess=1, max_len=1024, q=C, out=D, ws=A + 0x400000,
+           sm=0.088):
+    need = L.kv_decode_workspace_bytes(ctypes.byref(sh), n_sess, max_len) if sh else 0
+    wsb = need if ws_bytes is None else ws_bytes
+    return L.kv_decode_attn(ctypes.byref(sh) if sh is not None else None, tab, lens, n_sess, max_len,
+                            q, sm, out, ws, wsb, None, None)
+
+
+def test_decode_validation():
+    assert decode(None) == kq.KV_ERR_ARG
+    assert decode(shape(fmt=-1)) == kq.KV_ERR_FMT
+    assert decode(shape(hd=256)) == kq.KV_ERR_UNSUPPORTED
+    assert decode(shape(), tab=None) == kq.KV_ERR_ARG
+    assert decode(shape(), q=None) == kq.KV_ERR_ARG
+    assert decode(shape(), out=None) == kq.KV_ERR_ARG
+    assert decode(shape(), n_sess=0) == kq.KV_ERR_ARG
+    assert decode(shape(), max_len=-1) == kq.KV_ERR_ARG
+    assert decode(shape(), sm=math.inf) == kq.KV_ERR_ARG
+    assert decode(shape(), sm=math.nan) == kq.KV_ERR_ARG
+    assert decode(shape(), q=C + 8) == kq.KV_ERR_ALIGN
+    assert decode(shape(), out=D + 4) == kq.KV_ERR_ALIGN
+    assert decode(shape(), ws=A + 0x400008) == kq.KV_ERR_ALIGN
+    assert decode(shape(), ws=None) == kq.KV_ERR_WORKSPACE
+    need = L.kv_decode_workspace_bytes(ctypes.byref(shape()), 1, 1024)
+    assert decode(shape(), ws_bytes=need - 1) == kq.KV_ERR_WORKSPACE
+
+
+def test_decode_workspace_bytes():
+    sh = shape()
+    # full context, one session: (o, lse) per query head and split, 256-byte aligned parts
+    ws = L.kv_decode_workspace_bytes(ctypes.byref(sh), 1, 262144)
+    assert ws >= 32 * 128 * 4 * (262144 // 1024)
+    assert ws % 256 == 0
+    assert L.kv_decode_workspace_bytes(ctypes.byref(sh), 0, 10) == 0
+    assert L.kv_decode_workspace_bytes(ctypes.byref(shape(hd=64)), 1, 10) == 0
+    # grows with sessions and length
+    assert L.kv_decode_workspace_bytes(ctypes.byref(sh), 64, 65536) > ws
+
+
+def compact(sh, se, P=64, k16=C, v16=D):
+    return L.kv_compact_f16(ctypes.byref(sh), ctypes.byref(se) if se is not None else None, P, k16,
+                            v16, None)
+
+
+def test_compact_validation():
+    assert compact(shape(), None) == kq.KV_ERR_ARG
+    assert compact(shape(), sess(k=None)) == kq.KV_ERR_ARG
+    assert compact(shape(fmt=Q8), sess(fmt=Q8, ks=None)) == kq.KV_ERR_FMT
+    assert compact(shape(fmt=F16), sess(fmt=F16, ks=C, vs=D)) == kq.KV_ERR_FMT   # F16 with scales
+    assert compact(shape(fmt=F16), sess(fmt=Q8)) == kq.KV_ERR_FMT
+    assert compact(shape(), sess(k=A + 8)) == kq.KV_ERR_ALIGN
+    assert compact(shape(), sess(vs=D + 2)) == kq.KV_ERR_ALIGN
+    assert compact(shape(), sess(cap=1000)) == kq.KV_ERR_ALIGN
+    assert compact(shape(), sess(cap=0)) == kq.KV_ERR_ALIGN
+    assert compact(shape(), sess(), P=0) == kq.KV_ERR_ARG
+    assert compact(shape(), sess(), k16=None) == kq.KV_ERR_ARG
+    assert compact(shape(), sess(), v16=D + 2) == kq.KV_ERR_ALIGN
+    assert compact(shape(), sess(cap=1024), P=1025) == kq.KV_ERR_RANGE
+
+
+def prefill(sh, se, pos0=0, n_tok=16, q=A, out=B, ws=C, ws_bytes=None, sm=0.1):
+    need = L.kv_prefill_workspace_bytes(ctypes.byref(sh), pos0 + n_tok)
+    wsb = need if ws_bytes is None else ws_bytes
+    return L.kv_prefill_attn(ctypes.byref(sh), ctypes.byref(se) if se is not None else None, pos0,
+                             n_tok, q, sm, out, ws, wsb, None)
+
+
+def test_prefill_validation():
+    assert prefill(shape(), None) == kq.KV_ERR_ARG
+    assert prefill(shape(fmt=F16), sess(fmt=Q8)) == kq.KV_ERR_FMT
+    assert prefill(shape(), sess(), q=None) == kq.KV_ERR_ARG
+    assert prefill(shape(), sess(), pos0=-1) == kq.KV_ERR_ARG
+    assert prefill(shape(), sess(), n_tok=-2) == kq.KV_ERR_ARG
+    assert prefill(shape(), sess(), sm=math.inf) == kq.KV_ERR_ARG
+    assert prefill(shape(), sess(), q=A + 4) == kq.KV_ERR_ALIGN
+    assert prefill(shape(), sess(cap=1024), pos0=1000, n_tok=25) == kq.KV_ERR_RANGE
+    assert prefill(shape(), sess(), ws=None) == kq.KV_ERR_WORKSPACE
+    assert prefill(shape(), sess(), ws_bytes=100) == kq.KV_ERR_WORKSPACE
+    assert prefill(shape(), sess(), n_tok=0) == kq.KV_OK
+    # F16 needs no workspace (the cache is read in place)
+    assert L.kv_prefill_workspace_bytes(ctypes.byref(shape(fmt=F16)), 4096) == 0
+    assert L.kv_prefill_workspace_bytes(ctypes.byref(shape(fmt=Q8)), 135168) == \
+        2 * 8 * 135168 * 128 * 2
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_supported_head_ratios_pass_shape_checks(G):
+    # reaches the workspace check (so the shape was accepted)
+    assert decode(shape(kvh=2, nqh=2 * G), ws=None) == kq.KV_ERR_WORKSPACE
