@@ -201,9 +201,10 @@ def prefill_side(kq, torch, seed, steps, warmup):
         "flop": flop}
 
 
-def cpu_baseline_leg(seed):
-    """The oracle, as it stands, on a bounded sample of the workload: 2 of the 8 kv
-    heads of one layer at 262144 cells, both formats (cache write + decode)."""
+def cpu_baseline_leg(seed, repeats=2):
+    """The oracle, as it stands, on a bounded sample of the workload: one of the 48
+    layers (8 kv heads, 32 query heads, 262144 cells), both formats: cache write
+    of every cell, then the fp64 decode (repeated)."""
     import kvsynth
     import oracle
     try:
@@ -211,33 +212,36 @@ def cpu_baseline_leg(seed):
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         blas_threads = 1
-    kv_s = 2
-    xk = kvsynth.kv_tokens(seed, 0, CTX, KVH, HD, "K", outliers=True)[:, :kv_s].copy()
-    xv = kvsynth.kv_tokens(seed, 0, CTX, KVH, HD, "V", outliers=True)[:, :kv_s].copy()
-    q = kvsynth.queries(seed, 0, 1, NQH, HD)[0][: kv_s * (NQH // KVH)]
+    xk = kvsynth.kv_tokens(seed, 0, CTX, KVH, HD, "K", outliers=True)
+    xv = kvsynth.kv_tokens(seed, 0, CTX, KVH, HD, "V", outliers=True)
+    q = kvsynth.queries(seed, 0, 1, NQH, HD)[0]
     res = {}
     total_bytes, total_s = 0, 0.0
     for fmt in (F16, Q8):
         t0 = time.perf_counter()
-        c = oracle.Cache(fmt, kv_s, CTX, HD)
+        c = oracle.Cache(fmt, KVH, CTX, HD)
         c.append(0, xk, xv)
         t1 = time.perf_counter()
-        K = c.dequant("k", CTX)
-        V = c.dequant("v", CTX)
-        oracle.decode_attn(q, K, V, CTX, 1 / math.sqrt(HD))
+        for _ in range(repeats):
+            K = c.dequant("k", CTX)
+            V = c.dequant("v", CTX)
+            oracle.decode_attn(q, K, V, CTX, 1 / math.sqrt(HD))
+            del K, V
         t2 = time.perf_counter()
-        nbytes = CTX * kv_s * BYTES_PER_CELL_HEAD[fmt]
+        nbytes = decode_bytes(fmt, CTX) * repeats
         res["f16" if fmt == F16 else "int8"] = {
-            "decode_GB_s": nbytes / (t2 - t1) / 1e9, "decode_s": t2 - t1,
-            "append_cells_per_s": CTX * kv_s / KVH / (t1 - t0)}
+            "decode_GB_s": nbytes / (t2 - t1) / 1e9, "decode_s": (t2 - t1) / repeats,
+            "append_cells_per_s": CTX / (t1 - t0), "append_s": t1 - t0}
         total_bytes += nbytes
         total_s += t2 - t1
+        del c
     cores = len(os.sched_getaffinity(0))
     return {"value": total_bytes / total_s / 1e9, "unit": "GB/s", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": f"one layer, 2 of 8 kv heads (8 query heads), 262144 cells, FP16 and int8: "
-                      f"cache write then fp64 decode; value = decode K/V bytes / decode time; "
-                      f"numpy elementwise work on 1 thread, BLAS on {blas_threads} of {cores} cores",
+            "sample": f"one layer of the workload (8 kv heads, 32 query heads, 262144 cells), "
+                      f"FP16 and int8: oracle cache write of every cell, then its fp64 decode "
+                      f"{repeats}x; value = decode K/V bytes / decode time; numpy elementwise "
+                      f"work on 1 thread, BLAS on {blas_threads} of {cores} cores",
             "host_cores": cores, "per_format": res}
 
 

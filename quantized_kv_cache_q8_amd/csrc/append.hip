@@ -87,19 +87,14 @@ __global__ __launch_bounds__(APPEND_THREADS) void k_append(
       const uint32_t packed = (uint32_t)(c[0] & 0xFF) | ((uint32_t)(c[1] & 0xFF) << 8) |
                               ((uint32_t)(c[2] & 0xFF) << 16) | ((uint32_t)(c[3] & 0xFF) << 24);
       if (store) {
-        int8_t* dst = static_cast<int8_t*>(o.which ? s.v : s.k) + row * HD + sub * 4;
-        *reinterpret_cast<uint32_t*>(dst) = packed;
-        if ((sub & 15) == 0) {
-          uint16_t* sd = (o.which ? s.v_scale : s.k_scale) + row * NGRP + (sub >> 4);
-          *sd = sbits;
-        }
+        stg32(static_cast<int8_t*>(o.which ? s.v : s.k) + row * HD + sub * 4, packed);
+        if ((sub & 15) == 0) stg16((o.which ? s.v_scale : s.k_scale) + row * NGRP + (sub >> 4), sbits);
       }
     } else {
       const uint32_t lo = (uint32_t)f2h(x[p].x) | ((uint32_t)f2h(x[p].y) << 16);
       const uint32_t hi = (uint32_t)f2h(x[p].z) | ((uint32_t)f2h(x[p].w) << 16);
       if (store) {
-        uint16_t* dst = static_cast<uint16_t*>(o.which ? s.v : s.k) + row * HD + sub * 4;
-        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+        stg64(static_cast<uint16_t*>(o.which ? s.v : s.k) + row * HD + sub * 4, u32x2{lo, hi});
       }
     }
     if (in[p] && bad && sub == 0 && o.t == 0 && o.h == 0 && o.which == 0) flag(status, bad);

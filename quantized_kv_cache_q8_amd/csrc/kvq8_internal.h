@@ -22,10 +22,12 @@ constexpr int DPP_ROW_HALF_MIRROR = 0x141; // lane i <-> 7-i within 8 lanes
 constexpr int DPP_ROW_MIRROR = 0x140;      // lane i <-> 15-i within 16 lanes
 constexpr int DPP_ROW_ROR8 = 0x128;       // rotate a 16-lane row by 8
 
+// every control used here reads a lane inside the same 16-lane row, so no source is
+// out of range; bound_ctrl lets the compiler fold the move into the consuming add
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
 // sum over the 8 lanes {8k .. 8k+7}; every lane of the 8 gets the total
@@ -66,6 +68,43 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int m = 1; m < 64; m <<= 1) v += shfl_xor(v, m);
   return v;
 }
+
+// ---------------------------------------------------------------------------
+// Global-memory access through address space 1.  Pointers read from session
+// tables are generic to the compiler; casting them lets it emit global_load /
+// global_store (counted by vmcnt only) instead of flat accesses.
+// ---------------------------------------------------------------------------
+#define KVQ8_GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 ldg128(const void* p) {
+  return *(const KVQ8_GLOBAL u32x4*)(p);
+}
+// streaming (non-temporal) 128-bit load: data read once, not kept in the caches
+__device__ __forceinline__ u32x4 ldg128_nt(const void* p) {
+  return __builtin_nontemporal_load((const KVQ8_GLOBAL u32x4*)(p));
+}
+__device__ __forceinline__ uint16_t ldg16(const void* p) {
+  return *(const KVQ8_GLOBAL uint16_t*)(p);
+}
+__device__ __forceinline__ void stg128(void* p, u32x4 v) {
+  *(KVQ8_GLOBAL u32x4*)(p) = v;
+}
+__device__ __forceinline__ void stg64(void* p, u32x2 v) {
+  *(KVQ8_GLOBAL u32x2*)(p) = v;
+}
+__device__ __forceinline__ void stg32(void* p, uint32_t v) {
+  *(KVQ8_GLOBAL uint32_t*)(p) = v;
+}
+__device__ __forceinline__ void stg16(void* p, uint16_t v) {
+  *(KVQ8_GLOBAL uint16_t*)(p) = v;
+}
+
+// Reinterpret a 32-bit word as fp32.  Takes the word by value: applying
+// __builtin_bit_cast directly to an ext_vector element (v[i]) reads element 0
+// with this compiler, so vector elements must pass through a scalar first.
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 
 // ---------------------------------------------------------------------------
 // fp16 bit helpers (IEEE binary16; conversions round to nearest even)

@@ -12,8 +12,9 @@
 //   each 16-row block; the 16 keys of a lane are reduced in registers, then across
 //   the 4 lane groups)
 //   O^T[dim][row] += V^T P^T  A = V^T from LDS, B = P^T straight from the S^T
-//   accumulators (fp16), using one consistent assignment of keys to MFMA k-slots
-//   for both operands, so no data moves between lanes.
+//   accumulators (as hi + lo fp16 parts, two products), using one consistent
+//   assignment of keys to MFMA k-slots for both operands, so no data moves
+//   between lanes.
 // K is staged row-major with a 272-byte row pitch, V transposed with a 144-byte
 // pitch, both free of LDS bank conflicts on the fragment reads.  The next tile's
 // global loads are in flight while the current tile computes.
@@ -164,7 +165,10 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
 
     // ---- online softmax (log2 units) -----------------------------------------
     const bool need_mask = k0 + BK - 1 > wave_lim_min;
-    half8 pf[4][2];  // P^T fragments, k-slot (g4, e) -> key 4*g4 + e (e < 4), 16 + 4*g4 + e - 4
+    // P^T fragments, k-slot (g4, e) -> key 4*g4 + e (e < 4), 16 + 4*g4 + e - 4.  P is
+    // carried as hi + lo fp16 parts (hi = fp16(p), lo = fp16(p - hi)), so the P V
+    // product keeps ~22 significant bits of each weight instead of 11.
+    half8 pf[4][2], pl[4][2];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       float mx = -INFINITY;
@@ -196,13 +200,17 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
       for (int db = 0; db < 8; ++db) o[rb][db] *= alpha;
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
-        half8 f;
+        half8 f, fl;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          f[j] = (_Float16)s[2 * ks2][rb][j];
-          f[4 + j] = (_Float16)s[2 * ks2 + 1][rb][j];
+          const float p0 = s[2 * ks2][rb][j], p1 = s[2 * ks2 + 1][rb][j];
+          f[j] = (_Float16)p0;
+          f[4 + j] = (_Float16)p1;
+          fl[j] = (_Float16)(p0 - (float)f[j]);
+          fl[4 + j] = (_Float16)(p1 - (float)f[4 + j]);
         }
         pf[rb][ks2] = f;
+        pl[rb][ks2] = fl;
       }
     }
 
@@ -216,7 +224,10 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
         const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
         const half8 a = __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) o[rb][db] = mfma(a, pf[rb][ks2], o[rb][db]);
+        for (int rb = 0; rb < 4; ++rb) {
+          o[rb][db] = mfma(a, pf[rb][ks2], o[rb][db]);
+          o[rb][db] = mfma(a, pl[rb][ks2], o[rb][db]);
+        }
       }
     }
   }

@@ -89,7 +89,7 @@ def test_worked_examples_and_every_fp16_scale():
 @pytest.mark.parametrize("fmt", [F16, Q8])
 def test_sentinels_ranges_and_batched_sessions(fmt):
     kvh, hd = 3, 128
-    sh = shape(fmt, kvh, 3 * kvh)
+    sh = shape(fmt, kvh, kvh)
     caps = [128, 64, 192, 128]
     lens = [13, 60, 0, 125]          # session 1 and 3 do not fit 7 tokens
     n_tok = 7
