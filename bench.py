@@ -201,7 +201,37 @@ def prefill_side(kq, torch, seed, steps, warmup):
         "flop": flop}
 
 
-def cpu_baseline_leg(seed, repeats=2):
+def traffic_probe(kq, torch, seed):
+    """Kernels for counter collection (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
+    import kvsynth
+    # calibration: an elementwise kernel that reads exactly 1 GiB and writes 1 GiB
+    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.add(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    del a, b
+    xk = torch.from_numpy(kvsynth.kv_tokens(seed, 0, CTX, KVH, HD, "K", True)[None]).cuda()
+    xv = torch.from_numpy(kvsynth.kv_tokens(seed, 0, CTX, KVH, HD, "V", True)[None]).cuda()
+    q = torch.from_numpy(kvsynth.queries(seed, 0, 1, NQH, HD)).cuda()
+    out = torch.empty((1, NQH, HD), device="cuda")
+    for fmt in (F16, Q8):
+        sh = kq.make_shape(fmt, KVH, NQH, HD)
+        s = kq.Session(fmt, KVH, CTX)
+        tab = kq.session_table([s.entry()])
+        lens = torch.zeros(1, dtype=torch.int32, device="cuda")
+        kq.kv_append(sh, tab, lens, 1, CTX, xk, xv)
+        lens.fill_(CTX)
+        ws = torch.empty(kq.kv_decode_workspace_bytes(sh, 1, CTX), dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            kq.kv_decode_attn(sh, tab, lens, 1, CTX, q, 1 / math.sqrt(HD), out, ws)
+        torch.cuda.synchronize()
+        del s
+    log("traffic probe done")
+
+
+def cpu_baseline_leg(seed, repeats=4):
     """The oracle, as it stands, on a bounded sample of the workload: one of the 48
     layers (8 kv heads, 32 query heads, 262144 cells), both formats: cache write
     of every cell, then the fp64 decode (repeated)."""
@@ -254,6 +284,10 @@ def main():
     ap.add_argument("--seed", type=int, default=44)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run only what the HBM-traffic counters are read on: a 1 GiB device "
+                         "copy (calibration), then per format one 262144-cell layer: bulk "
+                         "append and 3 decodes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (--gpus {args.gpus} "
@@ -265,6 +299,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     import quantized_kv_cache_q8_amd as kq
+
+    if args.traffic_probe:
+        traffic_probe(kq, torch, args.seed)
+        return
 
     n_steps, n_warm = args.steps, args.warmup
     cap = ((CTX + 63) // 64) * 64

@@ -68,7 +68,8 @@ int kv_append(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d
 
 size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_len) {
   if (check_shape(h_shape) || n_sess < 1 || max_len < 0) return 0;
-  const DecodePlan p = decode_plan(h_shape->n_kv_heads, h_shape->n_q_heads, n_sess, max_len);
+  const DecodePlan p =
+      decode_plan(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, n_sess, max_len);
   return p.ws_o_bytes + p.ws_lse_bytes;
 }
 
@@ -82,8 +83,10 @@ int kv_decode_attn(const kv_shape* h_shape, const kv_session* d_tab, const int32
   if ((reinterpret_cast<uintptr_t>(d_tab) & 7) || !aligned4(d_len) || !aligned16(d_q) ||
       !aligned16(d_out) || !aligned16(d_ws) || !aligned4(d_status))
     return KV_ERR_ALIGN;
-  const DecodePlan p = decode_plan(h_shape->n_kv_heads, h_shape->n_q_heads, n_sess, max_len);
-  if (d_ws == nullptr || ws_bytes < p.ws_o_bytes + p.ws_lse_bytes) return KV_ERR_WORKSPACE;
+  if (d_ws == nullptr) return KV_ERR_WORKSPACE;
+  const DecodePlan p =
+      decode_plan(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, n_sess, max_len);
+  if (ws_bytes < p.ws_o_bytes + p.ws_lse_bytes) return KV_ERR_WORKSPACE;
   return hip_status(launch_decode(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, d_tab,
                                   d_len, n_sess, max_len, d_q, sm_scale, d_out, d_ws, p, d_status,
                                   static_cast<hipStream_t>(stream)));

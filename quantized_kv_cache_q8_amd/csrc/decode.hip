@@ -3,21 +3,28 @@
 // and Extra Notes: the next token's split-K decode reads the cache, FP16 or int8,
 // with no conversion pass).
 //
-// k_decode_split: one workgroup = (split s, kv head h, session b), T tokens.
-//   Each of its 4 waves owns T/4 consecutive tokens and works in two passes:
-//   K pass   lane (r = lane/8, c = lane%8) holds dims [16c, 16c+16) of token r of
-//            each 8-token step: 128-bit loads (int8: 16 codes; fp16: 2 x 8 halves),
-//            dequant in registers, partial dots for the G query heads, the int8
-//            group scale applied to the partial, and an 8-lane DPP sum; logits
-//            (already in log2 units) go to LDS.
-//   softmax  wave max and exp2 over its logits; p back to LDS.
-//   V pass   same lane mapping, acc[g][16 dims] += p * scale * v.
-//   The 4 wave partials are combined in LDS and written as one (o, lse) per
-//   query head and split (o normalised, lse in log2 units).
+// k_decode_split: grid (S splits, kv head h, session b), 4 waves per workgroup.
+//   Work is counted in 8-token steps (one 128-bit load per lane covers a step of
+//   one head: 8 rows x 8 lanes).  The W = 4S waves of a (session, head) take the
+//   steps round-robin -- wave gw owns steps gw, gw + W, gw + 2W, ... -- so all of
+//   them sweep that head's K/V together, front by front, as one stream.
+//   A wave works through its steps in chunks of CH steps, two passes per chunk:
+//   K pass   lane (r = lane/8, c = lane%8) holds 16 dims of token r of a step:
+//            in-register dequant, partial dots for the G query heads, the int8
+//            group scale applied to the partial, an 8-lane DPP sum; logits (log2
+//            units) go to LDS.
+//   softmax  chunk max, rescale of the running (m, l, acc), exp2.
+//   V pass   acc[g][16 dims] += p * scale * v.
+//   Load batches alternate between two register sets so the next batch is in
+//   flight while one is consumed.  The 4 wave partials are combined in LDS and
+//   written as one (o, lse) per query head and split (o normalised, lse in log2).
 // k_decode_merge: out = sum_j 2^(lse_j - L) o_j with L = log2 sum_j 2^lse_j.
 //
 // Dequantised values are exact in fp32 (a 7-bit code times an 11-bit fp16
 // significand), so the only rounding is fp32 accumulation.
+#include <algorithm>
+#include <atomic>
+
 #include "kvq8_internal.h"
 
 namespace kvq8 {
@@ -28,7 +35,11 @@ namespace {
 #define KVQ8_DEC_U_Q8 4
 #endif
 #ifndef KVQ8_DEC_U_F16
-#define KVQ8_DEC_U_F16 2
+#define KVQ8_DEC_U_F16 1
+#endif
+// most 8-token steps one wave handles (the per-wave LDS logits buffer)
+#ifndef KVQ8_DEC_CH
+#define KVQ8_DEC_CH 128
 #endif
 // K/V rows are read once per decode: non-temporal loads keep them out of the caches
 #ifndef KVQ8_DEC_NT
@@ -38,9 +49,8 @@ namespace {
 #ifndef KVQ8_DEC_WAVES_PER_EU
 #define KVQ8_DEC_WAVES_PER_EU 1
 #endif
-// largest tokens per workgroup the split heuristic may pick
-#ifndef KVQ8_DEC_T_MAX
-#define KVQ8_DEC_T_MAX 1024
+#ifndef KVQ8_MAX_DEVICES
+#define KVQ8_MAX_DEVICES 64
 #endif
 
 __device__ __forceinline__ u32x4 ldkv(const void* p) {
@@ -129,18 +139,21 @@ __device__ __forceinline__ void store_logits(float* dst, const float (&v)[G], bo
   }
 }
 
-// One batch of U rows (8 tokens each per wave) of K or V for one lane: U x 16 values
-// and, for int8, the U raw fp16 scales of the lane's 64-dim group.
+constexpr int CH = KVQ8_DEC_CH;  // most steps per wave (LDS holds its logits)
+
+// One batch of U steps for one lane: U x 16 values and, for int8, the U raw fp16
+// scales of the lane's 64-dim group.
 template <int FMT, int U>
 struct Batch {
   Chunk<FMT> ch[U];
   uint16_t sc[U];
-  // rows past w1 re-read the last valid row (in bounds); callers mask them
+  // steps k .. k+U-1 of wave gw; tokens past len re-read the last cell (in bounds)
+  // and are masked by the callers
   __device__ __forceinline__ void load(const void* vals, const uint16_t* scales, long long rowbase,
-                                       int w0, int w1, int it0, int r, int c) {
+                                       int gw, int W, int k, int len, int r, int c) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const long long row = rowbase + min(w0 + (it0 + u) * 8 + r, w1 - 1);
+      const long long row = rowbase + min((gw + (k + u) * W) * 8 + r, len - 1);
       ch[u].load(vals, row, c);
       if constexpr (FMT == KV_FMT_Q8) sc[u] = ldg16(scales + row * NGRP + (c >> 2));
     }
@@ -151,32 +164,38 @@ struct Batch {
   }
 };
 
+// LDS of one split workgroup: per-wave logits for CH steps, the wave partials
+template <int G>
+__host__ __device__ constexpr size_t split_lds_bytes() {
+  return sizeof(float) * ((size_t)DEC_WAVES * CH * 8 * G + DEC_WAVES * G * HD + 2 * DEC_WAVES * G);
+}
+
 template <int FMT, int G, int U>
 __global__ __launch_bounds__(DEC_THREADS)
 __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int kvh,
     const float* __restrict__ q, float qscale, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, int S, int T) {
+    float* __restrict__ ws_lse, int S) {
+  static_assert(CH % (2 * U) == 0, "a chunk holds whole pairs of load batches");
   const int s_idx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int nqh = kvh * G;
   const kv_session ss = tab[b];
   const int len = lens[b];
   if (session_bad(ss, FMT) || len < 0 || len > ss.cap || len > max_len) return;  // merge flags
-  const int t_begin = s_idx * T;
-  if (t_begin >= len) return;
-  const int t_end = min(t_begin + T, len);
+  const int J = (len + 7) >> 3;                  // 8-token steps of this session
+  if (s_idx * DEC_WAVES >= J) return;            // no step for this workgroup
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane >> 3, c = lane & 7;
-  const int Tw = T / DEC_WAVES;
-  const int w0 = t_begin + wave * Tw;
-  const int w1 = min(w0 + Tw, t_end);
+  const int gw = s_idx * DEC_WAVES + wave;       // wave index within (session, head)
+  const int W = S * DEC_WAVES;                   // waves per (session, head)
+  const int n_steps = gw < J ? (J - 1 - gw) / W + 1 : 0;
 
   extern __shared__ float smem[];
-  float* lg = smem + wave * Tw * G;                 // [Tw][G] logits, then p
-  float* o_l = smem + DEC_WAVES * Tw * G;           // [waves][G][HD]
-  float* m_l = o_l + DEC_WAVES * G * HD;            // [waves][G]
-  float* l_l = m_l + DEC_WAVES * G;                 // [waves][G]
+  float* lg = smem + wave * CH * 8 * G;          // [CH*8][G] logits, then p
+  float* o_l = smem + DEC_WAVES * CH * 8 * G;    // [waves][G][HD]
+  float* m_l = o_l + DEC_WAVES * G * HD;         // [waves][G]
+  float* l_l = m_l + DEC_WAVES * G;              // [waves][G]
 
   const long long rowbase = (long long)h * ss.cap;
   float m[G], l[G], acc[G][16];
@@ -188,100 +207,58 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
   }
 
-  if (w1 > w0) {
-    const int n_it = (w1 - w0 + 7) >> 3;
-    // Two load batches A and B alternate (a 2x-unrolled loop, no register copies):
-    // while one is consumed the other is in flight.  Steps past n_it read clamped,
-    // in-bounds rows and are masked.  The last K step prefetches V batch 0 into A,
-    // so its loads overlap the softmax.
-    Batch<FMT, U> A, B;
-    A.load(ss.k, ss.k_scale, rowbase, w0, w1, 0, r, c);
-    // ---- K pass ---------------------------------------------------------
-    {
-      float qv[G][16];
+  if (n_steps > 0) {
+    float qv[G][16];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float* qp = q + ((long long)b * nqh + h * G + g) * HD;
+    for (int g = 0; g < G; ++g) {
+      const float* qp = q + ((long long)b * nqh + h * G + g) * HD;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const u32x4 v = ldg128(qp + lane_dim<FMT>(c, 4 * k));   // 4 consecutive dims
+      for (int k = 0; k < 4; ++k) {
+        const u32x4 v = ldg128(qp + lane_dim<FMT>(c, 4 * k));   // 4 consecutive dims
 #pragma unroll
-          for (int e = 0; e < 4; ++e) qv[g][4 * k + e] = as_f32(v[e]) * qscale;
-        }
+        for (int e = 0; e < 4; ++e) qv[g][4 * k + e] = as_f32(v[e]) * qscale;
       }
-      // U x G independent dot products, interleaved so that no FMA waits on the one
-      // just before it; then the U x G 8-lane reductions, then the logit stores
-      auto kstep = [&](const Batch<FMT, U>& cur, int it0) {
-        float part[U][G];
+    }
+    // U x G independent dot products, interleaved so that no FMA waits on the one
+    // just before it; then the U x G 8-lane reductions, then the logit stores
+    auto kstep = [&](const Batch<FMT, U>& cur, int k0, int it0, int n_it) {
+      float part[U][G];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-          for (int g = 0; g < G; ++g) part[u][g] = 0.f;
+        for (int g = 0; g < G; ++g) part[u][g] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-#pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const float kf = cur.ch[u].get(i);
-#pragma unroll
-            for (int g = 0; g < G; ++g) part[u][g] = fmaf(qv[g][i], kf, part[u][g]);
-          }
-        }
+      for (int i = 0; i < 16; ++i) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const float sc = cur.scale(u);
+          const float kf = cur.ch[u].get(i);
 #pragma unroll
-          for (int g = 0; g < G; ++g)
-            if constexpr (FMT == KV_FMT_Q8) part[u][g] *= sc;
+          for (int g = 0; g < G; ++g) part[u][g] = fmaf(qv[g][i], kf, part[u][g]);
         }
+      }
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+        const float sc = cur.scale(u);
 #pragma unroll
-          for (int g = 0; g < G; ++g) part[u][g] = sum8(part[u][g]);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int it = it0 + u;
-          const int t = w0 + it * 8 + r;
-          if (c == 0 && it < n_it) store_logits<G>(lg + (it * 8 + r) * G, part[u], t < w1);
+        for (int g = 0; g < G; ++g) {
+          if constexpr (FMT == KV_FMT_Q8) part[u][g] *= sc;
+          part[u][g] = sum8(part[u][g]);
         }
-      };
-      for (int it0 = 0; it0 < n_it; it0 += 2 * U) {
-        B.load(ss.k, ss.k_scale, rowbase, w0, w1, it0 + U, r, c);
-        kstep(A, it0);
-        if (it0 + 2 * U < n_it)
-          A.load(ss.k, ss.k_scale, rowbase, w0, w1, it0 + 2 * U, r, c);
-        else
-          A.load(ss.v, ss.v_scale, rowbase, w0, w1, 0, r, c);
-        kstep(B, it0 + U);
       }
-    }
-    wave_lds_fence();
-    // ---- softmax over the wave's tokens --------------------------------------
-    const int n_loc = n_it * 8;
-    for (int tl = lane; tl < n_loc; tl += 64) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) m[g] = fmaxf(m[g], lg[tl * G + g]);
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) m[g] = wave_max(m[g]);
-    for (int tl = lane; tl < n_loc; tl += 64) {
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float p = exp2f(lg[tl * G + g] - m[g]);
-        lg[tl * G + g] = p;
-        l[g] += p;
+      for (int u = 0; u < U; ++u) {
+        const int it = it0 + u;
+        const int t = (gw + (k0 + it) * W) * 8 + r;
+        if (c == 0 && it < n_it) store_logits<G>(lg + (it * 8 + r) * G, part[u], t < len);
       }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) l[g] = wave_sum(l[g]);
-    wave_lds_fence();
-    // ---- V pass ---------------------------------------------------------------
-    auto vstep = [&](const Batch<FMT, U>& cur, int it0) {
+    };
+    auto vstep = [&](const Batch<FMT, U>& cur, int it0, int n_it) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int it = it0 + u;
         const float sc = cur.scale(u);
-        // p is 0 for rows past the end (their logits were stored as -inf); steps past
-        // n_it read stale LDS (in bounds: Tw/8 is a multiple of 2U) and are zeroed
+        // p is 0 for tokens past the end (their logits were stored as -inf); slots
+        // past n_it hold stale LDS (in bounds: CH is a multiple of 2U) and are zeroed
         float w[G];
         load_p<G>(lg + (it * 8 + r) * G, w);
 #pragma unroll
@@ -294,11 +271,52 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
         }
       }
     };
+
+    // Two load batches A and B alternate (a 2x-unrolled loop, no register copies);
+    // the last K batch of a chunk prefetches its first V batch, the last V batch the
+    // next chunk's first K batch, so loads stay in flight across the softmax.
+    // Two load batches A and B alternate (a 2x-unrolled loop, no register copies);
+    // the last K batch prefetches the first V batch, whose loads then overlap the
+    // softmax.  The plan gives every wave at most CH steps (n_it <= CH).
+    const int n_it = n_steps;
+    Batch<FMT, U> A, B;
+    A.load(ss.k, ss.k_scale, rowbase, gw, W, 0, len, r, c);
+    // ---- K pass ---------------------------------------------------------------
     for (int it0 = 0; it0 < n_it; it0 += 2 * U) {
-      B.load(ss.v, ss.v_scale, rowbase, w0, w1, it0 + U, r, c);
-      vstep(A, it0);
-      if (it0 + 2 * U < n_it) A.load(ss.v, ss.v_scale, rowbase, w0, w1, it0 + 2 * U, r, c);
-      vstep(B, it0 + U);
+      B.load(ss.k, ss.k_scale, rowbase, gw, W, it0 + U, len, r, c);
+      kstep(A, 0, it0, n_it);
+      if (it0 + 2 * U < n_it)
+        A.load(ss.k, ss.k_scale, rowbase, gw, W, it0 + 2 * U, len, r, c);
+      else
+        A.load(ss.v, ss.v_scale, rowbase, gw, W, 0, len, r, c);
+      kstep(B, 0, it0 + U, n_it);
+    }
+    wave_lds_fence();
+    // ---- softmax over the wave's tokens ---------------------------------------
+    const int n_loc = n_it * 8;
+    for (int tl = lane; tl < n_loc; tl += 64) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) m[g] = fmaxf(m[g], lg[tl * G + g]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) m[g] = wave_max(m[g]);   // finite: step 0 has token gw*8
+    for (int tl = lane; tl < n_loc; tl += 64) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float p = exp2f(lg[tl * G + g] - m[g]);
+        lg[tl * G + g] = p;
+        l[g] += p;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) l[g] = wave_sum(l[g]);
+    wave_lds_fence();
+    // ---- V pass ---------------------------------------------------------------
+    for (int it0 = 0; it0 < n_it; it0 += 2 * U) {
+      B.load(ss.v, ss.v_scale, rowbase, gw, W, it0 + U, len, r, c);
+      vstep(A, it0, n_it);
+      if (it0 + 2 * U < n_it) A.load(ss.v, ss.v_scale, rowbase, gw, W, it0 + 2 * U, len, r, c);
+      vstep(B, it0 + U, n_it);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -373,7 +391,7 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 template <int FMT>
 __global__ __launch_bounds__(DEC_THREADS) void k_decode_merge(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int nqh,
-    const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int S, int T,
+    const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int S,
     float* __restrict__ out, int32_t* __restrict__ status) {
   const int qh = blockIdx.x, b = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -389,7 +407,8 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode_merge(
   }
   __shared__ float red[DEC_WAVES];
   __shared__ float2 part[DEC_WAVES][64];
-  const int Sb = (len + T - 1) / T;
+  // workgroups that received a step: those with 4s < ceil(len / 8)
+  const int Sb = min(S, (((len + 7) >> 3) + DEC_WAVES - 1) / DEC_WAVES);
   const float* lse = ws_lse + ((long long)b * nqh + qh) * S;
   const float* o = ws_o + ((long long)b * nqh + qh) * S * HD;
   float mx = -INFINITY;
@@ -444,37 +463,83 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode_merge(
   }
 }
 
+template <int FMT>
+constexpr int batch_rows() {
+  return FMT == KV_FMT_Q8 ? KVQ8_DEC_U_Q8 : KVQ8_DEC_U_F16;
+}
+
+// Split workgroups of one kernel instance that fit on the current device at once
+// (CUs x resident workgroups per CU), cached per device; 0 when unknown.
+template <int FMT, int G>
+int resident_splits() {
+  static std::atomic<int> cache[KVQ8_MAX_DEVICES];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= KVQ8_MAX_DEVICES) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, k_decode_split<FMT, G, batch_rows<FMT>()>, DEC_THREADS,
+          split_lds_bytes<G>()) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  v = per_cu * cus;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+int resident(int fmt, int G) {
+#define KVQ8_RES(F, GG) \
+  if (fmt == F && G == GG) return resident_splits<F, GG>();
+  KVQ8_RES(KV_FMT_Q8, 1)
+  KVQ8_RES(KV_FMT_Q8, 2)
+  KVQ8_RES(KV_FMT_Q8, 4)
+  KVQ8_RES(KV_FMT_Q8, 8)
+  KVQ8_RES(KV_FMT_F16, 1)
+  KVQ8_RES(KV_FMT_F16, 2)
+  KVQ8_RES(KV_FMT_F16, 4)
+  KVQ8_RES(KV_FMT_F16, 8)
+#undef KVQ8_RES
+  return 0;
+}
+
 template <int FMT, int G>
 hipError_t launch_g(const kv_session* tab, const int32_t* lens, int n_sess, int max_len, int kvh,
                     const float* q, float sm_scale, float* out, float* ws_o, float* ws_lse,
                     const DecodePlan& plan, int32_t* status, hipStream_t st) {
-  constexpr int U = (FMT == KV_FMT_Q8) ? KVQ8_DEC_U_Q8 : KVQ8_DEC_U_F16;
-  static_assert(U == 1 || U == 2 || U == 4 || U == 8, "U must divide 8");
-  if ((plan.T / DEC_WAVES / 8) % (2 * U) != 0) return hipErrorInvalidValue;
-  const size_t lds = sizeof(float) * ((size_t)plan.T * G + DEC_WAVES * G * HD + 2 * DEC_WAVES * G);
+  constexpr int U = batch_rows<FMT>();
+  static_assert(U == 1 || U == 2 || U == 4, "U must divide CH / 2");
   dim3 grid(plan.S, kvh, n_sess), block(DEC_THREADS);
-  hipLaunchKernelGGL((k_decode_split<FMT, G, U>), grid, block, lds, st, tab, lens, max_len, kvh, q,
-                     sm_scale * LOG2E, ws_o, ws_lse, plan.S, plan.T);
+  hipLaunchKernelGGL((k_decode_split<FMT, G, U>), grid, block, split_lds_bytes<G>(), st, tab, lens,
+                     max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 mgrid(kvh * G, n_sess);
   hipLaunchKernelGGL((k_decode_merge<FMT>), mgrid, block, 0, st, tab, lens, max_len, kvh * G, ws_o,
-                     ws_lse, plan.S, plan.T, out, status);
+                     ws_lse, plan.S, out, status);
   return hipGetLastError();
 }
 
 }  // namespace
 
-DecodePlan decode_plan(int kvh, int nqh, int n_sess, int max_len) {
-  const int G = nqh / kvh;
-  // Largest T (tokens per workgroup) that still gives >= 2048 workgroups (8 per CU on
-  // 256 CUs); at least 256, at most 8192 / G so the logits fit in 32 KB of LDS.
-  int T = 8192 / G;
-  if (T > KVQ8_DEC_T_MAX) T = KVQ8_DEC_T_MAX;
-  while (T > 256 && (long long)n_sess * kvh * ((max_len + T - 1) / T) < 2048) T >>= 1;
+DecodePlan decode_plan(int fmt, int kvh, int nqh, int n_sess, int max_len) {
+  // Splits per (session, kv head): enough that no wave has more than CH steps, then
+  // raised so that the grid is a whole number of rounds of resident workgroups (a
+  // last, partly filled round would leave CUs idle), but not past one split per 4
+  // steps (so every workgroup has work).
+  const long long J = ((long long)max_len + 7) / 8;
+  const long long P = (long long)kvh * n_sess;
+  // S0 keeps every wave at <= CH steps (the kernel's LDS holds CH steps of logits)
+  const long long S0 = std::max(1LL, (J + DEC_WAVES * CH - 1) / (DEC_WAVES * CH));
+  long long S = S0;
+  const long long C = resident(fmt, nqh / kvh);
+  if (C > 0) {
+    const long long rounds = (P * S0 + C - 1) / C;
+    S = std::max(S0, (rounds * C + P - 1) / P);
+  }
+  S = std::min(S, std::max(S0, (J + DEC_WAVES - 1) / DEC_WAVES));
   DecodePlan p;
-  p.T = T;
-  p.S = max_len > 0 ? (max_len + T - 1) / T : 1;
+  p.S = (int)S;
   const size_t rows = (size_t)n_sess * nqh * p.S;
   p.ws_o_bytes = (rows * HD * sizeof(float) + 255) & ~(size_t)255;
   p.ws_lse_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;

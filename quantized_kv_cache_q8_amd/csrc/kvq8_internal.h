@@ -145,11 +145,12 @@ hipError_t launch_append(int fmt, int kvh, const kv_session* d_tab, const int32_
                          int32_t* d_status, hipStream_t st);
 
 struct DecodePlan {
-  int T;      // tokens per split (per workgroup)
-  int S;      // splits per session (grid x)
+  int S;      // splits (workgroups) per (session, kv head): grid x
   size_t ws_o_bytes, ws_lse_bytes;
 };
-DecodePlan decode_plan(int kvh, int nqh, int n_sess, int max_len);
+// depends on the arguments and on how many split workgroups the current device
+// holds at once (queried once per device)
+DecodePlan decode_plan(int fmt, int kvh, int nqh, int n_sess, int max_len);
 hipError_t launch_decode(int fmt, int kvh, int nqh, const kv_session* d_tab,
                          const int32_t* d_len, int n_sess, int max_len, const float* d_q,
                          float sm_scale, float* d_out, void* d_ws, const DecodePlan& plan,
