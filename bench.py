@@ -201,15 +201,19 @@ def prefill_side(kq, torch, seed, steps, warmup):
         "flop": flop}
 
 
+CALIB_BYTES = 3 << 28   # 768 MiB: a size no other copy in the probe has
+
+
 def traffic_probe(kq, torch, seed):
-    """Kernels for counter collection (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
+    """Kernels for counter collection (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE): a
+    plain device-to-device copy of CALIB_BYTES (the calibration), then per format
+    one 262144-cell layer: bulk append and 3 decodes."""
     import kvsynth
-    # calibration: an elementwise kernel that reads exactly 1 GiB and writes 1 GiB
-    a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     torch.cuda.synchronize()
     for _ in range(3):
-        torch.add(a, 1.0, out=b)
+        b.copy_(a)
     torch.cuda.synchronize()
     del a, b
     xk = torch.from_numpy(kvsynth.kv_tokens(seed, 0, CTX, KVH, HD, "K", True)[None]).cuda()
@@ -229,6 +233,71 @@ def traffic_probe(kq, torch, seed):
         torch.cuda.synchronize()
         del s
     log("traffic probe done")
+
+
+def traffic_summary(fetch_dir, write_dir, command):
+    """Turn the counter CSVs of two `--traffic-probe` runs (FETCH_SIZE, then
+    WRITE_SIZE; KiB per dispatch) into profiles/hbm_traffic.json.  Each counter is
+    scaled by expected / measured on the calibration copy (CALIB_BYTES read and
+    written); dispatches of the two runs pair up by dispatch id (same program)."""
+    import csv
+    import glob
+
+    def load(d, counter):
+        rows = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter:
+                    rows[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]))
+        if not rows:
+            raise SystemExit(f"no {counter} rows under {d}")
+        return rows
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    exp_kib = CALIB_BYTES / 1024
+    calib = [i for i, (n, v) in write.items() if "copyBuffer" in n and abs(v - exp_kib) < 0.02 * exp_kib]
+    if not calib or any(i not in fetch for i in calib):
+        raise SystemExit("calibration copy not found in both runs")
+    f_fac = exp_kib / float(np.mean([fetch[i][1] for i in calib]))
+    w_fac = exp_kib / float(np.mean([write[i][1] for i in calib]))
+    out = {"command": command, "calibration": {
+        "kernel": "__amd_rocclr_copyBuffer (device-to-device copy)", "bytes_read": CALIB_BYTES,
+        "bytes_written": CALIB_BYTES, "dispatches": len(calib),
+        "fetch_KiB": float(np.mean([fetch[i][1] for i in calib])),
+        "write_KiB": float(np.mean([write[i][1] for i in calib])),
+        "fetch_factor": f_fac, "write_factor": w_fac}}
+    ids = sorted(fetch)
+    for fmt, key in ((F16, "decode_f16"), (Q8, "decode_int8")):
+        # one kv_decode_attn call = one k_decode_split<fmt,...> then one k_decode_merge<fmt>
+        tag = f"k_decode_split<{fmt},"
+        splits = [i for i in ids if tag in fetch[i][0]]
+        per = []
+        for i in splits:
+            j = i + 1
+            assert f"k_decode_merge<{fmt}>" in fetch[j][0], fetch[j][0]
+            fk = fetch[i][1] + fetch[j][1]
+            wk = write[i][1] + write[j][1]
+            per.append((fk, wk, fk * 1024 * f_fac + wk * 1024 * w_fac))
+        per = np.array(per)
+        out[key] = {"source_hash": source_hash("decode.hip"), "launches": len(per),
+                    "context": CTX, "fetch_KiB": float(per[:, 0].mean()),
+                    "write_KiB": float(per[:, 1].mean()),
+                    "bytes_per_launch": float(per[:, 2].mean()),
+                    "algorithmic_bytes_per_launch": decode_bytes(fmt, CTX),
+                    "ratio_to_algorithmic": float(per[:, 2].mean()) / decode_bytes(fmt, CTX)}
+    for fmt, key in ((F16, "append_f16"), (Q8, "append_int8")):
+        a = [i for i in ids if f"k_append<{fmt}>" in fetch[i][0]]
+        fk = float(np.mean([fetch[i][1] for i in a]))
+        wk = float(np.mean([write[i][1] for i in a]))
+        alg = CTX * KVH * 2 * HD * 4 + CTX * KVH * BYTES_PER_CELL_HEAD[fmt]
+        out[key] = {"source_hash": source_hash("append.hip"), "cells": CTX, "fetch_KiB": fk,
+                    "write_KiB": wk, "bytes_per_launch": fk * 1024 * f_fac + wk * 1024 * w_fac,
+                    "algorithmic_bytes_per_launch": alg}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline_leg(seed, repeats=4):
@@ -285,10 +354,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
-                    help="run only what the HBM-traffic counters are read on: a 1 GiB device "
+                    help="run only what the HBM-traffic counters are read on: a 768 MiB device "
                          "copy (calibration), then per format one 262144-cell layer: bulk "
                          "append and 3 decodes")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="(no GPU) write profiles/hbm_traffic.json from the rocprofv3 counter "
+                         "output of two --traffic-probe runs")
+    ap.add_argument("--traffic-command", default="",
+                    help="with --traffic-summary: the rocprofv3 commands, recorded in the file")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary, args.traffic_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path has no multi-GPU mode (--gpus {args.gpus} "
               "requested). Run with --gpus 1.", file=sys.stderr)

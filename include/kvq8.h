@@ -101,7 +101,10 @@ int kv_append(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d
               int n_sess, int n_tok, const float* d_k_new, const float* d_v_new,
               int32_t* d_status, void* stream);
 
-/* Workspace for kv_decode_attn: split-K partials.  Depends only on its arguments. */
+/* Workspace for kv_decode_attn: split-K partials.  Depends on its arguments and on
+ * the current HIP device (the split count follows that device's occupancy); query
+ * it with the device current that kv_decode_attn will run on.  0 on invalid
+ * arguments. */
 size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_len);
 
 /* Split-K decode attention of one new token per session over the cache, reading
@@ -115,7 +118,7 @@ size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_le
  *   max_len : host upper bound of every d_len[b] (sizes the grid); a session over it
  *             is flagged KV_DEV_RANGE and gets a zero row.
  *   d_ws, ws_bytes : at least kv_decode_workspace_bytes(h_shape, n_sess, max_len).
- * Deterministic: the same inputs give bitwise the same output. */
+ * Deterministic: the same inputs on the same device give bitwise the same output. */
 int kv_decode_attn(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d_len,
                    int n_sess, int max_len, const float* d_q, float sm_scale, float* d_out,
                    void* d_ws, size_t ws_bytes, int32_t* d_status, void* stream);
