@@ -139,7 +139,9 @@ size_t kv_prefill_workspace_bytes(const kv_shape* h_shape, int P);
  * must already be appended at rows [pos0, pos0 + n_tok).  Row i (position pos0 + i)
  * of query head q attends keys [0, pos0 + i] of kv head q / G:
  *   out[i][q] = sum_t softmax_t(sm_scale * fp16(q_i) . K16[t]) V16[t]
- * with the softmax weights rounded to fp16 before the P V product.
+ * with each softmax weight carried into the P V product as the sum of two fp16
+ * values (about 22 significant bits).
+ *   sm_scale : finite and > 0, else KV_ERR_ARG
  *   d_q  : fp32 [n_tok][n_q_heads][head_dim];  d_out : fp32 [n_tok][n_q_heads][head_dim]
  *   d_ws : at least kv_prefill_workspace_bytes(h_shape, pos0 + n_tok) (may be NULL if 0). */
 int kv_prefill_attn(const kv_shape* h_shape, const kv_session* h_sess, int pos0, int n_tok,

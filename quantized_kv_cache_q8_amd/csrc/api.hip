@@ -119,7 +119,8 @@ int kv_prefill_attn(const kv_shape* h_shape, const kv_session* h_sess, int pos0,
   if (rc) return rc;
   rc = check_session(h_shape, h_sess);
   if (rc) return rc;
-  if (d_q == nullptr || d_out == nullptr || pos0 < 0 || n_tok < 0 || !std::isfinite(sm_scale))
+  if (d_q == nullptr || d_out == nullptr || pos0 < 0 || n_tok < 0 || !std::isfinite(sm_scale) ||
+      !(sm_scale > 0.0f))
     return KV_ERR_ARG;
   if (!aligned16(d_q) || !aligned16(d_out) || !aligned16(d_ws)) return KV_ERR_ALIGN;
   if ((long long)pos0 + n_tok > h_sess->cap) return KV_ERR_RANGE;

@@ -34,6 +34,7 @@ constexpr int BK = 64;     // keys per tile
 constexpr int KSTR = 136;  // K row pitch in halves (272 B)
 constexpr int VSTR = 72;   // V^T row pitch in halves (144 B)
 constexpr float LOG2E_F = 1.4426950408889634f;
+constexpr float PF_PRE = 15.0f;  // log2 scale of p (p <= 2^15)
 
 __device__ __forceinline__ floatx4 mfma(const half8& a, const half8& b, const floatx4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -164,10 +165,14 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
     }
 
     // ---- online softmax (log2 units) -----------------------------------------
+    // p is computed as 2^(s*qscale - m + PF_PRE): the fixed factor keeps the weights
+    // that matter clear of the fp16 subnormals (p <= 2^PF_PRE stays finite in fp16); O
+    // and l carry the same factor, which the final division removes.
     const bool need_mask = k0 + BK - 1 > wave_lim_min;
     // P^T fragments, k-slot (g4, e) -> key 4*g4 + e (e < 4), 16 + 4*g4 + e - 4.  P is
-    // carried as hi + lo fp16 parts (hi = fp16(p), lo = fp16(p - hi)), so the P V
-    // product keeps ~22 significant bits of each weight instead of 11.
+    // carried as hi + lo fp16 parts: hi = p with its low 13 fraction bits cleared (an
+    // exact fp16 value), lo = p - hi (exact in fp32), so the P V product keeps ~22
+    // significant bits of each weight instead of 11.
     half8 pf[4][2], pl[4][2];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
@@ -176,22 +181,23 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float v = s[kb][rb][j] * qscale;
+          float v = s[kb][rb][j];
           if (need_mask && k0 + 16 * kb + 4 * g4 + j > lim[rb]) v = -INFINITY;
           s[kb][rb][j] = v;
           mx = fmaxf(mx, v);
         }
       mx = fmaxf(mx, shfl_xor(mx, 16));
       mx = fmaxf(mx, shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[rb], mx);
-      const float alpha = exp2f(m[rb] - mnew);
+      const float mnew = fmaxf(m[rb], mx * qscale);   // qscale > 0 (checked by the caller)
+      const float alpha = __builtin_amdgcn_exp2f(m[rb] - mnew);
       m[rb] = mnew;
+      const float mb = mnew - PF_PRE;
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p = exp2f(s[kb][rb][j] - mnew);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][rb][j], qscale, -mb));
           s[kb][rb][j] = p;
           ls += p;
         }
@@ -200,17 +206,19 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
       for (int db = 0; db < 8; ++db) o[rb][db] *= alpha;
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
-        half8 f, fl;
+        uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = s[2 * ks2][rb][j], p1 = s[2 * ks2 + 1][rb][j];
-          f[j] = (_Float16)p0;
-          f[4 + j] = (_Float16)p1;
-          fl[j] = (_Float16)(p0 - (float)f[j]);
-          fl[4 + j] = (_Float16)(p1 - (float)f[4 + j]);
+        for (int e = 0; e < 4; ++e) {
+          // pairs (j, j+1) of key block 2*ks2 (e < 2) and 2*ks2 + 1 (e >= 2)
+          const int kb = 2 * ks2 + (e >> 1), j = 2 * (e & 1);
+          const float p0 = s[kb][rb][j], p1 = s[kb][rb][j + 1];
+          const float h0 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p0) & 0xFFFFE000u);
+          const float h1 = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, p1) & 0xFFFFE000u);
+          hw[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(h0, h1));
+          lw[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0 - h0, p1 - h1));
         }
-        pf[rb][ks2] = f;
-        pl[rb][ks2] = fl;
+        pf[rb][ks2] = __builtin_bit_cast(half8, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+        pl[rb][ks2] = __builtin_bit_cast(half8, make_uint4(lw[0], lw[1], lw[2], lw[3]));
       }
     }
 

@@ -175,6 +175,8 @@ def test_prefill_validation():
     assert prefill(shape(), sess(), pos0=-1) == kq.KV_ERR_ARG
     assert prefill(shape(), sess(), n_tok=-2) == kq.KV_ERR_ARG
     assert prefill(shape(), sess(), sm=math.inf) == kq.KV_ERR_ARG
+    assert prefill(shape(), sess(), sm=0.0) == kq.KV_ERR_ARG
+    assert prefill(shape(), sess(), sm=-0.5) == kq.KV_ERR_ARG
     assert prefill(shape(), sess(), q=A + 4) == kq.KV_ERR_ALIGN
     assert prefill(shape(), sess(cap=1024), pos0=1000, n_tok=25) == kq.KV_ERR_RANGE
     assert prefill(shape(), sess(), ws=None) == kq.KV_ERR_WORKSPACE
