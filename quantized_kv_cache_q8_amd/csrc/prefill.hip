@@ -4,7 +4,9 @@
 //
 // Workgroup = (kv head h, block of BQ = 256/G queries); its 256 rows are the
 // (query, head) pairs of the G query heads sharing kv head h, so one K/V tile in
-// LDS serves all of them.  Wave w owns rows [64w, 64w + 64) as 4 blocks of 16.
+// LDS serves all of them.  8 waves, two per SIMD: wave w owns rows [32w, 32w + 32)
+// as 2 blocks of 16, so its O accumulators (64 per lane) stay in ordinary VGPRs and
+// one wave's matrix products overlap the other wave's softmax arithmetic.
 //
 // Per 64-key tile, with v_mfma_f32_16x16x32_f16 (fp16 in, fp32 accumulate):
 //   S^T[key][row] = K Q^T    A = K rows from LDS, B = the wave's Q rows (registers)
@@ -16,8 +18,9 @@
 //   assignment of keys to MFMA k-slots for both operands, so no data moves
 //   between lanes.
 // K is staged row-major with a 272-byte row pitch, V transposed with a 144-byte
-// pitch, both free of LDS bank conflicts on the fragment reads.  The next tile's
-// global loads are in flight while the current tile computes.
+// pitch, both free of LDS bank conflicts on the fragment reads.  Tiles alternate
+// between two LDS buffers: the next tile's global loads are in flight while the
+// current tile computes, and one barrier per tile suffices.
 // Workgroups are numbered so that consecutive ones take different kv heads: the
 // hardware deals workgroups round-robin to the 8 XCDs, so with 8 kv heads each
 // XCD's L2 serves the K/V of one head to every query block of that head.
@@ -29,7 +32,8 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int PF_THREADS = 256;
+constexpr int PF_ROWS = 256;    // (query, head) rows per workgroup
+constexpr int PF_THREADS = 512; // 8 waves x 32 rows
 constexpr int BK = 64;     // keys per tile
 constexpr int KSTR = 136;  // K row pitch in halves (272 B)
 constexpr int VSTR = 72;   // V^T row pitch in halves (144 B)
@@ -52,7 +56,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
     const uint16_t* __restrict__ k16, const uint16_t* __restrict__ v16, long stride, int kvh,
     int pos0, int n_tok, const float* __restrict__ q, float qscale, float* __restrict__ out,
     int n_qblk) {
-  constexpr int BQ = PF_THREADS / G;  // queries per workgroup
+  constexpr int BQ = PF_ROWS / G;  // queries per workgroup
   const int h = blockIdx.x % kvh;
   const int qb = n_qblk - 1 - (int)(blockIdx.x / kvh);  // longest rows first
   const int q0 = qb * BQ;
@@ -64,15 +68,15 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
   const int q_last = min(q0 + BQ, n_tok) - 1;
   const int n_tiles = (pos0 + q_last + 1 + BK - 1) / BK;
 
-  __shared__ __attribute__((aligned(16))) _Float16 Ks[BK * KSTR];
-  __shared__ __attribute__((aligned(16))) _Float16 Vt[128 * VSTR];
+  __shared__ __attribute__((aligned(16))) _Float16 Ks[2][BK * KSTR];
+  __shared__ __attribute__((aligned(16))) _Float16 Vt[2][128 * VSTR];
 
   // ---- Q rows of this wave, fp16 (RNE), as B fragments of S^T = K Q^T ----------
-  half8 qf[4][4];
-  int lim[4];  // last key a row may attend
+  half8 qf[2][4];
+  int lim[2];  // last key a row may attend
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int R = 64 * wave + 16 * rb + l16;
+  for (int rb = 0; rb < 2; ++rb) {
+    const int R = 32 * wave + 16 * rb + l16;
     const int i = q0 + R / G, g = R % G;
     lim[rb] = min(pos0 + i, P - 1);
     const float* src = q + ((long)i * nqh + h * G + g) * HD;
@@ -91,12 +95,12 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
       qf[rb][ks] = f;
     }
   }
-  const int wave_lim_min = min(pos0 + q0 + (64 * wave) / G, P - 1);
+  const int wave_lim_min = min(pos0 + q0 + (32 * wave) / G, P - 1);
 
-  floatx4 o[4][8];  // O^T[dim = 16db + 4*g4 + j][row = 16rb + l16]
-  float m[4], l[4];
+  floatx4 o[2][8];  // O^T[dim = 16db + 4*g4 + j][row = 16rb + l16]
+  float m[2], l[2];
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
+  for (int rb = 0; rb < 2; ++rb) {
     m[rb] = -INFINITY;
     l[rb] = 0.f;
 #pragma unroll
@@ -104,63 +108,64 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
   }
 
   // ---- staging: K tile row-major, V tile transposed --------------------------
-  uint4 kreg[4], vreg[4];
-  const int kq = tid & 15, dq = tid >> 4;  // V: keys 4kq..4kq+3, dims 8dq..8dq+7
+  // K: 1024 chunks of 8 halves, 2 per thread.  V: thread holds keys 2kq, 2kq + 1 of
+  // dims 8dq .. 8dq + 7.
+  uint4 kreg[2], vreg[2];
+  const int kq = tid & 31, dq = tid >> 5;
   auto gload = [&](int tile) {
     const int k0 = tile * BK;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2; ++u) {
       const int c = tid + PF_THREADS * u;
       const int key = k0 + (c >> 4);
       kreg[u] = key < P ? *reinterpret_cast<const uint4*>(k16 + ((long)h * stride + key) * HD +
                                                           (c & 15) * 8)
                         : make_uint4(0, 0, 0, 0);
-      const int vkey = k0 + 4 * kq + u;
+      const int vkey = k0 + 2 * kq + u;
       vreg[u] = vkey < P ? *reinterpret_cast<const uint4*>(v16 + ((long)h * stride + vkey) * HD +
                                                            8 * dq)
                          : make_uint4(0, 0, 0, 0);
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2; ++u) {
       const int c = tid + PF_THREADS * u;
-      *reinterpret_cast<uint4*>(&Ks[(c >> 4) * KSTR + (c & 15) * 8]) = kreg[u];
+      *reinterpret_cast<uint4*>(&Ks[buf][(c >> 4) * KSTR + (c & 15) * 8]) = kreg[u];
     }
     const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
     const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-    const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-    const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {  // dims 2e and 2e+1 of the octet
-      const uint2 lo = make_uint2(pack_lo(w0[e], w1[e]), pack_lo(w2[e], w3[e]));
-      const uint2 hi = make_uint2(pack_hi(w0[e], w1[e]), pack_hi(w2[e], w3[e]));
-      *reinterpret_cast<uint2*>(&Vt[(8 * dq + 2 * e) * VSTR + 4 * kq]) = lo;
-      *reinterpret_cast<uint2*>(&Vt[(8 * dq + 2 * e + 1) * VSTR + 4 * kq]) = hi;
+    for (int e = 0; e < 4; ++e) {  // dims 2e and 2e+1 of the octet, keys 2kq and 2kq + 1
+      *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * dq + 2 * e) * VSTR + 2 * kq]) = pack_lo(w0[e], w1[e]);
+      *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * dq + 2 * e + 1) * VSTR + 2 * kq]) = pack_hi(w0[e], w1[e]);
     }
   };
 
   gload(0);
+  lstore(0);
+  __syncthreads();
   for (int tile = 0; tile < n_tiles; ++tile) {
-    __syncthreads();  // every wave is done reading the previous tile
-    lstore();
-    __syncthreads();
-    if (tile + 1 < n_tiles) gload(tile + 1);
+    const int cur = tile & 1;
+    const bool more = tile + 1 < n_tiles;
+    if (more) gload(tile + 1);
     const int k0 = tile * BK;
+    const _Float16* KsC = Ks[cur];
+    const _Float16* VtC = Vt[cur];
 
     // ---- S^T = K Q^T --------------------------------------------------------
-    floatx4 s[4][4];  // [kb][rb]: S^T[key = k0 + 16kb + 4*g4 + j][row = 16rb + l16]
+    floatx4 s[4][2];  // [kb][rb]: S^T[key = k0 + 16kb + 4*g4 + j][row = 16rb + l16]
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) s[kb][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < 2; ++rb) s[kb][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const half8 a = *reinterpret_cast<const half8*>(&Ks[(16 * kb + l16) * KSTR + 32 * ks + 8 * g4]);
+        const half8 a = *reinterpret_cast<const half8*>(&KsC[(16 * kb + l16) * KSTR + 32 * ks + 8 * g4]);
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) s[kb][rb] = mfma(a, qf[rb][ks], s[kb][rb]);
+        for (int rb = 0; rb < 2; ++rb) s[kb][rb] = mfma(a, qf[rb][ks], s[kb][rb]);
       }
     }
 
@@ -173,9 +178,9 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
     // carried as hi + lo fp16 parts: hi = p with its low 13 fraction bits cleared (an
     // exact fp16 value), lo = p - hi (exact in fp32), so the P V product keeps ~22
     // significant bits of each weight instead of 11.
-    half8 pf[4][2], pl[4][2];
+    half8 pf[2][2], pl[2][2];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < 2; ++rb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -227,26 +232,31 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
     for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const _Float16* vp = &Vt[(16 * db + l16) * VSTR + 32 * ks2 + 4 * g4];
+        const _Float16* vp = &VtC[(16 * db + l16) * VSTR + 32 * ks2 + 4 * g4];
         const uint2 lo = *reinterpret_cast<const uint2*>(vp);
         const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
         const half8 a = __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
+        for (int rb = 0; rb < 2; ++rb) {
           o[rb][db] = mfma(a, pf[rb][ks2], o[rb][db]);
           o[rb][db] = mfma(a, pl[rb][ks2], o[rb][db]);
         }
       }
     }
+
+    // the other buffer was last read in the previous tile, which every wave finished
+    // before the barrier that ended it
+    if (more) lstore(cur ^ 1);
+    __syncthreads();
   }
 
   // ---- normalise and store ----------------------------------------------------
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
+  for (int rb = 0; rb < 2; ++rb) {
     float L = l[rb];
     L += shfl_xor(L, 16);
     L += shfl_xor(L, 32);
-    const int R = 64 * wave + 16 * rb + l16;
+    const int R = 32 * wave + 16 * rb + l16;
     const int i = q0 + R / G, g = R % G;
     if (i >= n_tok) continue;
     float* dst = out + ((long)i * nqh + h * G + g) * HD;
@@ -265,7 +275,7 @@ hipError_t launch_prefill(int kvh, int nqh, const uint16_t* k16, const uint16_t*
                           long row_stride, int pos0, int n_tok, const float* d_q,
                           float sm_scale, float* d_out, hipStream_t st) {
   const int G = nqh / kvh;
-  const int BQ = PF_THREADS / G;
+  const int BQ = PF_ROWS / G;
   const int n_qblk = (n_tok + BQ - 1) / BQ;
   const long long blocks = (long long)n_qblk * kvh;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
