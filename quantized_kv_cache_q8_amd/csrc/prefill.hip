@@ -178,25 +178,45 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
     // carried as hi + lo fp16 parts: hi = p with its low 13 fraction bits cleared (an
     // exact fp16 value), lo = p - hi (exact in fp32), so the P V product keeps ~22
     // significant bits of each weight instead of 11.
-    half8 pf[2][2], pl[2][2];
+    if (need_mask) {   // only tiles that reach past some row's last key
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (k0 + 16 * kb + 4 * g4 + j > lim[rb]) s[kb][rb][j] = -INFINITY;
+    }
+    float alpha[2];
+    bool moved = false;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float v = s[kb][rb][j];
-          if (need_mask && k0 + 16 * kb + 4 * g4 + j > lim[rb]) v = -INFINITY;
-          s[kb][rb][j] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[kb][rb][j]);
       mx = fmaxf(mx, shfl_xor(mx, 16));
       mx = fmaxf(mx, shfl_xor(mx, 32));
       const float mnew = fmaxf(m[rb], mx * qscale);   // qscale > 0 (checked by the caller)
-      const float alpha = __builtin_amdgcn_exp2f(m[rb] - mnew);
+      moved |= mnew != m[rb];
+      alpha[rb] = __builtin_amdgcn_exp2f(m[rb] - mnew);
       m[rb] = mnew;
-      const float mb = mnew - PF_PRE;
+    }
+    // O only needs rescaling when some row of the wave raised its maximum: after the
+    // first tiles that is rare, and the branch is uniform
+    if (__ballot(moved) != 0) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        l[rb] *= alpha[rb];
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[rb][db] *= alpha[rb];
+      }
+    }
+    half8 pf[2][2], pl[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float mb = m[rb] - PF_PRE;
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -206,9 +226,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
           s[kb][rb][j] = p;
           ls += p;
         }
-      l[rb] = l[rb] * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) o[rb][db] *= alpha;
+      l[rb] += ls;
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
         uint32_t hw[4], lw[4];
