@@ -17,7 +17,7 @@
 //   accumulators (as hi + lo fp16 parts, two products), using one consistent
 //   assignment of keys to MFMA k-slots for both operands, so no data moves
 //   between lanes.
-// K is staged row-major with a 272-byte row pitch, V transposed with a 144-byte
+// K is staged row-major with a 288-byte row pitch, V transposed with a 136-byte
 // pitch, both free of LDS bank conflicts on the fragment reads.  Tiles alternate
 // between two LDS buffers: the next tile's global loads are in flight while the
 // current tile computes, and one barrier per tile suffices.
@@ -35,8 +35,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int PF_ROWS = 256;    // (query, head) rows per workgroup
 constexpr int PF_THREADS = 512; // 8 waves x 32 rows
 constexpr int BK = 64;     // keys per tile
-constexpr int KSTR = 136;  // K row pitch in halves (272 B)
-constexpr int VSTR = 72;   // V^T row pitch in halves (144 B)
+constexpr int KSTR = 144;  // K row pitch in halves (288 B)
+constexpr int VSTR = 68;   // V^T row pitch in halves (136 B)
 constexpr float LOG2E_F = 1.4426950408889634f;
 constexpr float PF_PRE = 15.0f;  // log2 scale of p (p <= 2^15)
 
