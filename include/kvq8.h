@@ -91,7 +91,7 @@ size_t kv_cache_bytes(int fmt, int n_kv_heads, int cap, int head_dim, int part);
  * with IEEE fp32 division and round-to-nearest-even; code = clamp(rint(x / s),
  * -127, 127) dividing (IEEE fp32) by the stored fp16 scale; a zero scale stores
  * code 0.  F16 stores fp16_rne(x).
- *   d_tab   : kv_session [n_sess] (device)
+ *   d_tab   : kv_session [n_sess] (device), 1 <= n_sess <= 65535
  *   d_len   : int32 [n_sess] (device): session b's cells go to rows
  *             [d_len[b], d_len[b] + n_tok).  NOT modified (the caller advances it).
  *   d_k_new, d_v_new : fp32 [n_sess][n_tok][n_kv_heads][head_dim] (device)

@@ -57,7 +57,7 @@ int kv_append(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d
   if (rc) return rc;
   if (d_tab == nullptr || d_len == nullptr || d_k_new == nullptr || d_v_new == nullptr)
     return KV_ERR_ARG;
-  if (n_sess < 1 || n_tok < 0) return KV_ERR_ARG;
+  if (n_sess < 1 || n_sess > 65535 || n_tok < 0) return KV_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(d_tab) & 7) || !aligned4(d_len) || !aligned16(d_k_new) ||
       !aligned16(d_v_new) || !aligned4(d_status))
     return KV_ERR_ALIGN;

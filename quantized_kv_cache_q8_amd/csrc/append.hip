@@ -11,67 +11,57 @@
 // 64-dim group is one 16-lane DPP row, so the group max is four DPP steps and
 // needs no LDS and no workgroup barrier (the page's kernel needed a block-wide
 // barrier for the same max; here every lane reaches the DPP steps and only the
-// stores are guarded).  A wave covers two rows per step and keeps ROWS_PAIRS
-// steps of loads in flight.
+// stores are guarded).  A wave covers two rows (tokens) per step and keeps
+// ROW_PAIRS steps of loads in flight; a block covers 32 tokens of one head of K or
+// of V of one session.
 #include "kvq8_internal.h"
 
 namespace kvq8 {
 namespace {
 
 constexpr int APPEND_THREADS = 256;
-constexpr int ROW_PAIRS = 4;  // row pairs per wave
+constexpr int ROW_PAIRS = 4;                                      // row pairs per wave
+constexpr int TOK_PER_BLOCK = (APPEND_THREADS / 64) * ROW_PAIRS * 2;  // 32
 
-struct RowRef {
-  int b, t, h, which;  // session, token, kv head, 0 = K / 1 = V
-  long long src;       // element offset of the row in its input array
-};
-
-__device__ __forceinline__ RowRef decode_row(long long r, int n_sess, int n_tok, int kvh) {
-  const long long per = (long long)n_sess * n_tok * kvh;
-  RowRef o;
-  o.which = r >= per;
-  const long long rem = o.which ? r - per : r;
-  o.h = (int)(rem % kvh);
-  const long long bt = rem / kvh;
-  o.t = (int)(bt % n_tok);
-  o.b = (int)(bt / n_tok);
-  o.src = rem * HD;
-  return o;
-}
-
+// Grid: x = blocks of TOK_PER_BLOCK tokens, y = (K or V, kv head), z = session.  Every
+// index comes from the block coordinates; a block writes the rows [len + t] of one
+// head of one of the two arrays.
 template <int FMT>
 __global__ __launch_bounds__(APPEND_THREADS) void k_append(
-    const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int n_sess, int n_tok,
-    int kvh, const float* __restrict__ xk, const float* __restrict__ xv,
-    int32_t* __restrict__ status) {
+    const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int n_tok, int kvh,
+    const float* __restrict__ xk, const float* __restrict__ xv, int32_t* __restrict__ status) {
+  const int b = blockIdx.z;
+  const int which = blockIdx.y >= (unsigned)kvh;   // 0 = K, 1 = V
+  const int h = blockIdx.y - which * kvh;
+  const kv_session s = tab[b];
+  const int len = lens[b];
+  int bad = session_bad(s, FMT);
+  if (!bad && (len < 0 || (long long)len + n_tok > s.cap)) bad = KV_DEV_RANGE;
+  if (bad) {   // the whole session is skipped; one thread of the session reports it
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) flag(status, bad);
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;   // which row of the pair
   const int sub = lane & 31;    // float4 index within the row
-  const long long n_rows = 2LL * n_sess * n_tok * kvh;
-  const long long wave = (long long)blockIdx.x * (APPEND_THREADS / 64) + (threadIdx.x >> 6);
+  const int t0 = blockIdx.x * TOK_PER_BLOCK + (threadIdx.x >> 6) * (ROW_PAIRS * 2);
+  // source row (b, t, h) of [n_sess][n_tok][kvh][HD]
+  const float* src = (which ? xv : xk) + ((size_t)b * n_tok * kvh + h) * HD + sub * 4;
+  const size_t drow0 = (size_t)h * s.cap + len;   // destination row of token 0
 
   float4 x[ROW_PAIRS];
-  RowRef rr[ROW_PAIRS];
-  bool in[ROW_PAIRS];
 #pragma unroll
   for (int p = 0; p < ROW_PAIRS; ++p) {
-    const long long r = (wave * ROW_PAIRS + p) * 2 + half;
-    in[p] = r < n_rows;
-    rr[p] = decode_row(in[p] ? r : 0, n_sess, n_tok, kvh);
-    const float* src = (rr[p].which ? xv : xk) + rr[p].src + sub * 4;
-    x[p] = in[p] ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int t = t0 + 2 * p + half;
+    x[p] = t < n_tok ? *reinterpret_cast<const float4*>(src + (size_t)t * kvh * HD)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
 #pragma unroll
   for (int p = 0; p < ROW_PAIRS; ++p) {
-    const RowRef& o = rr[p];
-    const kv_session s = tab[o.b];
-    const int len = lens[o.b];
-    int bad = session_bad(s, FMT);
-    if (!bad && (len < 0 || (long long)len + n_tok > s.cap)) bad = KV_DEV_RANGE;
-    const bool store = in[p] && !bad;
-    const long long row = (long long)o.h * s.cap + (long long)len + o.t;  // [kvh][cap] row
-
+    const int t = t0 + 2 * p + half;
+    const bool store = t < n_tok;
+    const size_t row = drow0 + t;
     if constexpr (FMT == KV_FMT_Q8) {
       float a = fmaxf(fmaxf(fabsf(x[p].x), fabsf(x[p].y)), fmaxf(fabsf(x[p].z), fabsf(x[p].w)));
       a = max16(a);                                  // group max: all 16 lanes of the group
@@ -87,17 +77,14 @@ __global__ __launch_bounds__(APPEND_THREADS) void k_append(
       const uint32_t packed = (uint32_t)(c[0] & 0xFF) | ((uint32_t)(c[1] & 0xFF) << 8) |
                               ((uint32_t)(c[2] & 0xFF) << 16) | ((uint32_t)(c[3] & 0xFF) << 24);
       if (store) {
-        stg32(static_cast<int8_t*>(o.which ? s.v : s.k) + row * HD + sub * 4, packed);
-        if ((sub & 15) == 0) stg16((o.which ? s.v_scale : s.k_scale) + row * NGRP + (sub >> 4), sbits);
+        stg32(static_cast<int8_t*>(which ? s.v : s.k) + row * HD + sub * 4, packed);
+        if ((sub & 15) == 0) stg16((which ? s.v_scale : s.k_scale) + row * NGRP + (sub >> 4), sbits);
       }
     } else {
       const uint32_t lo = (uint32_t)f2h(x[p].x) | ((uint32_t)f2h(x[p].y) << 16);
       const uint32_t hi = (uint32_t)f2h(x[p].z) | ((uint32_t)f2h(x[p].w) << 16);
-      if (store) {
-        stg64(static_cast<uint16_t*>(o.which ? s.v : s.k) + row * HD + sub * 4, u32x2{lo, hi});
-      }
+      if (store) stg64(static_cast<uint16_t*>(which ? s.v : s.k) + row * HD + sub * 4, u32x2{lo, hi});
     }
-    if (in[p] && bad && sub == 0 && o.t == 0 && o.h == 0 && o.which == 0) flag(status, bad);
   }
 }
 
@@ -106,17 +93,15 @@ __global__ __launch_bounds__(APPEND_THREADS) void k_append(
 hipError_t launch_append(int fmt, int kvh, const kv_session* d_tab, const int32_t* d_len,
                          int n_sess, int n_tok, const float* d_k, const float* d_v,
                          int32_t* d_status, hipStream_t st) {
-  const long long n_rows = 2LL * n_sess * n_tok * kvh;
-  const long long rows_per_block = (APPEND_THREADS / 64) * ROW_PAIRS * 2;
-  const long long blocks = (n_rows + rows_per_block - 1) / rows_per_block;
-  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-  dim3 grid((unsigned)blocks), block(APPEND_THREADS);
+  const long long bx = ((long long)n_tok + TOK_PER_BLOCK - 1) / TOK_PER_BLOCK;
+  if (bx > 0x7FFFFFFFLL || 2LL * kvh > 65535 || n_sess > 65535) return hipErrorInvalidValue;
+  dim3 grid((unsigned)bx, 2 * kvh, n_sess), block(APPEND_THREADS);
   if (fmt == KV_FMT_Q8)
-    hipLaunchKernelGGL(k_append<KV_FMT_Q8>, grid, block, 0, st, d_tab, d_len, n_sess, n_tok, kvh,
-                       d_k, d_v, d_status);
+    hipLaunchKernelGGL(k_append<KV_FMT_Q8>, grid, block, 0, st, d_tab, d_len, n_tok, kvh, d_k,
+                       d_v, d_status);
   else
-    hipLaunchKernelGGL(k_append<KV_FMT_F16>, grid, block, 0, st, d_tab, d_len, n_sess, n_tok, kvh,
-                       d_k, d_v, d_status);
+    hipLaunchKernelGGL(k_append<KV_FMT_F16>, grid, block, 0, st, d_tab, d_len, n_tok, kvh, d_k,
+                       d_v, d_status);
   return hipGetLastError();
 }
 
