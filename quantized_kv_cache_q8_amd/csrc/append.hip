@@ -12,16 +12,17 @@
 // needs no LDS and no workgroup barrier (the page's kernel needed a block-wide
 // barrier for the same max; here every lane reaches the DPP steps and only the
 // stores are guarded).  A wave covers two rows (tokens) per step and keeps
-// ROW_PAIRS steps of loads in flight; a block covers 32 tokens of one head of K or
-// of V of one session.
+// ROW_PAIRS steps of loads in flight; a block covers 16 tokens of one head of K or
+// of V of one session.  Inputs are read and cache rows written with non-temporal
+// accesses (each byte is touched once).
 #include "kvq8_internal.h"
 
 namespace kvq8 {
 namespace {
 
 constexpr int APPEND_THREADS = 256;
-constexpr int ROW_PAIRS = 4;                                      // row pairs per wave
-constexpr int TOK_PER_BLOCK = (APPEND_THREADS / 64) * ROW_PAIRS * 2;  // 32
+constexpr int ROW_PAIRS = 2;                                      // row pairs per wave
+constexpr int TOK_PER_BLOCK = (APPEND_THREADS / 64) * ROW_PAIRS * 2;  // 16
 
 // Grid: x = blocks of TOK_PER_BLOCK tokens, y = (K or V, kv head), z = session.  Every
 // index comes from the block coordinates; a block writes the rows [len + t] of one
@@ -53,8 +54,13 @@ __global__ __launch_bounds__(APPEND_THREADS) void k_append(
 #pragma unroll
   for (int p = 0; p < ROW_PAIRS; ++p) {
     const int t = t0 + 2 * p + half;
-    x[p] = t < n_tok ? *reinterpret_cast<const float4*>(src + (size_t)t * kvh * HD)
-                     : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* ps = src + (size_t)t * kvh * HD;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < n_tok) {   // the new values are read once: non-temporal
+      const u32x4 w = ldg128_nt(ps);
+      v = make_float4(as_f32(w[0]), as_f32(w[1]), as_f32(w[2]), as_f32(w[3]));
+    }
+    x[p] = v;
   }
 
 #pragma unroll
@@ -77,13 +83,18 @@ __global__ __launch_bounds__(APPEND_THREADS) void k_append(
       const uint32_t packed = (uint32_t)(c[0] & 0xFF) | ((uint32_t)(c[1] & 0xFF) << 8) |
                               ((uint32_t)(c[2] & 0xFF) << 16) | ((uint32_t)(c[3] & 0xFF) << 24);
       if (store) {
-        stg32(static_cast<int8_t*>(which ? s.v : s.k) + row * HD + sub * 4, packed);
+        // the cache rows are not read again by this kernel: non-temporal stores
+        int8_t* dst = static_cast<int8_t*>(which ? s.v : s.k) + row * HD + sub * 4;
+        __builtin_nontemporal_store(packed, (KVQ8_GLOBAL uint32_t*)dst);
         if ((sub & 15) == 0) stg16((which ? s.v_scale : s.k_scale) + row * NGRP + (sub >> 4), sbits);
       }
     } else {
       const uint32_t lo = (uint32_t)f2h(x[p].x) | ((uint32_t)f2h(x[p].y) << 16);
       const uint32_t hi = (uint32_t)f2h(x[p].z) | ((uint32_t)f2h(x[p].w) << 16);
-      if (store) stg64(static_cast<uint16_t*>(which ? s.v : s.k) + row * HD + sub * 4, u32x2{lo, hi});
+      if (store) {
+        uint16_t* dst = static_cast<uint16_t*>(which ? s.v : s.k) + row * HD + sub * 4;
+        __builtin_nontemporal_store(u32x2{lo, hi}, (KVQ8_GLOBAL u32x2*)dst);
+      }
     }
   }
 }
