@@ -58,8 +58,34 @@ __device__ __forceinline__ u32x4 ldkv(const void* p) {
   return ldg128(p);
 }
 
-constexpr int DEC_THREADS = 256;
-constexpr int DEC_WAVES = DEC_THREADS / 64;
+#ifndef KVQ8_DEC_WG_WAVES
+#define KVQ8_DEC_WG_WAVES 8
+#endif
+// share (sixteenths) of a head's steps taken by the leading group of waves
+#ifndef KVQ8_DEC_LEAD16_Q8
+#define KVQ8_DEC_LEAD16_Q8 12
+#endif
+#ifndef KVQ8_DEC_LEAD16_F16
+#define KVQ8_DEC_LEAD16_F16 8
+#endif
+constexpr int DEC_WAVES = KVQ8_DEC_WG_WAVES;
+constexpr int DEC_THREADS = 64 * DEC_WAVES;
+// With 8 waves per workgroup, waves w and w + 4 share a SIMD and the instruction
+// arbiter favours the older one, w: with equal work the younger wave of the int8
+// kernel, starved of issue slots, finishes ~40 % later and runs alone at the end.
+// The waves therefore form two groups: group 0 (waves 0-3) takes lead16 sixteenths
+// of the head's steps, group 1 the rest, each group interleaving its steps over its
+// own waves.
+constexpr int GRP_WAVES = DEC_WAVES >= 8 ? DEC_WAVES / 2 : DEC_WAVES;
+constexpr bool GROUPED = GRP_WAVES != DEC_WAVES;
+template <int FMT>
+__host__ __device__ constexpr int lead16() {
+  return GROUPED ? (FMT == KV_FMT_Q8 ? KVQ8_DEC_LEAD16_Q8 : KVQ8_DEC_LEAD16_F16) : 16;
+}
+template <int FMT>
+__host__ __device__ constexpr int lead_steps(int J) {  // >= J - lead_steps(J) (lead16 >= 8)
+  return (int)(((long long)J * lead16<FMT>() + 15) / 16);
+}
 constexpr float LOG2E = 1.4426950408889634f;
 
 __device__ __forceinline__ void wave_lds_fence() {
@@ -139,7 +165,13 @@ __device__ __forceinline__ void store_logits(float* dst, const float (&v)[G], bo
   }
 }
 
-constexpr int CH = KVQ8_DEC_CH;  // most steps per wave (LDS holds its logits)
+constexpr int CH = KVQ8_DEC_CH;  // most steps per wave (LDS holds its logits), on average
+// logits budget of a wave of group 0 and of group 1, in proportion to their shares
+template <int FMT>
+constexpr int ch0() { return GROUPED ? 2 * CH * lead16<FMT>() / 16 : CH; }
+template <int FMT>
+constexpr int ch1() { return GROUPED ? 2 * CH - ch0<FMT>() : 0; }
+static_assert(CH % 8 == 0, "the group budgets are whole multiples of 8 steps");
 
 // One batch of U steps for one lane: U x 16 values and, for int8, the U raw fp16
 // scales of the lane's 64-dim group.
@@ -167,6 +199,7 @@ struct Batch {
 // LDS of one split workgroup: per-wave logits for CH steps, the wave partials
 template <int G>
 __host__ __device__ constexpr size_t split_lds_bytes() {
+  // (ch0 + ch1 = 2 CH when grouped, whatever the format)
   return sizeof(float) * ((size_t)DEC_WAVES * CH * 8 * G + DEC_WAVES * G * HD + 2 * DEC_WAVES * G);
 }
 
@@ -176,24 +209,29 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int kvh,
     const float* __restrict__ q, float qscale, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, int S) {
-  static_assert(CH % (2 * U) == 0, "a chunk holds whole pairs of load batches");
+  constexpr int CH0 = ch0<FMT>(), CH1 = ch1<FMT>();
+  static_assert(CH0 % (2 * U) == 0 && CH1 % (2 * U) == 0, "a chunk holds whole pairs of load batches");
   const int s_idx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int nqh = kvh * G;
   const kv_session ss = tab[b];
   const int len = lens[b];
   if (session_bad(ss, FMT) || len < 0 || len > ss.cap || len > max_len) return;  // merge flags
   const int J = (len + 7) >> 3;                  // 8-token steps of this session
-  if (s_idx * DEC_WAVES >= J) return;            // no step for this workgroup
+  const int Jf = lead_steps<FMT>(J);             // steps of group 0 (>= those of group 1)
+  if (s_idx * GRP_WAVES >= Jf) return;           // no step for this workgroup
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane >> 3, c = lane & 7;
-  const int gw = s_idx * DEC_WAVES + wave;       // wave index within (session, head)
-  const int W = S * DEC_WAVES;                   // waves per (session, head)
-  const int n_steps = gw < J ? (J - 1 - gw) / W + 1 : 0;
+  const int grp = wave / GRP_WAVES, wg = wave % GRP_WAVES;
+  const int Jg = grp ? J - Jf : Jf;              // steps of this wave's group
+  const int gw0 = s_idx * GRP_WAVES + wg;        // wave index within the group's waves
+  const int gw = (grp ? Jf : 0) + gw0;           // first step of this wave
+  const int W = S * GRP_WAVES;                   // waves per group of (session, head)
+  const int n_steps = gw0 < Jg ? (Jg - 1 - gw0) / W + 1 : 0;
 
   extern __shared__ float smem[];
-  float* lg = smem + wave * CH * 8 * G;          // [CH*8][G] logits, then p
-  float* o_l = smem + DEC_WAVES * CH * 8 * G;    // [waves][G][HD]
+  float* lg = smem + (grp ? GRP_WAVES * CH0 + wg * CH1 : wg * CH0) * 8 * G;  // logits, then p
+  float* o_l = smem + GRP_WAVES * (CH0 + CH1) * 8 * G;   // [waves][G][HD]
   float* m_l = o_l + DEC_WAVES * G * HD;         // [waves][G]
   float* l_l = m_l + DEC_WAVES * G;              // [waves][G]
 
@@ -407,8 +445,8 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode_merge(
   }
   __shared__ float red[DEC_WAVES];
   __shared__ float2 part[DEC_WAVES][64];
-  // workgroups that received a step: those with 4s < ceil(len / 8)
-  const int Sb = min(S, (((len + 7) >> 3) + DEC_WAVES - 1) / DEC_WAVES);
+  // workgroups that received a step: those with s * GRP_WAVES < lead_steps(ceil(len / 8))
+  const int Sb = min(S, (lead_steps<FMT>((len + 7) >> 3) + GRP_WAVES - 1) / GRP_WAVES);
   const float* lse = ws_lse + ((long long)b * nqh + qh) * S;
   const float* o = ws_o + ((long long)b * nqh + qh) * S * HD;
   float mx = -INFINITY;
@@ -528,16 +566,22 @@ DecodePlan decode_plan(int fmt, int kvh, int nqh, int n_sess, int max_len) {
   // last, partly filled round would leave CUs idle), but not past one split per 4
   // steps (so every workgroup has work).
   const long long J = ((long long)max_len + 7) / 8;
+  const bool q8 = fmt == KV_FMT_Q8;
+  const long long Jf = q8 ? lead_steps<KV_FMT_Q8>((int)J) : lead_steps<KV_FMT_F16>((int)J);
+  const long long J1 = J - Jf;
+  const long long CH0 = q8 ? ch0<KV_FMT_Q8>() : ch0<KV_FMT_F16>();
+  const long long CH1 = q8 ? ch1<KV_FMT_Q8>() : ch1<KV_FMT_F16>();
   const long long P = (long long)kvh * n_sess;
-  // S0 keeps every wave at <= CH steps (the kernel's LDS holds CH steps of logits)
-  const long long S0 = std::max(1LL, (J + DEC_WAVES * CH - 1) / (DEC_WAVES * CH));
+  // S0 keeps every wave within its group's LDS budget of logits (CH0 or CH1 steps)
+  long long S0 = std::max(1LL, (Jf + GRP_WAVES * CH0 - 1) / (GRP_WAVES * CH0));
+  if (CH1 > 0) S0 = std::max(S0, (J1 + GRP_WAVES * CH1 - 1) / (GRP_WAVES * CH1));
   long long S = S0;
   const long long C = resident(fmt, nqh / kvh);
   if (C > 0) {
     const long long rounds = (P * S0 + C - 1) / C;
     S = std::max(S0, (rounds * C + P - 1) / P);
   }
-  S = std::min(S, std::max(S0, (J + DEC_WAVES - 1) / DEC_WAVES));
+  S = std::min(S, std::max(S0, (Jf + GRP_WAVES - 1) / GRP_WAVES));
   DecodePlan p;
   p.S = (int)S;
   const size_t rows = (size_t)n_sess * nqh * p.S;
