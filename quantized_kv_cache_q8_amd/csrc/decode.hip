@@ -57,6 +57,8 @@ __device__ __forceinline__ u32x4 ldkv(const void* p) {
   if constexpr (KVQ8_DEC_NT) return ldg128_nt(p);
   return ldg128(p);
 }
+// base: the head's first row (the same for the whole wave); off: 32-bit byte offset
+__device__ __forceinline__ u32x4 ldkv(const char* base, uint32_t off) { return ldkv(base + off); }
 
 #ifndef KVQ8_DEC_WG_WAVES
 #define KVQ8_DEC_WG_WAVES 8
@@ -101,8 +103,8 @@ struct Chunk;
 template <>
 struct Chunk<KV_FMT_Q8> {
   u32x4 w;  // 16 int8 codes
-  __device__ __forceinline__ void load(const void* base, long long row, int c) {
-    w = ldkv(static_cast<const int8_t*>(base) + row * HD + c * 16);
+  __device__ __forceinline__ void load(const char* base, uint32_t row, int c) {
+    w = ldkv(base, row * HD + c * 16);
   }
   __device__ __forceinline__ float get(int i) const {
     return (float)(int8_t)(w[i >> 2] >> (8 * (i & 3)));
@@ -112,10 +114,10 @@ struct Chunk<KV_FMT_Q8> {
 template <>
 struct Chunk<KV_FMT_F16> {
   u32x4 a, b;  // 16 fp16 values: dims [8c, 8c+8) and [64+8c, 64+8c+8)
-  __device__ __forceinline__ void load(const void* base, long long row, int c) {
-    const uint16_t* p = static_cast<const uint16_t*>(base) + row * HD + c * 8;
-    a = ldkv(p);        // the 8 lanes of a row cover bytes [0, 128) of it
-    b = ldkv(p + 64);   // ... and bytes [128, 256)
+  __device__ __forceinline__ void load(const char* base, uint32_t row, int c) {
+    const uint32_t off = row * (HD * 2) + c * 16;
+    a = ldkv(base, off);        // the 8 lanes of a row cover bytes [0, 128) of it
+    b = ldkv(base, off + 128);  // ... and bytes [128, 256)
   }
   __device__ __forceinline__ float get(int i) const {
     const u32x4& v = i < 8 ? a : b;
@@ -181,13 +183,14 @@ struct Batch {
   uint16_t sc[U];
   // steps k .. k+U-1 of wave gw; tokens past len re-read the last cell (in bounds)
   // and are masked by the callers
-  __device__ __forceinline__ void load(const void* vals, const uint16_t* scales, long long rowbase,
-                                       int gw, int W, int k, int len, int r, int c) {
+  // vals, scales: the head's first row of values and of scales
+  __device__ __forceinline__ void load(const char* vals, const char* scales, int gw, int W, int k,
+                                       int len, int r, int c) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const long long row = rowbase + min((gw + (k + u) * W) * 8 + r, len - 1);
+      const uint32_t row = (uint32_t)min((gw + (k + u) * W) * 8 + r, len - 1);
       ch[u].load(vals, row, c);
-      if constexpr (FMT == KV_FMT_Q8) sc[u] = ldg16(scales + row * NGRP + (c >> 2));
+      if constexpr (FMT == KV_FMT_Q8) sc[u] = ldg16(scales + (row * NGRP + (c >> 2)) * 2);
     }
   }
   __device__ __forceinline__ float scale(int u) const {
@@ -200,7 +203,8 @@ struct Batch {
 template <int G>
 __host__ __device__ constexpr size_t split_lds_bytes() {
   // (ch0 + ch1 = 2 CH when grouped, whatever the format)
-  return sizeof(float) * ((size_t)DEC_WAVES * CH * 8 * G + DEC_WAVES * G * HD + 2 * DEC_WAVES * G);
+  return sizeof(float) * ((size_t)DEC_WAVES * CH * 8 * G + DEC_WAVES * G * HD + 2 * DEC_WAVES * G +
+                          DEC_WAVES * 64 * G);
 }
 
 template <int FMT, int G, int U>
@@ -234,8 +238,14 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
   float* o_l = smem + GRP_WAVES * (CH0 + CH1) * 8 * G;   // [waves][G][HD]
   float* m_l = o_l + DEC_WAVES * G * HD;         // [waves][G]
   float* l_l = m_l + DEC_WAVES * G;              // [waves][G]
+  float* junk = l_l + DEC_WAVES * G + (threadIdx.x >> 6) * 64 * G;  // discarded stores
 
-  const long long rowbase = (long long)h * ss.cap;
+  constexpr int EB = FMT == KV_FMT_F16 ? 2 : 1;   // bytes per value
+  const size_t hrow = (size_t)h * (size_t)ss.cap;  // the head's first row
+  const char* kb = static_cast<const char*>(ss.k) + hrow * HD * EB;
+  const char* vb = static_cast<const char*>(ss.v) + hrow * HD * EB;
+  const char* ksb = reinterpret_cast<const char*>(ss.k_scale) + hrow * NGRP * 2;
+  const char* vsb = reinterpret_cast<const char*>(ss.v_scale) + hrow * NGRP * 2;
   float m[G], l[G], acc[G][16];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -274,20 +284,35 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
           for (int g = 0; g < G; ++g) part[u][g] = fmaf(qv[g][i], kf, part[u][g]);
         }
       }
+      // the 8-lane sums stage by stage over all U x G values, so that no DPP
+      // operation waits on the one before it; lanes c .. c^3 share a scale group
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float sc = cur.scale(u);
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          if constexpr (FMT == KV_FMT_Q8) part[u][g] *= sc;
-          part[u][g] = sum8(part[u][g]);
+        for (int g = 0; g < G; ++g) part[u][g] = __fadd_rn(part[u][g], dpp<DPP_QUAD_XOR1>(part[u][g]));
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g) part[u][g] = __fadd_rn(part[u][g], dpp<DPP_QUAD_XOR2>(part[u][g]));
+      if constexpr (FMT == KV_FMT_Q8) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float sc = cur.scale(u);
+#pragma unroll
+          for (int g = 0; g < G; ++g) part[u][g] *= sc;
         }
       }
 #pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+          part[u][g] = __fadd_rn(part[u][g], dpp<DPP_ROW_HALF_MIRROR>(part[u][g]));
+      // lane c == 0 of each row writes the row's logits; the other lanes write to
+      // their own slots of a scratch area, so no lane is masked off
+#pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int it = it0 + u;
-        const int t = (gw + (k0 + it) * W) * 8 + r;
-        if (c == 0 && it < n_it) store_logits<G>(lg + (it * 8 + r) * G, part[u], t < len);
+        float* dst = c == 0 ? lg + ((it0 + u) * 8 + r) * G : junk + lane * G;
+        store_logits<G>(dst, part[u], true);
       }
     };
     auto vstep = [&](const Batch<FMT, U>& cur, int it0, int n_it) {
@@ -300,7 +325,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
         float w[G];
         load_p<G>(lg + (it * 8 + r) * G, w);
 #pragma unroll
-        for (int g = 0; g < G; ++g) w[g] = (it < n_it) ? w[g] * sc : 0.f;
+        for (int g = 0; g < G; ++g) w[g] *= sc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float vf = cur.ch[u].get(i);
@@ -318,30 +343,36 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     // softmax.  The plan gives every wave at most CH steps (n_it <= CH).
     const int n_it = n_steps;
     Batch<FMT, U> A, B;
-    A.load(ss.k, ss.k_scale, rowbase, gw, W, 0, len, r, c);
+    A.load(kb, ksb, gw, W, 0, len, r, c);
     // ---- K pass ---------------------------------------------------------------
     for (int it0 = 0; it0 < n_it; it0 += 2 * U) {
-      B.load(ss.k, ss.k_scale, rowbase, gw, W, it0 + U, len, r, c);
+      B.load(kb, ksb, gw, W, it0 + U, len, r, c);
       kstep(A, 0, it0, n_it);
       if (it0 + 2 * U < n_it)
-        A.load(ss.k, ss.k_scale, rowbase, gw, W, it0 + 2 * U, len, r, c);
+        A.load(kb, ksb, gw, W, it0 + 2 * U, len, r, c);
       else
-        A.load(ss.v, ss.v_scale, rowbase, gw, W, 0, len, r, c);
+        A.load(vb, vsb, gw, W, 0, len, r, c);
       kstep(B, 0, it0 + U, n_it);
     }
     wave_lds_fence();
     // ---- softmax over the wave's tokens ---------------------------------------
     const int n_loc = n_it * 8;
+    const int n_pad = (n_it + 2 * U - 1) / (2 * U) * (2 * U);
     for (int tl = lane; tl < n_loc; tl += 64) {
+      const int t = (gw + (tl >> 3) * W) * 8 + (tl & 7);
+      if (t < len) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) m[g] = fmaxf(m[g], lg[tl * G + g]);
+        for (int g = 0; g < G; ++g) m[g] = fmaxf(m[g], lg[tl * G + g]);
+      }
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) m[g] = wave_max(m[g]);   // finite: step 0 has token gw*8
-    for (int tl = lane; tl < n_loc; tl += 64) {
+    for (int tl = lane; tl < n_pad * 8; tl += 64) {
+      const int t = (gw + (tl >> 3) * W) * 8 + (tl & 7);
+      const bool ok = tl < n_loc && t < len;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float p = exp2f(lg[tl * G + g] - m[g]);
+        const float p = ok ? exp2f(lg[tl * G + g] - m[g]) : 0.f;
         lg[tl * G + g] = p;
         l[g] += p;
       }
@@ -351,9 +382,9 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     wave_lds_fence();
     // ---- V pass ---------------------------------------------------------------
     for (int it0 = 0; it0 < n_it; it0 += 2 * U) {
-      B.load(ss.v, ss.v_scale, rowbase, gw, W, it0 + U, len, r, c);
+      B.load(vb, vsb, gw, W, it0 + U, len, r, c);
       vstep(A, it0, n_it);
-      if (it0 + 2 * U < n_it) A.load(ss.v, ss.v_scale, rowbase, gw, W, it0 + 2 * U, len, r, c);
+      if (it0 + 2 * U < n_it) A.load(vb, vsb, gw, W, it0 + 2 * U, len, r, c);
       vstep(B, it0 + U, n_it);
     }
 #pragma unroll
