@@ -51,7 +51,8 @@ typedef struct {
  *        k_scale, v_scale = fp16 bits, [n_kv_heads][cap][head_dim / 64]; scale g of
  *        a row covers dims [64g, 64g + 64).  Codes and scales are separate arrays
  *        ([P1, What changed]; separate byte runs in [P3, How]).
- * All four pointers 16-byte aligned; cap a multiple of 64.  An array of these
+ * All four pointers 16-byte aligned; cap a multiple of 64 and at most 2^24 (a head's
+ * rows are addressed with 32-bit byte offsets).  An array of these
  * lives in device memory for the batched calls. */
 typedef struct {
   void* k;
@@ -69,7 +70,7 @@ enum {
   KV_ERR_ALIGN = -3,       /* pointer not 16-byte aligned, or cap % 64 != 0 */
   KV_ERR_UNSUPPORTED = -4, /* head_dim != 128, or G not in {1, 2, 4, 8} */
   KV_ERR_WORKSPACE = -5,   /* workspace null or smaller than the *_workspace_bytes value */
-  KV_ERR_RANGE = -6,       /* rows outside [0, cap) (host-checkable cases) */
+  KV_ERR_RANGE = -6,       /* rows outside [0, cap), or cap above 2^24 (host-checkable cases) */
   KV_ERR_HIP = -7          /* a kernel launch failed */
 };
 
@@ -77,7 +78,7 @@ enum {
 enum {
   KV_DEV_RANGE = 1,      /* len < 0, len + n_tok > cap (append), len > max_len or cap (decode) */
   KV_DEV_BAD_SESSION = 2 /* table entry with null/unaligned pointers, scales inconsistent with
-                            the format, or cap not a positive multiple of 64 */
+                            the format, or cap not a positive multiple of 64 or above 2^24 */
 };
 
 /* Bytes of one K (or one V) array of one layer: part 0 the values/codes, part 1

@@ -32,6 +32,7 @@ int check_session(const kv_shape* s, const kv_session* e) {
   if (!aligned16(e->k) || !aligned16(e->v) || !aligned16(e->k_scale) || !aligned16(e->v_scale))
     return KV_ERR_ALIGN;
   if (e->cap <= 0 || (e->cap & 63)) return KV_ERR_ALIGN;
+  if (e->cap > KV_MAX_CAP) return KV_ERR_RANGE;
   return KV_OK;
 }
 

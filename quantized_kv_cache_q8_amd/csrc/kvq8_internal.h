@@ -11,6 +11,8 @@ namespace kvq8 {
 
 constexpr int HD = 128;        // head_dim supported by the kernels
 constexpr int NGRP = HD / KV_GROUP;  // fp16 scales per head row (2)
+// most cells per session: a head's rows (<= 256 B each) stay within 32-bit offsets
+constexpr int KV_MAX_CAP = 1 << 24;
 
 // ---------------------------------------------------------------------------
 // Cross-lane operations (DPP, within a 16-lane row; no LDS traffic)
@@ -129,7 +131,7 @@ __device__ __forceinline__ int session_bad(const kv_session& s, int fmt) {
   } else if (sc != 0) {
     return KV_DEV_BAD_SESSION;
   }
-  if (s.cap <= 0 || (s.cap & 63)) return KV_DEV_BAD_SESSION;
+  if (s.cap <= 0 || (s.cap & 63) || s.cap > KV_MAX_CAP) return KV_DEV_BAD_SESSION;
   return 0;
 }
 

@@ -155,6 +155,7 @@ def test_compact_validation():
     assert compact(shape(), sess(vs=D + 2)) == kq.KV_ERR_ALIGN
     assert compact(shape(), sess(cap=1000)) == kq.KV_ERR_ALIGN
     assert compact(shape(), sess(cap=0)) == kq.KV_ERR_ALIGN
+    assert compact(shape(), sess(cap=(1 << 24) + 64)) == kq.KV_ERR_RANGE
     assert compact(shape(), sess(), P=0) == kq.KV_ERR_ARG
     assert compact(shape(), sess(), k16=None) == kq.KV_ERR_ARG
     assert compact(shape(), sess(), v16=D + 2) == kq.KV_ERR_ALIGN

@@ -130,3 +130,14 @@ def test_bad_session_entries_are_skipped_and_flagged():
     for t in other.tensors():
         assert (t.view(torch.uint8) == 0x5A).all()
     assert (good.k[:, 0] == 127).all() and (good.k[:, 1:].view(torch.uint8) == 0x5A).all()
+    # a capacity beyond 2^24 cells is refused on the device as well (nothing is touched)
+    e_big = other.entry()
+    e_big.cap = (1 << 24) + 64
+    status.zero_()
+    tab = kq.session_table([e_big])
+    kq.kv_append(sh, tab, lens[:1], 1, 1, torch.from_numpy(x[:1]).to(DEV),
+                 torch.from_numpy(x[:1]).to(DEV), status)
+    torch.cuda.synchronize()
+    assert status.item() == kq.KV_DEV_BAD_SESSION
+    for t in other.tensors():
+        assert (t.view(torch.uint8) == 0x5A).all()
