@@ -50,10 +50,15 @@ def decode_bytes(fmt, length):
 
 
 def source_hash(*names):
+    """Hash of kernel sources with // comments and blank space dropped, so that a
+    comment edit does not invalidate counters taken on the same code."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "quantized_kv_cache_q8_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "quantized_kv_cache_q8_amd", "csrc", n)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

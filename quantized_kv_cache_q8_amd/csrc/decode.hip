@@ -3,11 +3,14 @@
 // and Extra Notes: the next token's split-K decode reads the cache, FP16 or int8,
 // with no conversion pass).
 //
-// k_decode_split: grid (S splits, kv head h, session b), 4 waves per workgroup.
-//   Work is counted in 8-token steps (one 128-bit load per lane covers a step of
-//   one head: 8 rows x 8 lanes).  The W = 4S waves of a (session, head) take the
-//   steps round-robin -- wave gw owns steps gw, gw + W, gw + 2W, ... -- so all of
-//   them sweep that head's K/V together, front by front, as one stream.
+// k_decode_split: grid (S splits, kv head h, session b), 8 waves per workgroup in
+//   two groups of 4 (waves w and w + 4 share a SIMD).  Work is counted in 8-token
+//   steps (one 128-bit load per lane covers a step of one head: 8 rows x 8 lanes).
+//   The steps of a (session, head) are cut in two ranges, one per group, in
+//   proportion to how fast each group runs (the older wave of a SIMD gets most
+//   issue slots).  The W = 4S waves of a group take the steps of its range
+//   round-robin -- wave gw owns steps gw, gw + W, gw + 2W, ... -- so they sweep
+//   that range of K/V together, front by front, as one stream.
 //   A wave works through its steps in chunks of CH steps, two passes per chunk:
 //   K pass   lane (r = lane/8, c = lane%8) holds 16 dims of token r of a step:
 //            in-register dequant, partial dots for the G query heads, the int8
@@ -16,8 +19,10 @@
 //   softmax  chunk max, rescale of the running (m, l, acc), exp2.
 //   V pass   acc[g][16 dims] += p * scale * v.
 //   Load batches alternate between two register sets so the next batch is in
-//   flight while one is consumed.  The 4 wave partials are combined in LDS and
+//   flight while one is consumed.  The 8 wave partials are combined in LDS and
 //   written as one (o, lse) per query head and split (o normalised, lse in log2).
+//   Offsets are 32-bit, from per-head base pointers (a head holds at most 2^24
+//   cells).
 // k_decode_merge: out = sum_j 2^(lse_j - L) o_j with L = log2 sum_j 2^lse_j.
 //
 // Dequantised values are exact in fp32 (a 7-bit code times an 11-bit fp16
