@@ -155,30 +155,20 @@ __device__ __forceinline__ void load_p(const float* src, float (&p)[G]) {
   }
 }
 
-// G logits of one token to LDS (one lane per 8-lane row), as 16/8/4-byte stores
+// Most steps per wave, on average over the two groups: the LDS holds each wave's
+// logits (8 tokens x G heads per step).  With 8 query heads the full budget would
+// not fit in the 160 KB of LDS beside the wave partials.
 template <int G>
-__device__ __forceinline__ void store_logits(float* dst, const float (&v)[G], bool valid) {
-  float x[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) x[g] = valid ? v[g] : -INFINITY;
-  if constexpr (G % 4 == 0) {
-#pragma unroll
-    for (int g = 0; g < G; g += 4)
-      *reinterpret_cast<float4*>(dst + g) = make_float4(x[g], x[g + 1], x[g + 2], x[g + 3]);
-  } else if constexpr (G == 2) {
-    *reinterpret_cast<float2*>(dst) = make_float2(x[0], x[1]);
-  } else {
-    dst[0] = x[0];
-  }
-}
-
-constexpr int CH = KVQ8_DEC_CH;  // most steps per wave (LDS holds its logits), on average
+__host__ __device__ constexpr int ch_steps() { return G >= 8 ? 56 : KVQ8_DEC_CH; }
 // logits budget of a wave of group 0 and of group 1, in proportion to their shares
-template <int FMT>
-constexpr int ch0() { return GROUPED ? 2 * CH * lead16<FMT>() / 16 : CH; }
-template <int FMT>
-constexpr int ch1() { return GROUPED ? 2 * CH - ch0<FMT>() : 0; }
-static_assert(CH % 8 == 0, "the group budgets are whole multiples of 8 steps");
+template <int FMT, int G>
+__host__ __device__ constexpr int ch0() {
+  return GROUPED ? 2 * ch_steps<G>() * lead16<FMT>() / 16 : ch_steps<G>();
+}
+template <int FMT, int G>
+__host__ __device__ constexpr int ch1() { return GROUPED ? 2 * ch_steps<G>() - ch0<FMT, G>() : 0; }
+static_assert(KVQ8_DEC_CH % 8 == 0 && ch_steps<8>() % 8 == 0,
+              "the group budgets are whole multiples of 8 steps");
 
 // One batch of U steps for one lane: U x 16 values and, for int8, the U raw fp16
 // scales of the lane's 64-dim group.
@@ -204,13 +194,48 @@ struct Batch {
   }
 };
 
-// LDS of one split workgroup: per-wave logits for CH steps, the wave partials
+// Register order of the G query heads in a lane's K-pass partials: slot j of lane
+// c (c = lane % 8) holds head j ^ head_map(c).  The three reduction stages pair
+// lane c with c^1, c^2 and 7-c; head_map makes the partner's slot j + n/2 (n the
+// values still carried) hold the head of this lane's slot j, so a stage is one
+// DPP add per value kept.  After log2(G) folding stages lane c holds head
+// head_map(c) alone, and lanes 0 .. G-1 of a row hold distinct heads.
+template <int G>
+__device__ __forceinline__ int head_map(int c) {
+  constexpr int A = G >= 8 ? 3 : G >= 4 ? 2 : G >= 2 ? 1 : 0;
+  const int c2 = (c >> 2) & 1;
+  const int f0 = (c & 1) ^ c2, f1 = ((c >> 1) & 1) ^ c2;
+  if constexpr (A == 3) return (f0 << 2) | (f1 << 1) | c2;
+  if constexpr (A == 2) return (f0 << 1) | f1;
+  if constexpr (A == 1) return f0;
+  return 0;
+}
+
+// One reduction stage over U rows of N live values: fold (N > 1) or plain add.
+template <int CTRL, int U, int G, int N>
+__device__ __forceinline__ void fold_stage(float (&x)[U][G]) {
+  if constexpr (N > 1) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int k = 0; k < N / 2; ++k) x[u][k] = __fadd_rn(x[u][k], dpp<CTRL>(x[u][k + N / 2]));
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u][0] = __fadd_rn(x[u][0], dpp<CTRL>(x[u][0]));
+  }
+}
+
+// LDS of one split workgroup: per-wave logits (ch0 + ch1 = 2 ch_steps per pair of
+// waves sharing a SIMD, whatever the format), the wave partials (o, m, l) and one
+// discarded-store slot per lane
 template <int G>
 __host__ __device__ constexpr size_t split_lds_bytes() {
-  // (ch0 + ch1 = 2 CH when grouped, whatever the format)
-  return sizeof(float) * ((size_t)DEC_WAVES * CH * 8 * G + DEC_WAVES * G * HD + 2 * DEC_WAVES * G +
-                          DEC_WAVES * 64 * G);
+  return sizeof(float) * ((size_t)DEC_WAVES * ch_steps<G>() * 8 * G + DEC_WAVES * G * HD +
+                          2 * DEC_WAVES * G + DEC_WAVES * 64);
 }
+static_assert(split_lds_bytes<1>() <= 160 * 1024 && split_lds_bytes<2>() <= 160 * 1024 &&
+                  split_lds_bytes<4>() <= 160 * 1024 && split_lds_bytes<8>() <= 160 * 1024,
+              "a split workgroup fits in one CU's LDS");
 
 template <int FMT, int G, int U>
 __global__ __launch_bounds__(DEC_THREADS)
@@ -218,7 +243,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int kvh,
     const float* __restrict__ q, float qscale, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, int S) {
-  constexpr int CH0 = ch0<FMT>(), CH1 = ch1<FMT>();
+  constexpr int CH0 = ch0<FMT, G>(), CH1 = ch1<FMT, G>();
   static_assert(CH0 % (2 * U) == 0 && CH1 % (2 * U) == 0, "a chunk holds whole pairs of load batches");
   const int s_idx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int nqh = kvh * G;
@@ -243,7 +268,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
   float* o_l = smem + GRP_WAVES * (CH0 + CH1) * 8 * G;   // [waves][G][HD]
   float* m_l = o_l + DEC_WAVES * G * HD;         // [waves][G]
   float* l_l = m_l + DEC_WAVES * G;              // [waves][G]
-  float* junk = l_l + DEC_WAVES * G + (threadIdx.x >> 6) * 64 * G;  // discarded stores
+  float* junk = l_l + DEC_WAVES * G + (threadIdx.x >> 6) * 64;  // discarded stores
 
   constexpr int EB = FMT == KV_FMT_F16 ? 2 : 1;   // bytes per value
   const size_t hrow = (size_t)h * (size_t)ss.cap;  // the head's first row
@@ -261,10 +286,11 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
   }
 
   if (n_steps > 0) {
-    float qv[G][16];
+    const int hsel = head_map<G>(c);
+    float qv[G][16];  // slot g: head g ^ hsel
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float* qp = q + ((long long)b * nqh + h * G + g) * HD;
+      const float* qp = q + ((long long)b * nqh + h * G + (g ^ hsel)) * HD;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const u32x4 v = ldg128(qp + lane_dim<FMT>(c, 4 * k));   // 4 consecutive dims
@@ -273,15 +299,20 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
       }
     }
     // U x G independent dot products, interleaved so that no FMA waits on the one
-    // just before it; then the U x G 8-lane reductions, then the logit stores
+    // just before it; then the 8-lane reductions, then the logit stores.  Slot j of
+    // a lane holds head j ^ hsel (see head_map), so the reduction folds: each DPP
+    // stage adds the partner's upper slots to this lane's lower ones and halves
+    // the values carried (4 DPP adds per step for G = 4 instead of 12).
     auto kstep = [&](const Batch<FMT, U>& cur, int k0, int it0, int n_it) {
       float part[U][G];
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u) {
+        const float kf = cur.ch[u].get(0);
 #pragma unroll
-        for (int g = 0; g < G; ++g) part[u][g] = 0.f;
+        for (int g = 0; g < G; ++g) part[u][g] = qv[g][0] * kf;
+      }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 1; i < 16; ++i) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const float kf = cur.ch[u].get(i);
@@ -289,35 +320,26 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
           for (int g = 0; g < G; ++g) part[u][g] = fmaf(qv[g][i], kf, part[u][g]);
         }
       }
-      // the 8-lane sums stage by stage over all U x G values, so that no DPP
-      // operation waits on the one before it; lanes c .. c^3 share a scale group
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int g = 0; g < G; ++g) part[u][g] = __fadd_rn(part[u][g], dpp<DPP_QUAD_XOR1>(part[u][g]));
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int g = 0; g < G; ++g) part[u][g] = __fadd_rn(part[u][g], dpp<DPP_QUAD_XOR2>(part[u][g]));
-      if constexpr (FMT == KV_FMT_Q8) {
+      // stage by stage over all U values, so that no DPP add waits on the one before
+      constexpr int N1 = G > 1 ? G / 2 : 1, N2 = N1 > 1 ? N1 / 2 : 1, N3 = N2 > 1 ? N2 / 2 : 1;
+      fold_stage<DPP_QUAD_XOR1, U, G, G>(part);
+      fold_stage<DPP_QUAD_XOR2, U, G, N1>(part);
+      if constexpr (FMT == KV_FMT_Q8) {  // lanes c .. c^3 share a scale group
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const float sc = cur.scale(u);
 #pragma unroll
-          for (int g = 0; g < G; ++g) part[u][g] *= sc;
+          for (int k = 0; k < N2; ++k) part[u][k] *= sc;
         }
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-          part[u][g] = __fadd_rn(part[u][g], dpp<DPP_ROW_HALF_MIRROR>(part[u][g]));
-      // lane c == 0 of each row writes the row's logits; the other lanes write to
-      // their own slots of a scratch area, so no lane is masked off
+      fold_stage<DPP_ROW_HALF_MIRROR, U, G, N2>(part);
+      static_assert(N3 == 1, "three stages reduce up to 8 heads");
+      // lanes c < G of each row hold distinct heads and write them; the others
+      // write to their own slots of a scratch area, so no lane is masked off
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        float* dst = c == 0 ? lg + ((it0 + u) * 8 + r) * G : junk + lane * G;
-        store_logits<G>(dst, part[u], true);
+        float* dst = c < G ? lg + ((it0 + u) * 8 + r) * G + hsel : junk + lane;
+        *dst = part[u][0];
       }
     };
     auto vstep = [&](const Batch<FMT, U>& cur, int it0, int n_it) {
@@ -326,7 +348,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
         const int it = it0 + u;
         const float sc = cur.scale(u);
         // p is 0 for tokens past the end (their logits were stored as -inf); slots
-        // past n_it hold stale LDS (in bounds: CH is a multiple of 2U) and are zeroed
+        // past n_it hold stale LDS (in bounds: CH0, CH1 are multiples of 2U) and are zeroed
         float w[G];
         load_p<G>(lg + (it * 8 + r) * G, w);
 #pragma unroll
@@ -345,7 +367,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     // next chunk's first K batch, so loads stay in flight across the softmax.
     // Two load batches A and B alternate (a 2x-unrolled loop, no register copies);
     // the last K batch prefetches the first V batch, whose loads then overlap the
-    // softmax.  The plan gives every wave at most CH steps (n_it <= CH).
+    // softmax.  The plan gives every wave at most its group's budget (CH0 or CH1) of steps.
     const int n_it = n_steps;
     Batch<FMT, U> A, B;
     A.load(kb, ksb, gw, W, 0, len, r, c);
@@ -537,9 +559,11 @@ __global__ __launch_bounds__(DEC_THREADS) void k_decode_merge(
   }
 }
 
-template <int FMT>
+// steps per load batch: int8 takes 4 (its loads are half the size), except with 8
+// query heads, where the batch registers would not fit beside the partials
+template <int FMT, int G>
 constexpr int batch_rows() {
-  return FMT == KV_FMT_Q8 ? KVQ8_DEC_U_Q8 : KVQ8_DEC_U_F16;
+  return FMT == KV_FMT_Q8 ? (G >= 8 ? 2 : KVQ8_DEC_U_Q8) : KVQ8_DEC_U_F16;
 }
 
 // Split workgroups of one kernel instance that fit on the current device at once
@@ -553,7 +577,7 @@ int resident_splits() {
   if (v > 0) return v;
   int per_cu = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, k_decode_split<FMT, G, batch_rows<FMT>()>, DEC_THREADS,
+          &per_cu, k_decode_split<FMT, G, batch_rows<FMT, G>()>, DEC_THREADS,
           split_lds_bytes<G>()) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
@@ -581,8 +605,8 @@ template <int FMT, int G>
 hipError_t launch_g(const kv_session* tab, const int32_t* lens, int n_sess, int max_len, int kvh,
                     const float* q, float sm_scale, float* out, float* ws_o, float* ws_lse,
                     const DecodePlan& plan, int32_t* status, hipStream_t st) {
-  constexpr int U = batch_rows<FMT>();
-  static_assert(U == 1 || U == 2 || U == 4, "U must divide CH / 2");
+  constexpr int U = batch_rows<FMT, G>();
+  static_assert(U == 1 || U == 2 || U == 4, "U must divide the group budgets / 2");
   dim3 grid(plan.S, kvh, n_sess), block(DEC_THREADS);
   hipLaunchKernelGGL((k_decode_split<FMT, G, U>), grid, block, split_lds_bytes<G>(), st, tab, lens,
                      max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S);
@@ -597,7 +621,8 @@ hipError_t launch_g(const kv_session* tab, const int32_t* lens, int n_sess, int 
 }  // namespace
 
 DecodePlan decode_plan(int fmt, int kvh, int nqh, int n_sess, int max_len) {
-  // Splits per (session, kv head): enough that no wave has more than CH steps, then
+  // Splits per (session, kv head): enough that no wave has more steps than its
+  // group's logits budget (CH0 or CH1), then
   // raised so that the grid is a whole number of rounds of resident workgroups (a
   // last, partly filled round would leave CUs idle), but not past one split per 4
   // steps (so every workgroup has work).
@@ -605,8 +630,16 @@ DecodePlan decode_plan(int fmt, int kvh, int nqh, int n_sess, int max_len) {
   const bool q8 = fmt == KV_FMT_Q8;
   const long long Jf = q8 ? lead_steps<KV_FMT_Q8>((int)J) : lead_steps<KV_FMT_F16>((int)J);
   const long long J1 = J - Jf;
-  const long long CH0 = q8 ? ch0<KV_FMT_Q8>() : ch0<KV_FMT_F16>();
-  const long long CH1 = q8 ? ch1<KV_FMT_Q8>() : ch1<KV_FMT_F16>();
+  const int G = nqh / kvh;
+  long long CH0 = 0, CH1 = 0;
+#define KVQ8_CHB(GG)                                                          \
+  if (G == GG) {                                                              \
+    CH0 = q8 ? ch0<KV_FMT_Q8, GG>() : ch0<KV_FMT_F16, GG>();                  \
+    CH1 = q8 ? ch1<KV_FMT_Q8, GG>() : ch1<KV_FMT_F16, GG>();                  \
+  }
+  KVQ8_CHB(1) KVQ8_CHB(2) KVQ8_CHB(4) KVQ8_CHB(8)
+#undef KVQ8_CHB
+  if (CH0 <= 0) CH0 = 1;  // unsupported G: rejected before any launch
   const long long P = (long long)kvh * n_sess;
   // S0 keeps every wave within its group's LDS budget of logits (CH0 or CH1 steps)
   long long S0 = std::max(1LL, (Jf + GRP_WAVES * CH0 - 1) / (GRP_WAVES * CH0));

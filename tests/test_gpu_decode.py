@@ -61,6 +61,21 @@ def test_single_cell_is_exactly_the_value_row(fmt):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+def test_every_head_ratio(fmt, G):
+    """Each supported query heads per kv head (the K-pass reduction and the logit
+    layout depend on it), at lengths that end inside a step, a split and a chunk."""
+    kvh = 2
+    s, ref = filled(fmt, kvh, 4096, 3001, 20 + G, outliers=True)
+    q = kvsynth.queries(20 + G, 0, 1, kvh * G, 128)[0]
+    sh = shape(fmt, kvh, kvh * G)
+    for length in (1, 9, 777, 3001):
+        say(f"decode fmt={fmt} G={G} len={length}")
+        got = decode_gpu(sh, [s], [length], q[None], sm_scale())[0]
+        check_close(got, oracle_decode(ref, q, length, sm_scale()), f"G={G} len={length}")
+
+
 def test_empty_session_gives_zeros_and_determinism():
     s, ref = filled(Q8, 2, 4096, 4000, 5, outliers=True)
     q = kvsynth.queries(5, 0, 3, 8, 128)
