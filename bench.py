@@ -232,7 +232,7 @@ def traffic_probe(kq, torch, seed):
         lens = torch.zeros(1, dtype=torch.int32, device="cuda")
         kq.kv_append(sh, tab, lens, 1, CTX, xk, xv)
         lens.fill_(CTX)
-        ws = torch.empty(kq.kv_decode_workspace_bytes(sh, 1, CTX), dtype=torch.uint8, device="cuda")
+        ws = kq.kv_decode_workspace(sh, 1, CTX)
         for _ in range(3):
             kq.kv_decode_attn(sh, tab, lens, 1, CTX, q, 1 / math.sqrt(HD), out, ws)
         torch.cuda.synchronize()
@@ -399,8 +399,7 @@ def main():
     xv_new = [torch.from_numpy(kvsynth.kv_tokens(args.seed, li, 1, KVH, HD, "V", True,
                                                  stream=kvsynth.S_V_NEW)[None]).cuda()
               for li in range(LAYERS)]
-    ws = {fmt: torch.empty(kq.kv_decode_workspace_bytes(model[fmt]["shape"], 1, CTX),
-                           dtype=torch.uint8, device="cuda") for fmt in model}
+    ws = {fmt: kq.kv_decode_workspace(model[fmt]["shape"], 1, CTX) for fmt in model}
 
     log(f"warmup {n_warm} steps")
     length = run_steps(kq, torch, model, n_warm, len0, q, xk_new, xv_new, ws)

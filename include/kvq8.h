@@ -40,7 +40,7 @@ typedef enum { KV_FMT_F16 = 0, KV_FMT_Q8 = 1 } kv_fmt;
 
 typedef struct {
   int32_t fmt;        /* kv_fmt */
-  int32_t n_kv_heads; /* >= 1 */
+  int32_t n_kv_heads; /* 1 .. 1024 */
   int32_t n_q_heads;  /* n_kv_heads * G, G in {1, 2, 4, 8}; query head q reads kv head q / G */
   int32_t head_dim;   /* 128 */
 } kv_shape;
@@ -65,7 +65,7 @@ typedef struct {
 
 enum {
   KV_OK = 0,
-  KV_ERR_ARG = -1,         /* null pointer, non-positive size, n_q_heads % n_kv_heads != 0 */
+  KV_ERR_ARG = -1,         /* null pointer, size out of range, n_q_heads % n_kv_heads != 0 */
   KV_ERR_FMT = -2,         /* unknown format, or scale pointers inconsistent with it */
   KV_ERR_ALIGN = -3,       /* pointer not 16-byte aligned, or cap % 64 != 0 */
   KV_ERR_UNSUPPORTED = -4, /* head_dim != 128, or G not in {1, 2, 4, 8} */
@@ -105,7 +105,7 @@ int kv_append(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d
 /* Workspace for kv_decode_attn: split-K partials.  Depends on its arguments and on
  * the current HIP device (the split count follows that device's occupancy); query
  * it with the device current that kv_decode_attn will run on.  0 on invalid
- * arguments. */
+ * arguments (n_sess outside 1 .. 65535). */
 size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_len);
 
 /* Split-K decode attention of one new token per session over the cache, reading
@@ -116,6 +116,7 @@ size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_le
  * fp16 values), fp32 arithmetic.  Partials of each split of the context are
  * merged by log-sum-exp.  d_len[b] == 0 gives a zero row.
  *   d_q   : fp32 [n_sess][n_q_heads][head_dim];  d_out : fp32 [n_sess][n_q_heads][head_dim]
+ *   n_sess : 1 .. 65535.
  *   max_len : host upper bound of every d_len[b] (sizes the grid); a session over it
  *             is flagged KV_DEV_RANGE and gets a zero row.
  *   d_ws, ws_bytes : at least kv_decode_workspace_bytes(h_shape, n_sess, max_len).

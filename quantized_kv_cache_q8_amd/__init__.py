@@ -171,6 +171,13 @@ def kv_decode_workspace_bytes(shape: kv_shape, n_sess: int, max_len: int) -> int
     return int(_lib.kv_decode_workspace_bytes(ctypes.byref(shape), n_sess, max_len))
 
 
+def kv_decode_workspace(shape: kv_shape, n_sess: int, max_len: int, device="cuda") -> torch.Tensor:
+    """A decode workspace on `device` (zero-filled; kv_decode_attn overwrites what it
+    reads)."""
+    return torch.zeros(max(kv_decode_workspace_bytes(shape, n_sess, max_len), 256),
+                       dtype=torch.uint8, device=device)
+
+
 def kv_decode_attn(shape: kv_shape, tab: torch.Tensor, lens: torch.Tensor, n_sess: int,
                    max_len: int, q: torch.Tensor, sm_scale: float, out: torch.Tensor,
                    ws: torch.Tensor, status: torch.Tensor | None = None, stream=None) -> None:

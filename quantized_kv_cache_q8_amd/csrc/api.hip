@@ -14,7 +14,9 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0;
 int check_shape(const kv_shape* s) {
   if (s == nullptr) return KV_ERR_ARG;
   if (s->fmt != KV_FMT_F16 && s->fmt != KV_FMT_Q8) return KV_ERR_FMT;
-  if (s->n_kv_heads < 1 || s->n_q_heads < 1 || s->n_q_heads % s->n_kv_heads != 0) return KV_ERR_ARG;
+  if (s->n_kv_heads < 1 || s->n_kv_heads > KV_MAX_KV_HEADS || s->n_q_heads < 1 ||
+      s->n_q_heads % s->n_kv_heads != 0)
+    return KV_ERR_ARG;
   if (s->head_dim != HD) return KV_ERR_UNSUPPORTED;
   const int G = s->n_q_heads / s->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return KV_ERR_UNSUPPORTED;
@@ -68,7 +70,7 @@ int kv_append(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d
 }
 
 size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_len) {
-  if (check_shape(h_shape) || n_sess < 1 || max_len < 0) return 0;
+  if (check_shape(h_shape) || n_sess < 1 || n_sess > KV_DEC_MAX_SESS || max_len < 0) return 0;
   const DecodePlan p =
       decode_plan(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, n_sess, max_len);
   return p.ws_o_bytes + p.ws_lse_bytes;
@@ -80,7 +82,8 @@ int kv_decode_attn(const kv_shape* h_shape, const kv_session* d_tab, const int32
   int rc = check_shape(h_shape);
   if (rc) return rc;
   if (d_tab == nullptr || d_len == nullptr || d_q == nullptr || d_out == nullptr) return KV_ERR_ARG;
-  if (n_sess < 1 || max_len < 0 || !std::isfinite(sm_scale)) return KV_ERR_ARG;
+  if (n_sess < 1 || n_sess > KV_DEC_MAX_SESS || max_len < 0 || !std::isfinite(sm_scale))
+    return KV_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(d_tab) & 7) || !aligned4(d_len) || !aligned16(d_q) ||
       !aligned16(d_out) || !aligned16(d_ws) || !aligned4(d_status))
     return KV_ERR_ALIGN;

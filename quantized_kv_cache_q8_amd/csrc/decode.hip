@@ -457,106 +457,68 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
   }
 }
 
-// block-wide max / sum over the 256 threads (waves combine through LDS)
-__device__ __forceinline__ float block_max(float v, float* red) {
-  v = wave_max(v);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < DEC_WAVES; ++w) r = fmaxf(r, red[w]);
-  return r;
-}
-__device__ __forceinline__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < DEC_WAVES; ++w) r += red[w];
-  return r;
-}
-
-// One workgroup per (query head, session).  The split lse values are read once,
-// coalesced, for the max and the normaliser; each wave then sums every 4th split's
-// o (2 dims per lane), 8 splits per loop trip so that many loads are in flight.
+// One wave per (session, query head), MERGE_WAVES heads per workgroup.  Splits are
+// taken 64 at a time: lane k loads split j0 + k's lse (one vector load), the wave
+// reduces the chunk's max and weight sum, and the o rows of the chunk (one float2
+// per lane each) are loaded together up front, so a chunk costs about one memory
+// round trip.  Chunks fold in with a running max: out = sum_j 2^(lse_j - L) o_j,
+// L = log2 sum_j 2^lse_j.
+constexpr int MERGE_WAVES = 4;
 template <int FMT>
-__global__ __launch_bounds__(DEC_THREADS) void k_decode_merge(
+__global__ __launch_bounds__(64 * MERGE_WAVES) void k_decode_merge(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int nqh,
-    const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int S,
+    int n_rows, const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int S,
     float* __restrict__ out, int32_t* __restrict__ status) {
-  const int qh = blockIdx.x, b = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * MERGE_WAVES + (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n_rows) return;
+  const int b = row / nqh, qh = row - b * nqh;
   const kv_session ss = tab[b];
   const int len = lens[b];
   int bad = session_bad(ss, FMT);
   if (!bad && (len < 0 || len > ss.cap || len > max_len)) bad = KV_DEV_RANGE;
-  float2* dst = reinterpret_cast<float2*>(out + ((long long)b * nqh + qh) * HD);
+  float2* dst = reinterpret_cast<float2*>(out + (long long)row * HD);
   if (bad || len == 0) {
-    if (wave == 0) dst[lane] = make_float2(0.f, 0.f);
-    if (bad && qh == 0 && threadIdx.x == 0) flag(status, bad);
+    dst[lane] = make_float2(0.f, 0.f);
+    if (bad && qh == 0 && lane == 0) flag(status, bad);
     return;
   }
-  __shared__ float red[DEC_WAVES];
-  __shared__ float2 part[DEC_WAVES][64];
   // workgroups that received a step: those with s * GRP_WAVES < lead_steps(ceil(len / 8))
   const int Sb = min(S, (lead_steps<FMT>((len + 7) >> 3) + GRP_WAVES - 1) / GRP_WAVES);
-  const float* lse = ws_lse + ((long long)b * nqh + qh) * S;
-  const float* o = ws_o + ((long long)b * nqh + qh) * S * HD;
-  float mx = -INFINITY;
-  for (int j = threadIdx.x; j < Sb; j += DEC_THREADS) mx = fmaxf(mx, lse[j]);
-  const float M = block_max(mx, red);
-  float sm = 0.f;
-  for (int j = threadIdx.x; j < Sb; j += DEC_THREADS) sm += exp2f(lse[j] - M);
-  const float L = block_sum(sm, red);
-  constexpr int UN = 8;
-  float2 acc[UN];
+  const float* lse = ws_lse + (long long)row * S;
+  const float2* o = reinterpret_cast<const float2*>(ws_o + (long long)row * S * HD);
+  float M = -INFINITY, L = 0.f;
+  float2 acc = make_float2(0.f, 0.f);
+  for (int j0 = 0; j0 < Sb; j0 += 64) {
+    const int n = min(64, Sb - j0);  // splits in this chunk (wave-uniform)
+    float2 v[64];
 #pragma unroll
-  for (int k = 0; k < UN; ++k) acc[k] = make_float2(0.f, 0.f);
-  int j = wave;
-  for (; j + (UN - 1) * DEC_WAVES < Sb; j += UN * DEC_WAVES) {
-    float2 v[UN];
-    float f[UN];
+    for (int q = 0; q < 4; ++q)
+      if (16 * q < n) {
 #pragma unroll
-    for (int k = 0; k < UN; ++k) {
-      const int jj = j + k * DEC_WAVES;
-      v[k] = reinterpret_cast<const float2*>(o + (long long)jj * HD)[lane];
-      f[k] = lse[jj];
-    }
+        for (int k = 16 * q; k < 16 * q + 16; ++k)
+          v[k] = o[(long long)(j0 + min(k, n - 1)) * (HD / 2) + lane];  // in bounds
+      }
+    const float f = lse[j0 + min(lane, n - 1)];
+    const float Mn = fmaxf(M, wave_max(f));  // finite: the chunk holds split j0
+    const float w = lane < n ? exp2f(f - Mn) : 0.f;
+    const float alpha = exp2f(M - Mn);       // 0 on the first chunk (M = -inf)
+    L = fmaf(L, alpha, wave_sum(w));
+    acc.x *= alpha;
+    acc.y *= alpha;
 #pragma unroll
-    for (int k = 0; k < UN; ++k) {
-      const float w = exp2f(f[k] - M);
-      acc[k].x = fmaf(w, v[k].x, acc[k].x);
-      acc[k].y = fmaf(w, v[k].y, acc[k].y);
-    }
+    for (int q = 0; q < 4; ++q)
+      if (16 * q < n) {
+#pragma unroll
+        for (int k = 16 * q; k < 16 * q + 16; ++k) {
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
+          acc.x = fmaf(wk, v[k].x, acc.x);
+          acc.y = fmaf(wk, v[k].y, acc.y);
+        }
+      }
+    M = Mn;
   }
-  for (; j < Sb; j += DEC_WAVES) {
-    const float w = exp2f(lse[j] - M);
-    const float2 v = reinterpret_cast<const float2*>(o + (long long)j * HD)[lane];
-    acc[0].x = fmaf(w, v.x, acc[0].x);
-    acc[0].y = fmaf(w, v.y, acc[0].y);
-  }
-  float2 a = acc[0];
-#pragma unroll
-  for (int k = 1; k < UN; ++k) {
-    a.x += acc[k].x;
-    a.y += acc[k].y;
-  }
-  part[wave][lane] = a;
-  __syncthreads();
-  if (wave == 0) {
-    float2 t = part[0][lane];
-#pragma unroll
-    for (int w = 1; w < DEC_WAVES; ++w) {
-      t.x += part[w][lane].x;
-      t.y += part[w][lane].y;
-    }
-    dst[lane] = make_float2(t.x / L, t.y / L);
-  }
+  dst[lane] = make_float2(acc.x / L, acc.y / L);
 }
 
 // steps per load batch: int8 takes 4 (its loads are half the size), except with 8
@@ -612,9 +574,10 @@ hipError_t launch_g(const kv_session* tab, const int32_t* lens, int n_sess, int 
                      max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 mgrid(kvh * G, n_sess);
-  hipLaunchKernelGGL((k_decode_merge<FMT>), mgrid, block, 0, st, tab, lens, max_len, kvh * G, ws_o,
-                     ws_lse, plan.S, out, status);
+  const int n_rows = n_sess * kvh * G;
+  dim3 mgrid((n_rows + MERGE_WAVES - 1) / MERGE_WAVES), mblock(64 * MERGE_WAVES);
+  hipLaunchKernelGGL((k_decode_merge<FMT>), mgrid, mblock, 0, st, tab, lens, max_len, kvh * G,
+                     n_rows, ws_o, ws_lse, plan.S, out, status);
   return hipGetLastError();
 }
 

@@ -13,6 +13,10 @@ constexpr int HD = 128;        // head_dim supported by the kernels
 constexpr int NGRP = HD / KV_GROUP;  // fp16 scales per head row (2)
 // most cells per session: a head's rows (<= 256 B each) stay within 32-bit offsets
 constexpr int KV_MAX_CAP = 1 << 24;
+// Most kv heads of a shape (grids put 2 x n_kv_heads on their y extent).
+constexpr int KV_MAX_KV_HEADS = 1024;
+// Most sessions one decode call takes (the grid's z extent).
+constexpr int KV_DEC_MAX_SESS = 65535;
 
 // ---------------------------------------------------------------------------
 // Cross-lane operations (DPP, within a 16-lane row; no LDS traffic)

@@ -81,13 +81,13 @@ def oracle_cache(fmt, kvh, cap, hd, xk_rows, xv_rows, pos=0):
     return c
 
 
-def decode_gpu(sh, sessions, lens, q, sm_scale, max_len=None, status=None):
+def decode_gpu(sh, sessions, lens, q, sm_scale, max_len=None, status=None, ws=None):
     n_sess = len(sessions)
     tab = kq.session_table([s.entry() for s in sessions])
     lt = to_dev(np.asarray(lens, np.int32))
     max_len = int(max(lens)) if max_len is None else max_len
-    ws = torch.empty(max(kq.kv_decode_workspace_bytes(sh, n_sess, max_len), 256), dtype=torch.uint8,
-                     device=DEV)
+    if ws is None:
+        ws = kq.kv_decode_workspace(sh, n_sess, max_len, DEV)
     out = torch.full((n_sess, sh.n_q_heads, sh.head_dim), float("nan"), device=DEV)
     qd = to_dev(q.astype(np.float32))
     kq.kv_decode_attn(sh, tab, lt, n_sess, max_len, qd, sm_scale, out, ws, status)

@@ -115,6 +115,8 @@ def test_decode_validation():
     assert decode(shape(), q=None) == kq.KV_ERR_ARG
     assert decode(shape(), out=None) == kq.KV_ERR_ARG
     assert decode(shape(), n_sess=0) == kq.KV_ERR_ARG
+    assert decode(shape(), n_sess=65536) == kq.KV_ERR_ARG      # the grid's z extent
+    assert decode(shape(kvh=1025, nqh=1025)) == kq.KV_ERR_ARG  # at most 1024 kv heads
     assert decode(shape(), max_len=-1) == kq.KV_ERR_ARG
     assert decode(shape(), sm=math.inf) == kq.KV_ERR_ARG
     assert decode(shape(), sm=math.nan) == kq.KV_ERR_ARG
@@ -132,6 +134,7 @@ def test_decode_workspace_bytes():
     # longer contexts never use fewer splits
     ws = L.kv_decode_workspace_bytes(ctypes.byref(sh), 1, 262144)
     assert ws >= 32 * (128 + 1) * 4
+    assert L.kv_decode_workspace_bytes(ctypes.byref(sh), 65536, 10) == 0
     assert ws % 256 == 0
     assert ws >= L.kv_decode_workspace_bytes(ctypes.byref(sh), 1, 1024)
     assert L.kv_decode_workspace_bytes(ctypes.byref(sh), 0, 10) == 0

@@ -191,6 +191,27 @@ def test_batched64_full_lengths_sampled():
         check_close(got[b], oracle_decode(refs[b], q[b], int(lens[b]), sm_scale()), f"session {b}")
 
 
+def test_workspace_reused_across_shapes():
+    """One workspace for calls of different session counts and lengths (so of
+    different split counts and partial layouts), each checked against the oracle."""
+    kvh, nqh = 2, 8
+    sh = shape(Q8, kvh, nqh)
+    s, ref = filled(Q8, kvh, 8192, 8000, 31, outliers=True)
+    calls = ((1, 8000, [8000]), (9, 300, [300, 1, 0, 299, 64, 65, 7, 200, 300]),
+             (3, 8000, [5000, 8000, 17]), (1, 1, [1]))
+    nbytes = max(kq.kv_decode_workspace_bytes(sh, n, m) for n, m, _ in calls)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    for n_sess, max_len, lens in calls:
+        q = kvsynth.queries(31, 0, n_sess, nqh, 128, sub=n_sess)
+        say(f"reuse n_sess={n_sess} max_len={max_len}")
+        got = decode_gpu(sh, [s] * n_sess, lens, q, sm_scale(), max_len=max_len, ws=ws)
+        for b in range(n_sess):
+            if lens[b] == 0:
+                assert not got[b].any()
+            else:
+                check_close(got[b], oracle_decode(ref, q[b], lens[b], sm_scale()), f"b={b}")
+
+
 def test_device_side_range_checks():
     s, ref = filled(Q8, 2, 128, 100, 8, outliers=False)
     q = kvsynth.queries(8, 0, 2, 4, 128)
@@ -208,7 +229,7 @@ def test_device_side_range_checks():
     sess_entries = [s.entry(), s.entry(), bad]
     tab = kq.session_table(sess_entries)
     lens = to_dev(np.array([129, -1, 10], np.int32))
-    ws = torch.empty(kq.kv_decode_workspace_bytes(sh, 3, 200), dtype=torch.uint8, device=DEV)
+    ws = kq.kv_decode_workspace(sh, 3, 200, DEV)
     out = torch.full((3, 4, 128), 7.0, device=DEV)
     kq.kv_decode_attn(sh, tab, lens, 3, 200, to_dev(np.zeros((3, 4, 128), np.float32)), 0.1, out,
                       ws, status)
