@@ -305,6 +305,59 @@ def traffic_summary(fetch_dir, write_dir, command):
     print(json.dumps(out, indent=1))
 
 
+def stream_ceiling(kq, torch, reps=10):
+    """Read rate of a plain streaming kernel (kv_probe_stream_read: the decode's
+    128-bit non-temporal loads, no arithmetic) over exactly the bytes one decode call
+    reads, per format.  Four buffers of that size rotate, so the 256 MB last-level
+    cache cannot serve repeats; HIP events on the launch stream around reps x 4
+    back-to-back launches, as for the decode."""
+    out = {}
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for key, fmt in (("f16", F16), ("int8", Q8)):
+        nbytes = decode_bytes(fmt, CTX)
+        bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(4)]
+        for b in bufs:
+            kq.kv_probe_stream_read(b, sink)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for b in bufs:
+                kq.kv_probe_stream_read(b, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * len(bufs))
+        out[key] = {"bytes": nbytes, "us": us, "GB_s": nbytes / us / 1e3}
+        del bufs
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_prefill_sample(cache, seed, n_rows=64):
+    """The oracle's prompt-chunk attention at the prefill workload's shape (4096-token
+    chunk at position 131072, P = 135168, 32 query heads) on n_rows evenly spaced
+    rows of the chunk, over the given int8 cache's compacted copy; the full chunk's
+    time is extrapolated by its share of the causal flops."""
+    import kvsynth
+    import oracle
+    pos0, n_tok = 131072, 4096
+    P = pos0 + n_tok
+    q = kvsynth.queries(seed, 0, n_tok, NQH, HD, stream=kvsynth.S_Q_PREFILL)
+    rows = np.linspace(0, n_tok - 1, n_rows).round().astype(np.int64)
+    t0 = time.perf_counter()
+    k16, v16 = oracle.compact_f16(cache, P)
+    t1 = time.perf_counter()
+    oracle.prefill_attn(q, k16, v16, pos0, 1 / math.sqrt(HD), rows=rows)
+    t2 = time.perf_counter()
+    flop_rows = 4.0 * HD * NQH * float(np.sum(pos0 + rows + 1))
+    flop_all = 4.0 * HD * NQH * float(np.sum(pos0 + np.arange(n_tok) + 1))
+    return {"rows": n_rows, "attention_s": t2 - t1, "GFLOP_s": flop_rows / (t2 - t1) / 1e9,
+            "compaction_s": t1 - t0,
+            "extrapolated_chunk_s": (t2 - t1) * flop_all / flop_rows + (t1 - t0),
+            "note": "extrapolated from the sampled rows by causal flops"}
+
+
 def cpu_baseline_leg(seed, repeats=4):
     """The oracle, as it stands, on a bounded sample of the workload: one of the 48
     layers (8 kv heads, 32 query heads, 262144 cells), both formats: cache write
@@ -338,13 +391,17 @@ def cpu_baseline_leg(seed, repeats=4):
             "append_cells_per_s": CTX / (t1 - t0), "append_s": t1 - t0}
         total_bytes += nbytes
         total_s += t2 - t1
+        if fmt == Q8:
+            res["prefill"] = cpu_prefill_sample(c, seed)
         del c
     cores = len(os.sched_getaffinity(0))
     return {"value": total_bytes / total_s / 1e9, "unit": "GB/s", "cores": int(blas_threads),
             "kind": "oracle",
             "sample": f"one layer of the workload (8 kv heads, 32 query heads, 262144 cells), "
                       f"FP16 and int8: oracle cache write of every cell, then its fp64 decode "
-                      f"{repeats}x; value = decode K/V bytes / decode time; numpy elementwise "
+                      f"{repeats}x; value = decode K/V bytes / decode time (per_format.int8."
+                      f"prefill: the oracle's prompt-chunk attention on 64 sampled rows of the "
+                      f"4096-token chunk at 131072, extrapolated); numpy elementwise "
                       f"work on 1 thread, BLAS on {blas_threads} of {cores} cores",
             "host_cores": cores, "per_format": res}
 
@@ -358,6 +415,9 @@ def main():
     ap.add_argument("--seed", type=int, default=44)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the prompt-chunk side (compaction + attention, 2 timed "
+                         "calls), e.g. under rocprofv3 counters")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only what the HBM-traffic counters are read on: a 768 MiB device "
                          "copy (calibration), then per format one 262144-cell layer: bulk "
@@ -384,6 +444,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe(kq, torch, args.seed)
+        return
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_side(kq, torch, 55, steps=2, warmup=1)}), flush=True)
         return
 
     n_steps, n_warm = args.steps, args.warmup
@@ -432,11 +495,17 @@ def main():
                      "tokens_per_s_48_layers": 1.0 / (avg * LAYERS)}
         log(f"fmt={fmt}: {avg * 1e6:.1f} us/layer, {ach:.0f} GB/s ({ach / HBM_PEAK_GBS:.1%})")
     dominant = F16 if roof[F16]["avg_us"] >= roof[Q8]["avg_us"] else Q8
+    del model
+    torch.cuda.empty_cache()
+
+    ceiling = stream_ceiling(kq, torch)
+    for fmt, key in ((F16, "f16"), (Q8, "int8")):
+        roof[fmt]["vs_stream_ceiling"] = roof[fmt]["achieved"] / ceiling[key]["GB_s"]
+        log(f"stream ceiling {key}: {ceiling[key]['GB_s']:.0f} GB/s over {ceiling[key]['bytes']} B; "
+            f"decode at {roof[fmt]['vs_stream_ceiling']:.1%} of it")
 
     prefill = None
     if not args.no_prefill:
-        del model
-        torch.cuda.empty_cache()
         prefill = prefill_side(kq, torch, 55, steps=5, warmup=1)
         log(f"prefill: {prefill['attention_ms']:.2f} ms attention, "
             f"{prefill['attention_TFLOP_s']:.0f} TFLOP/s ({prefill['mfma_frac']:.1%})")
@@ -460,6 +529,7 @@ def main():
         "roofline_int8" if dominant == F16 else "roofline_f16": roof[Q8 if dominant == F16 else F16],
         "cpu_baseline": cpu,
         "append_bulk": append_rate,
+        "stream_ceiling": ceiling,
         "prefill": prefill,
     }
     print(json.dumps(line), flush=True)

@@ -153,6 +153,16 @@ int kv_prefill_attn(const kv_shape* h_shape, const kv_session* h_sess, int pos0,
 /* Static text for a KV_* status code. */
 const char* kv_status_str(int status);
 
+/* Measurement aid, not part of the method: reads bytes bytes at d_src once, with
+ * the loads a decode makes (128-bit, non-temporal, every CU busy) and no
+ * arithmetic, so that its rate is the read bandwidth a decode of the same bytes
+ * can be set against.
+ *   d_src : device, 16-byte aligned; bytes : a multiple of 16 (0: nothing launched).
+ *   d_sink : one device uint32 the kernel may overwrite (it keeps the loads live).
+ * KV_ERR_ARG for a null pointer or bytes not a multiple of 16, KV_ERR_ALIGN for a
+ * misaligned d_src or d_sink, KV_ERR_HIP if the launch fails. */
+int kv_probe_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

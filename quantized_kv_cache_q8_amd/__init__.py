@@ -25,7 +25,8 @@ KV_ERR_WORKSPACE, KV_ERR_RANGE, KV_ERR_HIP = -5, -6, -7
 KV_DEV_RANGE, KV_DEV_BAD_SESSION = 1, 2
 
 EXPORTED = ["kv_cache_bytes", "kv_append", "kv_decode_workspace_bytes", "kv_decode_attn",
-            "kv_compact_f16", "kv_prefill_workspace_bytes", "kv_prefill_attn", "kv_status_str"]
+            "kv_compact_f16", "kv_prefill_workspace_bytes", "kv_prefill_attn", "kv_status_str",
+            "kv_probe_stream_read"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run quantized_kv_cache_q8_amd.build.build() "
@@ -59,6 +60,7 @@ _sig = {
     "kv_prefill_attn": (_I, [ctypes.POINTER(kv_shape), ctypes.POINTER(kv_session), _I, _I, _P,
                              ctypes.c_float, _P, _P, _SZ, _P]),
     "kv_status_str": (ctypes.c_char_p, [_I]),
+    "kv_probe_stream_read": (_I, [_P, _SZ, _P, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -208,6 +210,13 @@ def kv_prefill_attn(shape: kv_shape, sess: kv_session, pos0: int, n_tok: int, q:
                                 _ptr(q, torch.float32, "q"), float(sm_scale),
                                 _ptr(out, torch.float32, "out"), _ptr(ws, None, "ws"), nbytes,
                                 _stream(stream)), "kv_prefill_attn")
+
+
+def kv_probe_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement aid: one plain read of all of src (see include/kvq8.h)."""
+    _check(_lib.kv_probe_stream_read(_ptr(src, None, "src"), src.numel() * src.element_size(),
+                                     _ptr(sink, torch.int32, "sink"), _stream(stream)),
+           "kv_probe_stream_read")
 
 
 def raw_lib() -> ctypes.CDLL:

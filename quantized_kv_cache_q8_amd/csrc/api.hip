@@ -154,6 +154,13 @@ int kv_prefill_attn(const kv_shape* h_shape, const kv_session* h_sess, int pos0,
                                    sm_scale, d_out, st));
 }
 
+int kv_probe_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink, void* stream) {
+  if (d_src == nullptr || d_sink == nullptr || (bytes & 15)) return KV_ERR_ARG;
+  if (!aligned16(d_src) || !aligned4(d_sink)) return KV_ERR_ALIGN;
+  if (bytes == 0) return KV_OK;
+  return hip_status(launch_stream_read(d_src, bytes, d_sink, static_cast<hipStream_t>(stream)));
+}
+
 const char* kv_status_str(int status) {
   switch (status) {
     case KV_OK: return "ok";

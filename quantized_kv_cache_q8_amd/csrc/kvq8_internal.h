@@ -169,4 +169,6 @@ hipError_t launch_prefill(int kvh, int nqh, const uint16_t* k16, const uint16_t*
                           long row_stride, int pos0, int n_tok, const float* d_q,
                           float sm_scale, float* d_out, hipStream_t st);
 
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
+
 }  // namespace kvq8

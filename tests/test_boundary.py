@@ -196,3 +196,13 @@ def test_prefill_validation():
 def test_supported_head_ratios_pass_shape_checks(G):
     # reaches the workspace check (so the shape was accepted)
     assert decode(shape(kvh=2, nqh=2 * G), ws=None) == kq.KV_ERR_WORKSPACE
+
+
+def test_probe_validation():
+    P = L.kv_probe_stream_read
+    assert P(None, 64, B, None) == kq.KV_ERR_ARG
+    assert P(A, 64, None, None) == kq.KV_ERR_ARG
+    assert P(A, 65, B, None) == kq.KV_ERR_ARG          # not a whole number of 16-byte words
+    assert P(A + 8, 64, B, None) == kq.KV_ERR_ALIGN
+    assert P(A, 64, B + 2, None) == kq.KV_ERR_ALIGN
+    assert P(A, 0, B, None) == kq.KV_OK                # nothing to read, nothing launched
