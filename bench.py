@@ -36,6 +36,8 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attn KV read GB/s (% HBM peak) at 262144 ctx, fp16 & int8; append cells/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix, vendor figure
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed FMA), vendor figure
+DECODE_FLOP_PER_TOKEN_HEAD = 2048  # per (context token, kv head): 4 heads x 128 dims x 2 x 2
 KVH, NQH, HD, CTX, LAYERS = 8, 32, 128, 262144, 48
 F16, Q8 = 0, 1
 BYTES_PER_CELL_HEAD = {F16: 2 * HD * 2, Q8: 2 * (HD + 2 * (HD // 64))}   # K+V per (cell, kv head)
@@ -493,6 +495,18 @@ def main():
                      "kernel": "k_decode_split + k_decode_merge (one kv_decode_attn call)",
                      "avg_us": avg * 1e6, "algorithmic_bytes_per_launch": per_launch,
                      "tokens_per_s_48_layers": 1.0 / (avg * LAYERS)}
+        if fmt == Q8:
+            # the int8 decode issues vector instructions ~90 % of the SIMD time (SQ
+            # counters): its arithmetic, set against the vector ALU peak
+            flop = DECODE_FLOP_PER_TOKEN_HEAD * KVH * float(np.mean([length + s + 1
+                                                                     for s in range(n_steps)]))
+            tf = flop / avg / 1e12
+            roof[fmt]["alu_view"] = {
+                "bound": "alu", "achieved": tf, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": tf / FP32_VECTOR_PEAK_TFLOPS, "algorithmic_flop_per_launch": flop,
+                "peak_without_packed_fma": FP32_VECTOR_PEAK_TFLOPS / 2,
+                "note": "2048 flop per (token, kv head): 4 query heads x 128 dims x 2 (K, V) "
+                        "x 2; packed fp32 FMA, half of the peak, is not used"}
         log(f"fmt={fmt}: {avg * 1e6:.1f} us/layer, {ach:.0f} GB/s ({ach / HBM_PEAK_GBS:.1%})")
     dominant = F16 if roof[F16]["avg_us"] >= roof[Q8]["avg_us"] else Q8
     del model
