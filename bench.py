@@ -336,6 +336,116 @@ def stream_ceiling(kq, torch, reps=10):
     return out
 
 
+def _time_calls(torch, calls, reps):
+    """Mean HIP-event time (s) of each of the zero-argument callables in calls,
+    recorded around it on the launch stream over reps rounds."""
+    ev = [[] for _ in calls]
+    for _ in range(reps):
+        for i, f in enumerate(calls):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            ev[i].append((e0, e1))
+    torch.cuda.synchronize()
+    return [float(np.mean([a.elapsed_time(b) for a, b in e])) * 1e-3 for e in ev]
+
+
+def side_configs(kq, torch, steps=10, warmup=3):
+    """The smaller workloads: the 64-session int8 batch (session lengths uniform on
+    [1024, 65536], one session table; a step is one batched 1-token append and one
+    batched decode), and single-session decodes at 32768 cells (F16) and 131072
+    cells (int8) over 4 layer copies in turn, so the 256 MB last-level cache cannot
+    serve repeats.  Cache contents come from seeded host K/V (outlier channels)."""
+    import kvsynth
+    out = {}
+    sm = 1 / math.sqrt(HD)
+
+    # ---- 64 sessions ---------------------------------------------------------
+    w = kvsynth.WORKLOADS["batched64_q8"]
+    lens = [int(x) for x in kvsynth.session_lengths(w["seed"], w["batch"], w["lo"], w["hi"])]
+    n_sess, hi = len(lens), max(lens)
+    sh = kq.make_shape(Q8, KVH, NQH, HD)
+    dk = torch.from_numpy(kvsynth.kv_tokens(w["seed"], 0, hi, KVH, HD, "K", True)[None]).cuda()
+    dv = torch.from_numpy(kvsynth.kv_tokens(w["seed"], 0, hi, KVH, HD, "V", True)[None]).cuda()
+    sess = [kq.Session(Q8, KVH, kvsynth.round_up(n + steps + warmup + 1, 64)) for n in lens]
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for s_, n in zip(sess, lens):
+        kq.kv_append(sh, kq.session_table([s_.entry()]), zero, 1, n,
+                     dk[:, :n].contiguous(), dv[:, :n].contiguous())
+    del dk, dv
+    tab = kq.session_table([s_.entry() for s_ in sess])
+    lens_w = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    lens_d = lens_w + 1
+    q = torch.from_numpy(kvsynth.queries(w["seed"], 0, n_sess, NQH, HD)).cuda()
+    xk1 = torch.from_numpy(kvsynth.kv_tokens(w["seed"], 0, n_sess, KVH, HD, "K", True,
+                                             stream=kvsynth.S_K_NEW)[:, None]).cuda()
+    xv1 = torch.from_numpy(kvsynth.kv_tokens(w["seed"], 0, n_sess, KVH, HD, "V", True,
+                                             stream=kvsynth.S_V_NEW)[:, None]).cuda()
+    max_len = hi + steps + warmup + 1
+    ws = kq.kv_decode_workspace(sh, n_sess, max_len)
+    o = torch.empty((n_sess, NQH, HD), device="cuda")
+    t_app, t_dec, read = [], [], 0
+    for step in range(warmup + steps):
+        ta, td = _time_calls(torch, [
+            lambda: kq.kv_append(sh, tab, lens_w, n_sess, 1, xk1, xv1),
+            lambda: kq.kv_decode_attn(sh, tab, lens_d, n_sess, max_len, q, sm, o, ws)], 1)
+        if step >= warmup:
+            t_app.append(ta)
+            t_dec.append(td)
+            read += decode_bytes(Q8, int(lens_d.sum().item()))
+        lens_w += 1
+        lens_d += 1
+    assert torch.isfinite(o).all().item()
+    out["batched64_int8"] = {
+        "workload": "64 int8 sessions, lengths uniform on [1024, 65536] (sum "
+                    f"{sum(lens)}), one session table; a step = batched 1-token append + "
+                    "batched decode",
+        "decode_us": float(np.mean(t_dec)) * 1e6,
+        "decode_GB_s": read / sum(t_dec) / 1e9,
+        "decode_frac_hbm": read / sum(t_dec) / 1e9 / HBM_PEAK_GBS,
+        "append_us": float(np.mean(t_app)) * 1e6,
+        "append_cells_per_s": n_sess / float(np.mean(t_app))}
+    log(f"batched64 int8: decode {out['batched64_int8']['decode_us']:.1f} us = "
+        f"{out['batched64_int8']['decode_GB_s']:.0f} GB/s; append "
+        f"{out['batched64_int8']['append_us']:.1f} us per 64 cells")
+    del sess, tab, ws
+    torch.cuda.empty_cache()
+
+    # ---- single sessions at 32768 (F16) and 131072 (int8) cells ----------------
+    for key, fmt in (("f16_ctx32768", F16), ("q8_ctx131072", Q8)):
+        w = kvsynth.WORKLOADS[key]
+        ctx = w["ctx"]
+        sh = kq.make_shape(fmt, KVH, NQH, HD)
+        dk = torch.from_numpy(kvsynth.kv_tokens(w["seed"], 0, ctx, KVH, HD, "K", True)[None]).cuda()
+        dv = torch.from_numpy(kvsynth.kv_tokens(w["seed"], 0, ctx, KVH, HD, "V", True)[None]).cuda()
+        cap = kvsynth.round_up(ctx, 64)
+        copies = []
+        for i in range(4):
+            s_ = kq.Session(fmt, KVH, cap)
+            kq.kv_append(sh, kq.session_table([s_.entry()]), zero, 1, ctx, dk, dv)
+            copies.append(s_)
+        del dk, dv
+        tabs = [kq.session_table([s_.entry()]) for s_ in copies]
+        ld = torch.full((1,), ctx, dtype=torch.int32, device="cuda")
+        q = torch.from_numpy(kvsynth.queries(w["seed"], 0, 1, NQH, HD)).cuda()
+        ws = kq.kv_decode_workspace(sh, 1, ctx)
+        o = torch.empty((1, NQH, HD), device="cuda")
+        calls = [lambda t=t: kq.kv_decode_attn(sh, t, ld, 1, ctx, q, sm, o, ws) for t in tabs]
+        _time_calls(torch, calls, warmup)
+        ts = _time_calls(torch, calls, steps)
+        t = float(np.mean(ts))
+        nb = decode_bytes(fmt, ctx)
+        out[key] = {"workload": f"{'F16' if fmt == F16 else 'int8'} cache, {ctx} cells, "
+                                "4 copies in turn", "decode_us": t * 1e6,
+                    "decode_GB_s": nb / t / 1e9, "decode_frac_hbm": nb / t / 1e9 / HBM_PEAK_GBS}
+        log(f"{key}: decode {t * 1e6:.1f} us = {nb / t / 1e9:.0f} GB/s")
+        del copies, tabs, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_prefill_sample(cache, seed, n_rows=64):
     """The oracle's prompt-chunk attention at the prefill workload's shape (4096-token
     chunk at position 131072, P = 135168, 32 query heads) on n_rows evenly spaced
@@ -518,6 +628,8 @@ def main():
         log(f"stream ceiling {key}: {ceiling[key]['GB_s']:.0f} GB/s over {ceiling[key]['bytes']} B; "
             f"decode at {roof[fmt]['vs_stream_ceiling']:.1%} of it")
 
+    sides = side_configs(kq, torch)
+
     prefill = None
     if not args.no_prefill:
         prefill = prefill_side(kq, torch, 55, steps=5, warmup=1)
@@ -544,6 +656,7 @@ def main():
         "cpu_baseline": cpu,
         "append_bulk": append_rate,
         "stream_ceiling": ceiling,
+        "side_configs": sides,
         "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
