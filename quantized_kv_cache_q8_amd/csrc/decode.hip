@@ -95,6 +95,20 @@ __host__ __device__ constexpr int lead_steps(int J) {  // >= J - lead_steps(J) (
 }
 constexpr float LOG2E = 1.4426950408889634f;
 
+// fewest steps a wave of the leading group is given when a session is short for the
+// grid's split count (the grid is sized by the longest session of the call)
+#ifndef KVQ8_DEC_MIN_STEPS
+#define KVQ8_DEC_MIN_STEPS 16
+#endif
+// Splits (workgroups) that work on a session of len cells, of the S in the grid: all
+// of them for long sessions, fewer for short ones so that no wave gets a token or
+// two; the split kernel and the merge both use it.
+template <int FMT>
+__host__ __device__ inline int active_splits(int len, int S) {
+  const int Jf = lead_steps<FMT>((len + 7) >> 3);
+  return min(S, max(1, (Jf + GRP_WAVES * KVQ8_DEC_MIN_STEPS - 1) / (GRP_WAVES * KVQ8_DEC_MIN_STEPS)));
+}
+
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -245,6 +259,8 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     float* __restrict__ ws_lse, int S) {
   constexpr int CH0 = ch0<FMT, G>(), CH1 = ch1<FMT, G>();
   static_assert(CH0 % (2 * U) == 0 && CH1 % (2 * U) == 0, "a chunk holds whole pairs of load batches");
+  static_assert(CH0 >= KVQ8_DEC_MIN_STEPS && (!GROUPED || CH1 >= KVQ8_DEC_MIN_STEPS),
+                "a short session's waves (at most KVQ8_DEC_MIN_STEPS steps) fit the logits budget");
   const int s_idx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int nqh = kvh * G;
   const kv_session ss = tab[b];
@@ -252,7 +268,8 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
   if (session_bad(ss, FMT) || len < 0 || len > ss.cap || len > max_len) return;  // merge flags
   const int J = (len + 7) >> 3;                  // 8-token steps of this session
   const int Jf = lead_steps<FMT>(J);             // steps of group 0 (>= those of group 1)
-  if (s_idx * GRP_WAVES >= Jf) return;           // no step for this workgroup
+  const int Sb = active_splits<FMT>(len, S);   // workgroups of this session
+  if (s_idx >= Sb) return;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane >> 3, c = lane & 7;
@@ -260,7 +277,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
   const int Jg = grp ? J - Jf : Jf;              // steps of this wave's group
   const int gw0 = s_idx * GRP_WAVES + wg;        // wave index within the group's waves
   const int gw = (grp ? Jf : 0) + gw0;           // first step of this wave
-  const int W = S * GRP_WAVES;                   // waves per group of (session, head)
+  const int W = Sb * GRP_WAVES;                  // waves per group of (session, head)
   const int n_steps = gw0 < Jg ? (Jg - 1 - gw0) / W + 1 : 0;
 
   extern __shared__ float smem[];
@@ -483,8 +500,8 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void k_decode_merge(
     if (bad && qh == 0 && lane == 0) flag(status, bad);
     return;
   }
-  // workgroups that received a step: those with s * GRP_WAVES < lead_steps(ceil(len / 8))
-  const int Sb = min(S, (lead_steps<FMT>((len + 7) >> 3) + GRP_WAVES - 1) / GRP_WAVES);
+  // the splits that worked on this session (the same count the split kernel used)
+  const int Sb = active_splits<FMT>(len, S);
   const float* lse = ws_lse + (long long)row * S;
   const float2* o = reinterpret_cast<const float2*>(ws_o + (long long)row * S * HD);
   float M = -INFINITY, L = 0.f;
