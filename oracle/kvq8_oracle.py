@@ -15,6 +15,16 @@ Sources (web pages; cited by title and section):
   [P3] PR #711 "kv: --kv k8v4 streams with --kv-resident": sections What, How.
 
 Readings where the pages are silent (all listed in the design doc):
+  * K8V4 ([P3, What]: "INT8 K + rotated Q4_0 V"): K is the q8 K; V is rotated by
+    the orthonormal Walsh-Hadamard matrix H/sqrt(HD) (H the Sylvester Hadamard
+    matrix), computed as the unnormalised transform w = H x in fp32 butterflies
+    (stages h = 1, 2, 4, ..., HD/2), then quantised per 32-value block with the
+    int8 rule with 7 for 127: d = fp16(max|w| / 7), code = clamp(rint(w / d), -7, 7),
+    stored as code + 8 in nibbles (byte j: value 2j low, 2j+1 high).  The V a
+    read sees is H (code * d) / HD, i.e. H/sqrt(HD) applied to code * d / sqrt(HD)
+    ... = the orthonormal rotation undone.  Which rotation and which 4-bit
+    rounding the pages' kernels use is not on the pages: those two are readings,
+    pinned here to mathematics, not to the pages.
   * fp16(.) is IEEE round-to-nearest-even; rint is round-half-to-even.
   * ``x / scale`` divides by the *stored* fp16 scale widened to fp32, with a
     true IEEE fp32 division (not a reciprocal multiply).
@@ -37,20 +47,27 @@ import numpy as np
 
 GROUP = 64          # dims per fp16 scale  [P1, Summary]
 QMAX = 127          # symmetric int8 range [P1, What changed]
-FMT_F16, FMT_Q8 = 0, 1
+Q4_BLOCK = 32       # values per fp16 scale of the 4-bit V (Q4_0 blocks) [P3, What]
+Q4_MAX = 7          # symmetric 4-bit range (codes -7 .. 7, stored + 8 in a nibble)
+FMT_F16, FMT_Q8, FMT_K8V4 = 0, 1, 2
 
 
 # ----------------------------------------------------------------------------
 # Storage cost
 # ----------------------------------------------------------------------------
 def cache_bytes(fmt: int, kvh: int, cap: int, hd: int, part: int) -> int:
-    """Bytes of one K (or one V) array of one layer.
+    """Bytes of one array of one layer.
 
-    part 0: values (fp16, 2 B each) or int8 codes (1 B each); part 1: the fp16
-    scales of the q8 format (one 2-B scale per 64 values, [P1, Summary]); the
-    FP16 format has no scales.
+    part 0: K values (fp16, 2 B each) or int8 codes (1 B each); part 1: the fp16
+    K scales of the q8 and K8V4 formats (one 2-B scale per 64 values, [P1,
+    Summary]); the FP16 format has no scales.  parts 2 and 3: the same for V, which
+    differs only for K8V4 (4-bit codes, 2 per byte, and one fp16 scale per 32
+    values [P3, What]).
     """
     n = kvh * cap * hd
+    if part in (2, 3) and fmt == FMT_K8V4:
+        return n // 2 if part == 2 else 2 * (n // Q4_BLOCK)
+    part = part - 2 if part in (2, 3) else part
     if part == 0:
         return 2 * n if fmt == FMT_F16 else n
     return 0 if fmt == FMT_F16 else 2 * (n // GROUP)
@@ -80,6 +97,60 @@ def quantize_q8(x: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return codes.reshape(x.shape), s16
 
 
+def fwht_f32(x: np.ndarray) -> np.ndarray:
+    """Unnormalised Walsh-Hadamard transform over the last axis (length a power of
+    two), H x with H the Sylvester Hadamard matrix, as fp32 butterflies: stage h
+    (h = 1, 2, 4, ...) maps each pair (i, i + h) inside blocks of 2h to (a + b,
+    a - b).  Every output of a stage is one IEEE fp32 addition or subtraction, so
+    the result does not depend on the order pairs are visited in."""
+    y = np.array(x, dtype=np.float32, copy=True)
+    n = y.shape[-1]
+    assert n & (n - 1) == 0
+    lead = y.shape[:-1]
+    h = 1
+    while h < n:
+        z = y.reshape(*lead, n // (2 * h), 2, h)
+        a, b = z[..., 0, :], z[..., 1, :]
+        y = np.stack([a + b, a - b], axis=-2).reshape(*lead, n)
+        h *= 2
+    return y
+
+
+def quantize_q4(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """4-bit quantisation of the rotated V, per 32-value block (the int8 rule with
+    7 for 127): d = fp16(max|w| / 7), code = clamp(rint(w / d), -7, 7), a zero scale
+    giving code 0.  w: float32 [..., HD].  Returns (codes int8 in -7..7 [..., HD],
+    scales float16 [..., HD // 32])."""
+    w = np.asarray(w, dtype=np.float32)
+    hd = w.shape[-1]
+    assert hd % Q4_BLOCK == 0
+    g = w.reshape(*w.shape[:-1], hd // Q4_BLOCK, Q4_BLOCK)
+    amax = np.abs(g).max(axis=-1)
+    d16 = (amax / np.float32(Q4_MAX)).astype(np.float16)
+    d32 = d16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = g / d32
+    r = np.where(d32 == 0, np.float32(0), r)
+    codes = np.clip(np.rint(r), -Q4_MAX, Q4_MAX).astype(np.int8)
+    return codes.reshape(w.shape), d16
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """codes int8 -8..7 [..., HD] -> uint8 [..., HD // 2]: byte j holds code 2j + 8
+    in its low nibble and code 2j + 1 + 8 in its high nibble."""
+    u = (np.asarray(codes, np.int16) + 8).astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(b: np.ndarray) -> np.ndarray:
+    """The inverse of pack_nibbles: uint8 [..., HD // 2] -> int8 -8..7 [..., HD]."""
+    b = np.asarray(b, np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.int8)
+    out[..., 0::2] = (b & 0x0F).astype(np.int8) - 8
+    out[..., 1::2] = (b >> 4).astype(np.int8) - 8
+    return out
+
+
 def store_f16(x: np.ndarray) -> np.ndarray:
     """FP16 cache write of [P1, Summary]: IEEE round-to-nearest-even to binary16."""
     return np.asarray(x, dtype=np.float32).astype(np.float16)
@@ -95,6 +166,8 @@ class Cache:
     Q8 : k, v int8 [kvh][cap][hd] plus k_scale, v_scale float16 [kvh][cap][hd/64]
          (scale arrays kept beside the code arrays, [P1, What changed]; codes and
          scales are separate runs of bytes, [P3, How]).
+    K8V4: k, k_scale as Q8; v uint8 [kvh][cap][hd/2] (4-bit codes of the rotated
+         row, pack_nibbles), v_scale float16 [kvh][cap][hd/32].
     """
 
     def __init__(self, fmt: int, kvh: int, cap: int, hd: int):
@@ -103,6 +176,11 @@ class Cache:
             self.k = np.zeros((kvh, cap, hd), np.float16)
             self.v = np.zeros((kvh, cap, hd), np.float16)
             self.k_scale = self.v_scale = None
+        elif fmt == FMT_K8V4:
+            self.k = np.zeros((kvh, cap, hd), np.int8)
+            self.k_scale = np.zeros((kvh, cap, hd // GROUP), np.float16)
+            self.v = np.zeros((kvh, cap, hd // 2), np.uint8)
+            self.v_scale = np.zeros((kvh, cap, hd // Q4_BLOCK), np.float16)
         else:
             self.k = np.zeros((kvh, cap, hd), np.int8)
             self.v = np.zeros((kvh, cap, hd), np.int8)
@@ -119,6 +197,10 @@ class Cache:
             rows = np.transpose(np.asarray(src, np.float32), (1, 0, 2))  # [kvh][n][hd]
             if self.fmt == FMT_F16:
                 getattr(self, dst)[:, pos:pos + n] = store_f16(rows)
+            elif self.fmt == FMT_K8V4 and dst == "v":
+                c, s = quantize_q4(fwht_f32(rows))
+                self.v[:, pos:pos + n] = pack_nibbles(c)
+                self.v_scale[:, pos:pos + n] = s
             else:
                 c, s = quantize_q8(rows)
                 getattr(self, dst)[:, pos:pos + n] = c
@@ -133,20 +215,44 @@ class Cache:
         if self.fmt == FMT_F16:
             return vals.astype(np.float64)
         sc = getattr(self, which + "_scale")[:, :length].astype(np.float64)
+        if self.fmt == FMT_K8V4 and which == "v":
+            # the rotation undone: H (code * d) / HD, exact in float64 up to the sum
+            rot = self.v_rotated(length)
+            return rot @ hadamard_f64(self.hd).T / self.hd
         return vals.astype(np.float64) * np.repeat(sc, GROUP, axis=-1)
+
+    def v_rotated(self, length: int) -> np.ndarray:
+        """K8V4: the dequantised rotated V, code * d (exact), float64 [kvh][length][hd]."""
+        assert self.fmt == FMT_K8V4
+        codes = unpack_nibbles(self.v[:, :length]).astype(np.float64)
+        d = self.v_scale[:, :length].astype(np.float64)
+        return codes * np.repeat(d, Q4_BLOCK, axis=-1)
 
 
 # ----------------------------------------------------------------------------
 # O4: compaction to the FP16 [kvh][P][HD] copy the prompt GEMMs read
 # ----------------------------------------------------------------------------
+def hadamard_f64(n: int) -> np.ndarray:
+    """The Sylvester Hadamard matrix of order n (a power of two), float64."""
+    h = np.ones((1, 1))
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
 def compact_f16(cache: Cache, P: int) -> tuple[np.ndarray, np.ndarray]:
     """[P1, Extra Notes]: the prompt chunk's GEMMs read an FP16 [kvh][P][HD] copy
     of the cache.  F16: rows 0..P-1 copied (a stride change only).  q8:
-    fp16(float(code) * float(scale)), one rounding of an exact fp32 product."""
+    fp16(float(code) * float(scale)), one rounding of an exact fp32 product.
+    K8V4 V: the rotation undone in fp32 -- u = code * d (exact), then
+    fp16(fwht_f32(u) * 2^-log2(HD)) (the power of two is exact)."""
     out = []
     for which in ("k", "v"):
         vals = getattr(cache, which)[:, :P]
-        if cache.fmt == FMT_F16:
+        if cache.fmt == FMT_K8V4 and which == "v":
+            u = cache.v_rotated(P).astype(np.float32)          # exact in fp32
+            out.append((fwht_f32(u) * np.float32(1.0 / cache.hd)).astype(np.float16))
+        elif cache.fmt == FMT_F16:
             out.append(vals.copy())
         else:
             sc = getattr(cache, which + "_scale")[:, :P].astype(np.float32)

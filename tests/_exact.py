@@ -67,3 +67,41 @@ def quant_group_exact(xs, brute: bool = False):
             c = min(cands, key=lambda c: (abs(r - c), c % 2))
             codes.append(c)
     return s, codes
+
+
+def quant_block_exact(xs, qmax: int, lo: int, hi: int, brute: bool = False):
+    """The same rule for any symmetric range: s = f16(f32(amax / qmax)); code = the
+    integer in [lo, hi] nearest to f32(x / s), ties to even (0 when s == 0)."""
+    fx = [Fraction(float(x)) for x in xs]
+    amax = max(abs(v) for v in fx)
+    s = f16(f32(amax / qmax))
+    codes = []
+    for v in fx:
+        if s == 0:
+            codes.append(0)
+            continue
+        r = f32(v / s)
+        if brute:
+            codes.append(nearest_code(r, lo, hi))
+        else:
+            n = r.numerator // r.denominator
+            cands = [c for c in (n, n + 1) if lo <= c <= hi] or [hi if r > 0 else lo]
+            codes.append(min(cands, key=lambda c: (abs(r - c), c % 2)))
+    return s, codes
+
+
+def fwht_f32_exact(xs):
+    """The butterfly Walsh-Hadamard transform with each addition and subtraction
+    rounded to fp32, written out in exact fractions: stage h = 1, 2, 4, ... maps
+    (y[i], y[i + h]) to (f32(y[i] + y[i + h]), f32(y[i] - y[i + h])) for i in the
+    first half of each block of 2h."""
+    y = [Fraction(float(v)) for v in xs]
+    n = len(y)
+    h = 1
+    while h < n:
+        for i0 in range(0, n, 2 * h):
+            for i in range(i0, i0 + h):
+                a, b = y[i], y[i + h]
+                y[i], y[i + h] = f32(a + b), f32(a - b)
+        h *= 2
+    return y

@@ -21,6 +21,13 @@ What pins what:
   * prefill: torch's causal SDPA over the whole sequence (rows pos0..);
     a one-token chunk equals decode; future keys do not affect a row; brute force.
   * compaction: the exact rational product rounded once to fp16.
+  * K8V4: the rotation against SciPy's Hadamard matrix (a library routine), its
+    involution H H = 128 I and a rounding bound, and the per-operation fp32
+    rounding written out in fractions; the 4-bit quantiser by hand-worked
+    examples, brute force and invariants; the nibble layout; the read-back
+    against SciPy's matrix and a closed-form error bound; the compacted V exact
+    on dyadic inputs and per row against the fraction butterflies; the byte
+    count against the 816 B per cell of PR #711, section What.
 """
 from __future__ import annotations
 
@@ -33,7 +40,7 @@ import numpy as np
 import torch
 import torch.nn.functional as F
 
-from _exact import f16, quant_group_exact
+from _exact import f16, fwht_f32_exact, quant_block_exact, quant_group_exact
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -394,3 +401,161 @@ def pin_compact_exact(compact, Cache, FMT_F16, FMT_Q8):
                     [tuple(r.integers(0, m) for m in (kvh, n, hd)) for _ in range(200)]:
                 exact = Fraction(int(codes[h, t, d])) * Fraction(float(sc[h, t, d // 64]))
                 assert Fraction(float(out[h, t, d])) == f16(exact), (which, h, t, d)
+
+
+# ----------------------------------------------------------------------------
+# K8V4: rotation, 4-bit quantiser, nibble layout, read-back, byte count
+# ----------------------------------------------------------------------------
+def _hadamard(n):
+    from scipy.linalg import hadamard
+    return hadamard(n).astype(np.float64)
+
+
+def pin_fwht(fwht):
+    H = _hadamard(128)
+    r = np.random.default_rng(80)
+    xi = r.integers(-1000, 1001, size=(20, 128)).astype(np.float32)   # integer rows: exact
+    assert np.array_equal(fwht(xi).astype(np.float64), xi.astype(np.float64) @ H.T)
+    assert np.array_equal(fwht(fwht(xi)), xi * np.float32(128))        # H H = 128 I
+    x = r.standard_normal((50, 128)).astype(np.float32)
+    err = np.abs(fwht(x).astype(np.float64) - x.astype(np.float64) @ H.T)
+    # seven stages, each rounding a partial sum bounded by the sum of |x|
+    assert (err <= 7 * 2.0 ** -24 * np.abs(x).astype(np.float64).sum(-1, keepdims=True)).all()
+    for row in r.standard_normal((12, 8)).astype(np.float32):         # order-8 rows, in fractions
+        assert [Fraction(float(v)) for v in fwht(row[None])[0]] == fwht_f32_exact(row)
+    for row in x[:3]:
+        assert [Fraction(float(v)) for v in fwht(row[None])[0]] == fwht_f32_exact(row)
+
+
+def _q4_block(vals):
+    x = np.zeros(32, np.float32)
+    x[: len(vals)] = np.asarray(vals, np.float32)
+    return x
+
+
+def pin_q4_worked_examples(quant4):
+    # amax 7 -> d = 7/7 = 1 exactly: codes are rint(x), ties to even; -3.5 -> -4
+    a = _q4_block([7, -3.5, 0.5, 1.5, 2.5, -7, 0, 6.49])
+    # amax 14 -> d = 2: x / 2 = 7, 0.5 -> 0, 1.5 -> 2, -2.5 -> -2, 3.25 -> 3
+    b = _q4_block([14, 1, 3, -5, 6.5])
+    z = _q4_block([])                              # all zero: d = 0, codes 0
+    # amax 0.7 -> d = fp16(0.1) = 0x2E66 = 0.0999755859375; 0.7 / d = 7.0017 -> 7,
+    # -0.35 / d = -3.5009 -> -4 (not a tie), 0.05 / d = 0.5001 -> 1
+    t = _q4_block([0.7, -0.35, 0.05])
+    codes, d = quant4(np.stack([a, b, z, t]))
+    bits = [int(v) for v in d.view(np.uint16)[:, 0]]
+    assert bits == [0x3C00, 0x4000, 0x0000, 0x2E66], [hex(v) for v in bits]
+    assert codes[0, :8].tolist() == [7, -4, 0, 2, 2, -7, 0, 6]
+    assert codes[1, :5].tolist() == [7, 0, 2, -2, 3]
+    assert not codes[2].any()
+    assert codes[3, :3].tolist() == [7, -4, 1]
+    # four blocks per 128-dim row, each with its own scale
+    row = np.concatenate([a, b, z, t])
+    c, s = quant4(row[None])
+    assert s.shape == (1, 4) and np.array_equal(c[0], codes.reshape(-1))
+
+
+def _random_blocks(seed, n):
+    r = np.random.default_rng(seed)
+    x = r.standard_normal((n, 32), dtype=np.float32)
+    x *= np.exp2(r.integers(-20, 12, size=(n, 1))).astype(np.float32)
+    x[r.random((n, 32)) < 0.05] *= np.float32(20)
+    x[:2] = 0
+    x[1, 3] = np.float32(-1e-30)
+    return x
+
+
+def pin_q4_brute_force(quant4, n=300):
+    x = _random_blocks(81, n)
+    codes, d = quant4(x)
+    for i in range(n):
+        s, c = quant_block_exact(x[i], 7, -7, 7, brute=(i < 8))
+        assert Fraction(float(d[i, 0])) == s, i
+        assert codes[i].tolist() == c, i
+
+
+def pin_q4_invariants(quant4):
+    x = _random_blocks(82, 4000)
+    codes, d = quant4(x)
+    c = codes.astype(np.int32)
+    s = d[:, 0].astype(np.float64)
+    assert np.abs(c).max() <= 7
+    normal = s >= 2.0 ** -14
+    assert normal.sum() > 1000
+    assert (np.abs(c[normal]).max(-1) == 7).all()
+    err = np.abs(c * s[:, None] - x.astype(np.float64))
+    assert (err[normal] <= s[normal, None] * (0.5 + 2.0 ** -8)).all()
+    cn, dn = quant4(-x)
+    assert np.array_equal(cn, -codes) and np.array_equal(dn.view(np.uint16), d.view(np.uint16))
+
+
+def pin_nibbles(pack, unpack):
+    # byte j: code 2j + 8 in the low nibble, code 2j + 1 + 8 in the high nibble
+    assert pack(np.array([[-8, 7, 0, -1]], np.int8)).tolist() == [[0xF0, 0x78]]
+    c = np.random.default_rng(83).integers(-8, 8, size=(7, 128)).astype(np.int8)
+    b = pack(c)
+    assert b.shape == (7, 64) and b.dtype == np.uint8
+    assert np.array_equal(unpack(b), c)
+    assert np.array_equal(b & 0x0F, (c[:, 0::2] + 8).astype(np.uint8))
+
+
+def pin_k8v4_read(Cache, FMT_K8V4, unpack):
+    kvh, hd, cap, n = 2, 128, 64, 24
+    r = np.random.default_rng(84)
+    xk = r.standard_normal((n, kvh, hd), dtype=np.float32)
+    xv = r.standard_normal((n, kvh, hd), dtype=np.float32)
+    xv[:, :, 5] *= np.float32(20)                                    # an outlier channel
+    c = Cache(FMT_K8V4, kvh, cap, hd)
+    assert c.append(0, xk, xv)
+    assert c.v.shape == (kvh, cap, hd // 2) and c.v_scale.shape == (kvh, cap, hd // 32)
+    codes = unpack(c.v[:, :n]).astype(np.float64)
+    d = np.repeat(c.v_scale[:, :n].astype(np.float64), 32, axis=-1)
+    want = (codes * d) @ _hadamard(hd).T / hd                         # H (code d) / hd
+    got = c.dequant("v", n)
+    assert np.allclose(got, want, rtol=0, atol=1e-12 * np.abs(want).max())
+    # error bound: the rotated error is at most d/2 per value, and H / sqrt(hd) is
+    # orthonormal, so |V - x|_2 <= sqrt(sum of (d/2)^2 over the row) / sqrt(hd) * sqrt(hd)
+    xr = np.transpose(xv, (1, 0, 2)).astype(np.float64)
+    row_err = np.sqrt(((got - xr) ** 2).sum(-1))
+    bound = np.sqrt(((d / 2 * (1 + 2.0 ** -7)) ** 2).sum(-1)) / np.sqrt(hd)
+    assert (row_err <= bound).all()
+    assert row_err.max() > 0
+    # K is stored exactly as in the int8 format
+    assert c.k.dtype == np.int8 and c.k_scale.shape == (kvh, cap, hd // 64)
+
+
+def pin_k8v4_compact(compact, Cache, FMT_K8V4):
+    kvh, hd, cap = 1, 128, 64
+    H = _hadamard(hd)
+    r = np.random.default_rng(85)
+    # dyadic rows: y integer with block maxima 7 * 2^k, x = H y / 128 exactly; then the
+    # rotated row is y, d = 2^k, code = y / 2^k, and the compacted V is fp16(x)
+    y = r.integers(-7, 8, size=(6, hd)).astype(np.float64)
+    y[:, 0::32] = 7
+    y *= np.repeat(np.exp2(r.integers(-3, 3, size=(6, hd // 32))), 32, axis=-1)
+    x = (y @ H.T) / hd
+    xv = x.astype(np.float32)[:, None, :]
+    assert np.array_equal(xv[:, 0].astype(np.float64), x)
+    c = Cache(FMT_K8V4, kvh, cap, hd)
+    assert c.append(0, xv, xv)
+    _, v16 = compact(c, 6)
+    assert np.array_equal(v16[0].astype(np.float64), np.vectorize(lambda t: float(f16(Fraction(t))))(x))
+    # random rows: fp16 of the fraction butterflies of code * d, times 2^-7
+    xr = r.standard_normal((5, 1, hd), dtype=np.float32)
+    c = Cache(FMT_K8V4, kvh, cap, hd)
+    assert c.append(0, xr, xr)
+    _, v16 = compact(c, 5)
+    u = c.v_rotated(5)[0]
+    for t in range(5):
+        want = [f16(v / hd) for v in fwht_f32_exact(u[t].astype(np.float32))]
+        assert [Fraction(float(v)) for v in v16[0, t]] == want, t
+
+
+def pin_cache_bytes_k8v4(cache_bytes, FMT_K8V4):
+    gold = _load("k8v4_pages.json")
+    # any kvh * hd = 512 (e.g. 2 heads of 256): K codes + K scales + V nibbles + V scales
+    for kvh, hd in ((2, 256), (4, 128)):
+        per_cell = sum(cache_bytes(FMT_K8V4, kvh, 1, hd, p) for p in range(4))
+        assert per_cell == gold["bytes_per_cell"], (kvh, hd, per_cell)
+    assert cache_bytes(FMT_K8V4, 8, 1, 128, 2) == 8 * 64
+    assert cache_bytes(FMT_K8V4, 8, 1, 128, 3) == 8 * 4 * 2

@@ -237,3 +237,99 @@ def test_compaction_mutants_caught():
         assert _fails(pins.pin_compact_exact, m, oracle.Cache, oracle.FMT_F16, oracle.FMT_Q8), \
             m.__name__
     assert math.isfinite(1.0)
+
+
+# ----------------------------------------------------------------------------
+# K8V4 mutants: rotation, 4-bit quantiser, nibble layout, read-back, bytes
+# ----------------------------------------------------------------------------
+from oracle import kvq8_oracle as _o  # noqa: E402
+
+
+def _fwht_template(x, sign="ab", stages=None):
+    y = np.array(x, dtype=np.float32, copy=True)
+    n = y.shape[-1]
+    lead = y.shape[:-1]
+    h, k = 1, 0
+    while h < n and (stages is None or k < stages):
+        z = y.reshape(*lead, n // (2 * h), 2, h)
+        a, b = z[..., 0, :], z[..., 1, :]
+        y = np.stack([a + b, a - b if sign == "ab" else b - a], axis=-2).reshape(*lead, n)
+        h *= 2
+        k += 1
+    return y
+
+
+@pytest.mark.parametrize("kw", [dict(sign="ba"), dict(stages=6)])
+def test_fwht_mutant_is_caught(kw):
+    assert _fails(pins.pin_fwht, lambda x: _fwht_template(x, **kw)), kw
+
+
+def test_unmutated_fwht_template_passes():
+    pins.pin_fwht(_fwht_template)
+
+
+def _q4_template(w, divisor=7.0, lo=-7, hi=7, rounding="rint"):
+    w = np.asarray(w, np.float32)
+    g = w.reshape(*w.shape[:-1], w.shape[-1] // 32, 32)
+    d16 = (np.abs(g).max(-1) / np.float32(divisor)).astype(np.float16)
+    d32 = d16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(d32 == 0, np.float32(0), g / d32)
+    q = np.rint(r) if rounding == "rint" else np.trunc(r)
+    return np.clip(q, lo, hi).astype(np.int8).reshape(w.shape), d16
+
+
+Q4_MUTANTS = {"divide by 8": dict(divisor=8.0), "clamp to -8": dict(lo=-8),
+              "truncate": dict(rounding="trunc")}
+
+
+@pytest.mark.parametrize("name", list(Q4_MUTANTS))
+def test_q4_mutant_is_caught(name):
+    mutant = lambda w: _q4_template(w, **Q4_MUTANTS[name])  # noqa: E731
+    caught = [p.__name__ for p in (pins.pin_q4_worked_examples, pins.pin_q4_brute_force,
+                                   pins.pin_q4_invariants) if _fails(p, mutant)]
+    assert caught, name
+
+
+def test_unmutated_q4_template_passes():
+    for p in (pins.pin_q4_worked_examples, pins.pin_q4_brute_force, pins.pin_q4_invariants):
+        p(_q4_template)
+
+
+def test_nibble_order_mutant_is_caught():
+    def pack_high_first(c):
+        u = (np.asarray(c, np.int16) + 8).astype(np.uint8)
+        return ((u[..., 0::2] << 4) | u[..., 1::2]).astype(np.uint8)
+
+    def unpack_high_first(b):
+        out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), np.int8)
+        out[..., 0::2] = (b >> 4).astype(np.int8) - 8
+        out[..., 1::2] = (b & 0x0F).astype(np.int8) - 8
+        return out
+
+    assert _fails(pins.pin_nibbles, pack_high_first, unpack_high_first)
+
+
+def test_k8v4_read_mutants_caught():
+    class NoInverseScale(oracle.Cache):      # forgets the 1/HD of the inverse rotation
+        def dequant(self, which, length):
+            out = super().dequant(which, length)
+            return out * self.hd if which == "v" and self.fmt == _o.FMT_K8V4 else out
+
+    class NotRotatedBack(oracle.Cache):      # returns the rotated V as if it were V
+        def dequant(self, which, length):
+            if which == "v" and self.fmt == _o.FMT_K8V4:
+                return self.v_rotated(length)
+            return super().dequant(which, length)
+
+    for m in (NoInverseScale, NotRotatedBack):
+        assert _fails(pins.pin_k8v4_read, m, _o.FMT_K8V4, _o.unpack_nibbles), m.__name__
+
+
+def test_k8v4_bytes_mutant_caught():
+    def v_scales_per_64(fmt, kvh, cap, hd, part):
+        if fmt == _o.FMT_K8V4 and part == 3:
+            return 2 * (kvh * cap * hd // 64)
+        return oracle.cache_bytes(fmt, kvh, cap, hd, part)
+
+    assert _fails(pins.pin_cache_bytes_k8v4, v_scales_per_64, _o.FMT_K8V4)
