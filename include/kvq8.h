@@ -31,12 +31,13 @@ extern "C" {
 #endif
 
 /* Cache formats [P1, Summary]: FP16 values, or int8 codes with one FP16 scale per
- * 64 dims.  An explicit enum, checked against which scale pointers are present,
- * rather than inferring the format from pointer presence (the silent-skip trap
- * described in [P3, How]). */
-typedef enum { KV_FMT_F16 = 0, KV_FMT_Q8 = 1 } kv_fmt;
+ * 64 dims; and [P3, What]'s K8V4: the int8 K with a rotated 4-bit V.  An explicit
+ * enum, checked against which scale pointers are present, rather than inferring the
+ * format from pointer presence (the silent-skip trap described in [P3, How]). */
+typedef enum { KV_FMT_F16 = 0, KV_FMT_Q8 = 1, KV_FMT_K8V4 = 2 } kv_fmt;
 
-#define KV_GROUP 64 /* dims per FP16 scale [P1, Summary] */
+#define KV_GROUP 64    /* dims per FP16 scale of the int8 codes [P1, Summary] */
+#define KV_Q4_BLOCK 32 /* values per FP16 scale of the K8V4 V codes [P3, What] */
 
 typedef struct {
   int32_t fmt;        /* kv_fmt */
@@ -51,6 +52,13 @@ typedef struct {
  *        k_scale, v_scale = fp16 bits, [n_kv_heads][cap][head_dim / 64]; scale g of
  *        a row covers dims [64g, 64g + 64).  Codes and scales are separate arrays
  *        ([P1, What changed]; separate byte runs in [P3, How]).
+ *   K8V4: k, k_scale as Q8.  v = uint8 [n_kv_heads][cap][head_dim / 2]: the V row
+ *        rotated, w = H x (H the 128 x 128 Sylvester Hadamard matrix, applied as fp32
+ *        butterflies, stages 1, 2, 4, ..., 64), quantised per 32 values as
+ *        d = fp16(max|w| / 7), code = clamp(rint(w / d), -7, 7), stored as code + 8,
+ *        byte j holding value 2j in its low nibble and 2j + 1 in its high nibble;
+ *        v_scale = fp16 bits [n_kv_heads][cap][head_dim / 32].  A read sees
+ *        V = H (code * d) / 128: the orthonormal rotation H / sqrt(128), undone.
  * All four pointers 16-byte aligned; cap a multiple of 64 and at most 2^24 (a head's
  * rows are addressed with 32-bit byte offsets).  An array of these
  * lives in device memory for the batched calls. */
@@ -81,10 +89,11 @@ enum {
                             the format, or cap not a positive multiple of 64 or above 2^24 */
 };
 
-/* Bytes of one K (or one V) array of one layer: part 0 the values/codes, part 1
- * the scales (0 for F16).  Per value: 2 B (F16), or 1 B + 2 B per 64 (Q8), which
- * reproduces the 6.0 / 3.1 GiB at 262144 cells of [P1, Summary].  Returns 0 for
- * invalid arguments. */
+/* Bytes of one array of one layer: part 0 the K values/codes, part 1 the K scales
+ * (0 for F16), parts 2 and 3 the same for V.  Per value: 2 B (F16), or 1 B + 2 B
+ * per 64 (Q8, and the K8V4 K), which reproduces the 6.0 / 3.1 GiB at 262144 cells of
+ * [P1, Summary]; the K8V4 V: 1/2 B + 2 B per 32, so a K8V4 cell of 512 values per
+ * array takes the 816 B of [P3, What].  Returns 0 for invalid arguments. */
 size_t kv_cache_bytes(int fmt, int n_kv_heads, int cap, int head_dim, int part);
 
 /* Write n_tok new cells per session: quantise-on-write (Q8) or FP16 store (F16).

@@ -18,8 +18,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq8.so")
 
-KV_FMT_F16, KV_FMT_Q8 = 0, 1
+KV_FMT_F16, KV_FMT_Q8, KV_FMT_K8V4 = 0, 1, 2
 KV_GROUP = 64
+KV_Q4_BLOCK = 32
 KV_OK, KV_ERR_ARG, KV_ERR_FMT, KV_ERR_ALIGN, KV_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
 KV_ERR_WORKSPACE, KV_ERR_RANGE, KV_ERR_HIP = -5, -6, -7
 KV_DEV_RANGE, KV_DEV_BAD_SESSION = 1, 2
@@ -119,7 +120,9 @@ class Session:
     """One session's cache arrays for one layer, allocated with torch.
 
     F16: k, v int16 tensors holding fp16 bits [kvh][cap][hd]; Q8: k, v int8 codes
-    [kvh][cap][hd] and k_scale, v_scale int16 (fp16 bits) [kvh][cap][hd/64]."""
+    [kvh][cap][hd] and k_scale, v_scale int16 (fp16 bits) [kvh][cap][hd/64];
+    K8V4: k, k_scale as Q8, v uint8 nibble pairs [kvh][cap][hd/2] and v_scale int16
+    (fp16 bits) [kvh][cap][hd/32]."""
 
     def __init__(self, fmt: int, n_kv_heads: int, cap: int, head_dim: int = 128,
                  device="cuda", fill: int | None = None):
@@ -129,6 +132,13 @@ class Session:
             self.k = torch.empty(shp, dtype=torch.int16, device=device)
             self.v = torch.empty(shp, dtype=torch.int16, device=device)
             self.k_scale = self.v_scale = None
+        elif fmt == KV_FMT_K8V4:
+            self.k = torch.empty(shp, dtype=torch.int8, device=device)
+            self.v = torch.empty((n_kv_heads, cap, head_dim // 2), dtype=torch.uint8, device=device)
+            self.k_scale = torch.empty((n_kv_heads, cap, head_dim // KV_GROUP), dtype=torch.int16,
+                                       device=device)
+            self.v_scale = torch.empty((n_kv_heads, cap, head_dim // KV_Q4_BLOCK), dtype=torch.int16,
+                                       device=device)
         else:
             self.k = torch.empty(shp, dtype=torch.int8, device=device)
             self.v = torch.empty(shp, dtype=torch.int8, device=device)

@@ -13,7 +13,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0;
 
 int check_shape(const kv_shape* s) {
   if (s == nullptr) return KV_ERR_ARG;
-  if (s->fmt != KV_FMT_F16 && s->fmt != KV_FMT_Q8) return KV_ERR_FMT;
+  if (s->fmt != KV_FMT_F16 && s->fmt != KV_FMT_Q8 && s->fmt != KV_FMT_K8V4) return KV_ERR_FMT;
   if (s->n_kv_heads < 1 || s->n_kv_heads > KV_MAX_KV_HEADS || s->n_q_heads < 1 ||
       s->n_q_heads % s->n_kv_heads != 0)
     return KV_ERR_ARG;
@@ -26,7 +26,7 @@ int check_shape(const kv_shape* s) {
 // host copy of one session entry (prefill / compaction take one on the host)
 int check_session(const kv_shape* s, const kv_session* e) {
   if (e == nullptr || e->k == nullptr || e->v == nullptr) return KV_ERR_ARG;
-  if (s->fmt == KV_FMT_Q8) {
+  if (s->fmt != KV_FMT_F16) {
     if (e->k_scale == nullptr || e->v_scale == nullptr) return KV_ERR_FMT;
   } else if (e->k_scale != nullptr || e->v_scale != nullptr) {
     return KV_ERR_FMT;
@@ -45,11 +45,12 @@ int hip_status(hipError_t e) { return e == hipSuccess ? KV_OK : KV_ERR_HIP; }
 extern "C" {
 
 size_t kv_cache_bytes(int fmt, int n_kv_heads, int cap, int head_dim, int part) {
-  if ((fmt != KV_FMT_F16 && fmt != KV_FMT_Q8) || n_kv_heads < 0 || cap < 0 || head_dim <= 0 ||
-      head_dim % KV_GROUP != 0 || (part != 0 && part != 1))
+  if ((fmt != KV_FMT_F16 && fmt != KV_FMT_Q8 && fmt != KV_FMT_K8V4) || n_kv_heads < 0 ||
+      cap < 0 || head_dim <= 0 || head_dim % KV_GROUP != 0 || part < 0 || part > 3)
     return 0;
   const size_t n = (size_t)n_kv_heads * (size_t)cap * (size_t)head_dim;
-  if (part == 0) return fmt == KV_FMT_F16 ? 2 * n : n;
+  if (fmt == KV_FMT_K8V4 && part >= 2) return part == 2 ? n / 2 : 2 * (n / KV_Q4_BLOCK);
+  if ((part & 1) == 0) return fmt == KV_FMT_F16 ? 2 * n : n;
   return fmt == KV_FMT_F16 ? 0 : 2 * (n / KV_GROUP);
 }
 
@@ -136,10 +137,10 @@ int kv_prefill_attn(const kv_shape* h_shape, const kv_session* h_sess, int pos0,
   const int kvh = h_shape->n_kv_heads;
   const uint16_t *k16, *v16;
   long row_stride;  // rows between kv heads
-  if (h_shape->fmt == KV_FMT_Q8) {
+  if (h_shape->fmt != KV_FMT_F16) {
     uint16_t* wk = static_cast<uint16_t*>(d_ws);
     uint16_t* wv = reinterpret_cast<uint16_t*>(static_cast<char*>(d_ws) + need / 2);
-    rc = hip_status(launch_compact(KV_FMT_Q8, kvh, *h_sess, P, wk, wv, st));
+    rc = hip_status(launch_compact(h_shape->fmt, kvh, *h_sess, P, wk, wv, st));
     if (rc) return rc;
     k16 = wk;
     v16 = wv;

@@ -15,6 +15,17 @@
 // ROW_PAIRS steps of loads in flight; a block covers 16 tokens of one head of K or
 // of V of one session.  Inputs are read and cache rows written with non-temporal
 // accesses (each byte is touched once).
+//
+// K8V4 (PR #711 "kv: --kv k8v4 streams with --kv-resident", section What: INT8 K and
+// a rotated 4-bit V): K takes the int8 path above.  A V row is rotated, w = H x with
+// H the Sylvester Hadamard matrix, by fp32 butterflies (stage h pairs dims i and i + h
+// inside blocks of 2h, giving a + b and a - b; h = 1, 2, ..., 64), then quantised per
+// 32 values: d = fp16(max|w| / 7), code = clamp(rint(w / d), -7, 7), stored as
+// code + 8 in nibbles (byte j: value 2j low, 2j + 1 high).  Here 16 lanes hold a row,
+// 8 dims each: stages 1, 2, 4 stay in a lane, stages 8 .. 64 pair lanes 1, 2, 4, 8
+// apart; each output is one fp32 addition or subtraction of the same two operands as
+// in the definition, so the result is bit-identical to it.  A 32-value block is 4
+// lanes (a quad): its max is two DPP steps.
 #include "kvq8_internal.h"
 
 namespace kvq8 {
@@ -23,6 +34,69 @@ namespace {
 constexpr int APPEND_THREADS = 256;
 constexpr int ROW_PAIRS = 2;                                      // row pairs per wave
 constexpr int TOK_PER_BLOCK = (APPEND_THREADS / 64) * ROW_PAIRS * 2;  // 16
+static_assert(TOK_PER_BLOCK == (APPEND_THREADS / 64) * 4, "the K8V4 V path: 4 rows per wave");
+
+// K8V4 V rows [len + t] of head h: 16 lanes per row, 4 rows per wave (TOK_PER_BLOCK
+// rows per block, the same tokens the other paths cover)
+__device__ __forceinline__ void append_v_rot4(const kv_session& s, int len, int n_tok, int kvh,
+                                              int h, int b, const float* __restrict__ xv) {
+  const int lane = threadIdx.x & 63;
+  const int l = lane & 15;   // dims 8l .. 8l + 7 of the row
+  const int t = blockIdx.x * TOK_PER_BLOCK + (threadIdx.x >> 6) * 4 + (lane >> 4);
+  float x[8];
+  if (t < n_tok) {
+    const float* src = xv + (((size_t)b * n_tok + t) * kvh + h) * HD + 8 * l;
+    const u32x4 p = ldg128_nt(src), q = ldg128_nt(src + 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = as_f32(p[j]);
+      x[4 + j] = as_f32(q[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = 0.f;
+  }
+  // stages 1, 2, 4: pairs inside the lane's 8 dims
+#pragma unroll
+  for (int hh = 1; hh < 8; hh *= 2)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if ((j & hh) == 0) {
+        const float a = x[j], c = x[j + hh];
+        x[j] = a + c;
+        x[j + hh] = a - c;
+      }
+  // stages 8 .. 64: the partner dim is in lane l ^ m; the lower lane keeps a + b,
+  // the upper one a - b (a the lower dim's value)
+#pragma unroll
+  for (int m = 1; m < 16; m *= 2)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = __shfl_xor(x[j], m, 64);
+      x[j] = (l & m) ? p - x[j] : x[j] + p;
+    }
+  // 4-bit codes per 32 dims (a quad of lanes)
+  float a = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(x[j]));
+  a = fmaxf(a, dpp<DPP_QUAD_XOR1>(a));
+  a = fmaxf(a, dpp<DPP_QUAD_XOR2>(a));
+  const uint16_t dbits = f2h(a / 7.0f);   // IEEE fp32 division, then RNE to fp16
+  const float d = h2f(dbits);
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float r = d == 0.0f ? 0.0f : rintf(x[j] / d);   // IEEE fp32 division
+    const uint32_t nib = (uint32_t)((int)fminf(fmaxf(r, -7.0f), 7.0f) + 8);
+    word |= nib << (4 * j);   // dim 8l + j: byte j / 2, low nibble for even j
+  }
+  if (t < n_tok) {
+    const size_t row = (size_t)h * s.cap + len + t;
+    uint8_t* dst = static_cast<uint8_t*>(s.v) + row * (HD / 2) + 4 * l;
+    __builtin_nontemporal_store(word, (KVQ8_GLOBAL uint32_t*)dst);
+    if ((l & 3) == 0) stg16(s.v_scale + row * NQ4 + (l >> 2), dbits);
+  }
+}
 
 // Grid: x = blocks of TOK_PER_BLOCK tokens, y = (K or V, kv head), z = session.  Every
 // index comes from the block coordinates; a block writes the rows [len + t] of one
@@ -41,6 +115,12 @@ __global__ __launch_bounds__(APPEND_THREADS) void k_append(
   if (bad) {   // the whole session is skipped; one thread of the session reports it
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) flag(status, bad);
     return;
+  }
+  if constexpr (FMT == KV_FMT_K8V4) {
+    if (which) {
+      append_v_rot4(s, len, n_tok, kvh, h, b, xv);
+      return;
+    }
   }
   const int lane = threadIdx.x & 63;
   const int half = lane >> 5;   // which row of the pair
@@ -68,7 +148,7 @@ __global__ __launch_bounds__(APPEND_THREADS) void k_append(
     const int t = t0 + 2 * p + half;
     const bool store = t < n_tok;
     const size_t row = drow0 + t;
-    if constexpr (FMT == KV_FMT_Q8) {
+    if constexpr (FMT != KV_FMT_F16) {   // int8: the Q8 arrays, and the K8V4 K
       float a = fmaxf(fmaxf(fabsf(x[p].x), fabsf(x[p].y)), fmaxf(fabsf(x[p].z), fabsf(x[p].w)));
       a = max16(a);                                  // group max: all 16 lanes of the group
       const uint16_t sbits = f2h(a / 127.0f);        // IEEE fp32 division, then RNE to fp16
@@ -109,6 +189,9 @@ hipError_t launch_append(int fmt, int kvh, const kv_session* d_tab, const int32_
   dim3 grid((unsigned)bx, 2 * kvh, n_sess), block(APPEND_THREADS);
   if (fmt == KV_FMT_Q8)
     hipLaunchKernelGGL(k_append<KV_FMT_Q8>, grid, block, 0, st, d_tab, d_len, n_tok, kvh, d_k,
+                       d_v, d_status);
+  else if (fmt == KV_FMT_K8V4)
+    hipLaunchKernelGGL(k_append<KV_FMT_K8V4>, grid, block, 0, st, d_tab, d_len, n_tok, kvh, d_k,
                        d_v, d_status);
   else
     hipLaunchKernelGGL(k_append<KV_FMT_F16>, grid, block, 0, st, d_tab, d_len, n_tok, kvh, d_k,

@@ -64,6 +64,10 @@ __device__ __forceinline__ u32x4 ldkv(const void* p) {
 }
 // base: the head's first row (the same for the whole wave); off: 32-bit byte offset
 __device__ __forceinline__ u32x4 ldkv(const char* base, uint32_t off) { return ldkv(base + off); }
+__device__ __forceinline__ u32x2 ldkv64(const char* base, uint32_t off) {
+  if constexpr (KVQ8_DEC_NT) return __builtin_nontemporal_load((const KVQ8_GLOBAL u32x2*)(base + off));
+  return *(const KVQ8_GLOBAL u32x2*)(base + off);
+}
 
 #ifndef KVQ8_DEC_WG_WAVES
 #define KVQ8_DEC_WG_WAVES 8
@@ -87,7 +91,7 @@ constexpr int GRP_WAVES = DEC_WAVES >= 8 ? DEC_WAVES / 2 : DEC_WAVES;
 constexpr bool GROUPED = GRP_WAVES != DEC_WAVES;
 template <int FMT>
 __host__ __device__ constexpr int lead16() {
-  return GROUPED ? (FMT == KV_FMT_Q8 ? KVQ8_DEC_LEAD16_Q8 : KVQ8_DEC_LEAD16_F16) : 16;
+  return GROUPED ? (FMT != KV_FMT_F16 ? KVQ8_DEC_LEAD16_Q8 : KVQ8_DEC_LEAD16_F16) : 16;
 }
 template <int FMT>
 __host__ __device__ constexpr int lead_steps(int J) {  // >= J - lead_steps(J) (lead16 >= 8)
@@ -130,6 +134,27 @@ struct Chunk<KV_FMT_Q8> {
   }
 };
 
+// K8V4: the K chunk is the int8 one; a V chunk is 16 nibbles (8 bytes: w[0], w[1])
+// of the rotated row, read as code + 8 (the 8 is taken out by the caller)
+template <>
+struct Chunk<KV_FMT_K8V4> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const char* base, uint32_t row, int c) {
+    w = ldkv(base, row * HD + c * 16);
+  }
+  __device__ __forceinline__ void load_v(const char* base, uint32_t row, int c) {
+    const u32x2 t = ldkv64(base, row * (HD / 2) + c * 8);
+    w[0] = t[0];
+    w[1] = t[1];
+  }
+  __device__ __forceinline__ float get(int i) const {  // int8 K code
+    return (float)(int8_t)(w[i >> 2] >> (8 * (i & 3)));
+  }
+  __device__ __forceinline__ float get_v(int i) const {  // V nibble, code + 8
+    return (float)((w[i >> 3] >> (4 * (i & 7))) & 15u);
+  }
+};
+
 template <>
 struct Chunk<KV_FMT_F16> {
   u32x4 a, b;  // 16 fp16 values: dims [8c, 8c+8) and [64+8c, 64+8c+8)
@@ -148,7 +173,7 @@ struct Chunk<KV_FMT_F16> {
 // Head dim of the i-th of the 16 values a lane (c = lane % 8) holds of a row.
 template <int FMT>
 __device__ __forceinline__ int lane_dim(int c, int i) {
-  if constexpr (FMT == KV_FMT_Q8) return 16 * c + i;  // one 64-dim scale group per lane
+  if constexpr (FMT != KV_FMT_F16) return 16 * c + i;  // one 64-dim scale group per lane
   return i < 8 ? 8 * c + i : 64 + 8 * c + (i - 8);
 }
 
@@ -193,17 +218,24 @@ struct Batch {
   // steps k .. k+U-1 of wave gw; tokens past len re-read the last cell (in bounds)
   // and are masked by the callers
   // vals, scales: the head's first row of values and of scales
+  // V: the V array (only K8V4 lays it out differently from K)
+  template <bool V>
   __device__ __forceinline__ void load(const char* vals, const char* scales, int gw, int W, int k,
                                        int len, int r, int c) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t row = (uint32_t)min((gw + (k + u) * W) * 8 + r, len - 1);
-      ch[u].load(vals, row, c);
-      if constexpr (FMT == KV_FMT_Q8) sc[u] = ldg16(scales + (row * NGRP + (c >> 2)) * 2);
+      if constexpr (FMT == KV_FMT_K8V4 && V) {
+        ch[u].load_v(vals, row, c);
+        sc[u] = ldg16(scales + (row * NQ4 + (c >> 1)) * 2);   // lane c: dims of block c / 2
+      } else {
+        ch[u].load(vals, row, c);
+        if constexpr (FMT != KV_FMT_F16) sc[u] = ldg16(scales + (row * NGRP + (c >> 2)) * 2);
+      }
     }
   }
   __device__ __forceinline__ float scale(int u) const {
-    if constexpr (FMT == KV_FMT_Q8) return h2f(sc[u]);
+    if constexpr (FMT != KV_FMT_F16) return h2f(sc[u]);
     return 1.f;
   }
 };
@@ -290,14 +322,18 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
   constexpr int EB = FMT == KV_FMT_F16 ? 2 : 1;   // bytes per value
   const size_t hrow = (size_t)h * (size_t)ss.cap;  // the head's first row
   const char* kb = static_cast<const char*>(ss.k) + hrow * HD * EB;
-  const char* vb = static_cast<const char*>(ss.v) + hrow * HD * EB;
+  constexpr int VB = FMT == KV_FMT_K8V4 ? HD / 2 : HD * EB;   // bytes per V row
+  constexpr int VSC = FMT == KV_FMT_K8V4 ? NQ4 : NGRP;          // V scales per row
+  const char* vb = static_cast<const char*>(ss.v) + hrow * VB;
   const char* ksb = reinterpret_cast<const char*>(ss.k_scale) + hrow * NGRP * 2;
-  const char* vsb = reinterpret_cast<const char*>(ss.v_scale) + hrow * NGRP * 2;
+  const char* vsb = reinterpret_cast<const char*>(ss.v_scale) + hrow * VSC * 2;
   float m[G], l[G], acc[G][16];
+  float accw[G];  // K8V4: the V-pass weights summed (takes the + 8 of the nibbles out)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.f;
+    accw[g] = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
   }
@@ -341,7 +377,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
       constexpr int N1 = G > 1 ? G / 2 : 1, N2 = N1 > 1 ? N1 / 2 : 1, N3 = N2 > 1 ? N2 / 2 : 1;
       fold_stage<DPP_QUAD_XOR1, U, G, G>(part);
       fold_stage<DPP_QUAD_XOR2, U, G, N1>(part);
-      if constexpr (FMT == KV_FMT_Q8) {  // lanes c .. c^3 share a scale group
+      if constexpr (FMT != KV_FMT_F16) {  // lanes c .. c^3 share a scale group
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const float sc = cur.scale(u);
@@ -370,11 +406,22 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
         load_p<G>(lg + (it * 8 + r) * G, w);
 #pragma unroll
         for (int g = 0; g < G; ++g) w[g] *= sc;
+        if constexpr (FMT == KV_FMT_K8V4) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float vf = cur.ch[u].get(i);
+          for (int g = 0; g < G; ++g) accw[g] += w[g];
 #pragma unroll
-          for (int g = 0; g < G; ++g) acc[g][i] = fmaf(w[g], vf, acc[g][i]);
+          for (int i = 0; i < 16; ++i) {
+            const float vf = cur.ch[u].get_v(i);   // code + 8
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g][i] = fmaf(w[g], vf, acc[g][i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float vf = cur.ch[u].get(i);
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g][i] = fmaf(w[g], vf, acc[g][i]);
+          }
         }
       }
     };
@@ -387,15 +434,15 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     // softmax.  The plan gives every wave at most its group's budget (CH0 or CH1) of steps.
     const int n_it = n_steps;
     Batch<FMT, U> A, B;
-    A.load(kb, ksb, gw, W, 0, len, r, c);
+    A.template load<false>(kb, ksb, gw, W, 0, len, r, c);
     // ---- K pass ---------------------------------------------------------------
     for (int it0 = 0; it0 < n_it; it0 += 2 * U) {
-      B.load(kb, ksb, gw, W, it0 + U, len, r, c);
+      B.template load<false>(kb, ksb, gw, W, it0 + U, len, r, c);
       kstep(A, 0, it0, n_it);
       if (it0 + 2 * U < n_it)
-        A.load(kb, ksb, gw, W, it0 + 2 * U, len, r, c);
+        A.template load<false>(kb, ksb, gw, W, it0 + 2 * U, len, r, c);
       else
-        A.load(vb, vsb, gw, W, 0, len, r, c);
+        A.template load<true>(vb, vsb, gw, W, 0, len, r, c);
       kstep(B, 0, it0 + U, n_it);
     }
     wave_lds_fence();
@@ -426,10 +473,16 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     wave_lds_fence();
     // ---- V pass ---------------------------------------------------------------
     for (int it0 = 0; it0 < n_it; it0 += 2 * U) {
-      B.load(vb, vsb, gw, W, it0 + U, len, r, c);
+      B.template load<true>(vb, vsb, gw, W, it0 + U, len, r, c);
       vstep(A, it0, n_it);
-      if (it0 + 2 * U < n_it) A.load(vb, vsb, gw, W, it0 + 2 * U, len, r, c);
+      if (it0 + 2 * U < n_it) A.template load<true>(vb, vsb, gw, W, it0 + 2 * U, len, r, c);
       vstep(B, it0 + U, n_it);
+    }
+    if constexpr (FMT == KV_FMT_K8V4) {  // sum_t w_t (n - 8) = sum_t w_t n - 8 sum_t w_t
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[g][i] = fmaf(-8.f, accw[g], acc[g][i]);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -535,14 +588,28 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void k_decode_merge(
       }
     M = Mn;
   }
-  dst[lane] = make_float2(acc.x / L, acc.y / L);
+  float2 res = make_float2(acc.x / L, acc.y / L);
+  if constexpr (FMT == KV_FMT_K8V4) {
+    // the merged row is in the rotated basis: V = H (code d) / 128, so out = H res / 128.
+    // Lane holds dims 2 lane, 2 lane + 1: stage 1 in the lane, stages 2 .. 64 pair
+    // lanes 1 .. 32 apart (the lower lane keeps a + b, the upper a - b)
+    float u0 = res.x + res.y, u1 = res.x - res.y;
+#pragma unroll
+    for (int mk = 1; mk < 64; mk *= 2) {
+      const float p0 = __shfl_xor(u0, mk, 64), p1 = __shfl_xor(u1, mk, 64);
+      u0 = (lane & mk) ? p0 - u0 : u0 + p0;
+      u1 = (lane & mk) ? p1 - u1 : u1 + p1;
+    }
+    res = make_float2(u0 * 0.0078125f, u1 * 0.0078125f);
+  }
+  dst[lane] = res;
 }
 
 // steps per load batch: int8 takes 4 (its loads are half the size), except with 8
 // query heads, where the batch registers would not fit beside the partials
 template <int FMT, int G>
 constexpr int batch_rows() {
-  return FMT == KV_FMT_Q8 ? (G >= 8 ? 2 : KVQ8_DEC_U_Q8) : KVQ8_DEC_U_F16;
+  return FMT != KV_FMT_F16 ? (G >= 8 ? 2 : KVQ8_DEC_U_Q8) : KVQ8_DEC_U_F16;
 }
 
 // Split workgroups of one kernel instance that fit on the current device at once
@@ -568,6 +635,10 @@ int resident_splits() {
 int resident(int fmt, int G) {
 #define KVQ8_RES(F, GG) \
   if (fmt == F && G == GG) return resident_splits<F, GG>();
+  KVQ8_RES(KV_FMT_K8V4, 1)
+  KVQ8_RES(KV_FMT_K8V4, 2)
+  KVQ8_RES(KV_FMT_K8V4, 4)
+  KVQ8_RES(KV_FMT_K8V4, 8)
   KVQ8_RES(KV_FMT_Q8, 1)
   KVQ8_RES(KV_FMT_Q8, 2)
   KVQ8_RES(KV_FMT_Q8, 4)
@@ -607,7 +678,7 @@ DecodePlan decode_plan(int fmt, int kvh, int nqh, int n_sess, int max_len) {
   // last, partly filled round would leave CUs idle), but not past one split per 4
   // steps (so every workgroup has work).
   const long long J = ((long long)max_len + 7) / 8;
-  const bool q8 = fmt == KV_FMT_Q8;
+  const bool q8 = fmt != KV_FMT_F16;   // the int8 K formats share the q8 plan
   const long long Jf = q8 ? lead_steps<KV_FMT_Q8>((int)J) : lead_steps<KV_FMT_F16>((int)J);
   const long long J1 = J - Jf;
   const int G = nqh / kvh;
@@ -650,6 +721,10 @@ hipError_t launch_decode(int fmt, int kvh, int nqh, const kv_session* d_tab,
   if (fmt == F && G == GG)                                                                       \
     return launch_g<F, GG>(d_tab, d_len, n_sess, max_len, kvh, d_q, sm_scale, d_out, ws_o, ws_lse, \
                            plan, d_status, st);
+  KVQ8_DEC(KV_FMT_K8V4, 1)
+  KVQ8_DEC(KV_FMT_K8V4, 2)
+  KVQ8_DEC(KV_FMT_K8V4, 4)
+  KVQ8_DEC(KV_FMT_K8V4, 8)
   KVQ8_DEC(KV_FMT_Q8, 1)
   KVQ8_DEC(KV_FMT_Q8, 2)
   KVQ8_DEC(KV_FMT_Q8, 4)

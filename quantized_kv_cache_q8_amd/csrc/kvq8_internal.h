@@ -11,6 +11,7 @@ namespace kvq8 {
 
 constexpr int HD = 128;        // head_dim supported by the kernels
 constexpr int NGRP = HD / KV_GROUP;  // fp16 scales per head row (2)
+constexpr int NQ4 = HD / KV_Q4_BLOCK;  // fp16 scales per K8V4 V row (4)
 // most cells per session: a head's rows (<= 256 B each) stay within 32-bit offsets
 constexpr int KV_MAX_CAP = 1 << 24;
 // Most kv heads of a shape (grids put 2 x n_kv_heads on their y extent).
@@ -130,7 +131,7 @@ __device__ __forceinline__ int session_bad(const kv_session& s, int fmt) {
   const uintptr_t sc =
       reinterpret_cast<uintptr_t>(s.k_scale) | reinterpret_cast<uintptr_t>(s.v_scale);
   if (s.k == nullptr || s.v == nullptr || (kv & 15)) return KV_DEV_BAD_SESSION;
-  if (fmt == KV_FMT_Q8) {
+  if (fmt != KV_FMT_F16) {
     if (s.k_scale == nullptr || s.v_scale == nullptr || (sc & 15)) return KV_DEV_BAD_SESSION;
   } else if (sc != 0) {
     return KV_DEV_BAD_SESSION;

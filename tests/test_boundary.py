@@ -42,14 +42,14 @@ def test_struct_layout():
 
 
 def test_cache_bytes_matches_oracle():
-    for fmt in (F16, Q8):
+    for fmt in (F16, Q8, kq.KV_FMT_K8V4):
         for kvh, cap, hd in [(8, 262144, 128), (2, 1024, 128), (3, 64, 256), (1, 0, 64)]:
-            for part in (0, 1):
+            for part in (0, 1, 2, 3):
                 assert kq.kv_cache_bytes(fmt, kvh, cap, hd, part) == \
-                    oracle.cache_bytes(fmt, kvh, cap, hd, part)
-    assert kq.kv_cache_bytes(2, 8, 64, 128, 0) == 0
+                    oracle.cache_bytes(fmt, kvh, cap, hd, part), (fmt, kvh, cap, hd, part)
+    assert kq.kv_cache_bytes(3, 8, 64, 128, 0) == 0          # no such format
     assert kq.kv_cache_bytes(Q8, 8, 64, 100, 0) == 0
-    assert kq.kv_cache_bytes(Q8, 8, 64, 128, 2) == 0
+    assert kq.kv_cache_bytes(Q8, 8, 64, 128, 4) == 0          # no such part
 
 
 def test_status_strings():
@@ -152,6 +152,7 @@ def test_compact_validation():
     assert compact(shape(), None) == kq.KV_ERR_ARG
     assert compact(shape(), sess(k=None)) == kq.KV_ERR_ARG
     assert compact(shape(fmt=Q8), sess(fmt=Q8, ks=None)) == kq.KV_ERR_FMT
+    assert compact(shape(fmt=kq.KV_FMT_K8V4), sess(fmt=Q8, ks=None)) == kq.KV_ERR_FMT  # K8V4 needs scales
     assert compact(shape(fmt=F16), sess(fmt=F16, ks=C, vs=D)) == kq.KV_ERR_FMT   # F16 with scales
     assert compact(shape(fmt=F16), sess(fmt=Q8)) == kq.KV_ERR_FMT
     assert compact(shape(), sess(k=A + 8)) == kq.KV_ERR_ALIGN

@@ -12,7 +12,7 @@ from gpu_util import (DEV, append_bulk, check_close, decode_gpu, oracle_cache, s
                       sm_scale, to_dev)
 
 pytestmark = pytest.mark.gpu
-F16, Q8 = kq.KV_FMT_F16, kq.KV_FMT_Q8
+F16, Q8, K4 = kq.KV_FMT_F16, kq.KV_FMT_Q8, kq.KV_FMT_K8V4
 
 
 def oracle_decode(cache: oracle.Cache, q, length, sm):
@@ -23,7 +23,7 @@ def oracle_decode(cache: oracle.Cache, q, length, sm):
     for h in range(cache.kvh):
         sub = oracle.Cache(cache.fmt, 1, cache.cap, cache.hd)
         sub.k, sub.v = cache.k[h:h + 1], cache.v[h:h + 1]
-        if cache.fmt == Q8:
+        if cache.fmt != F16:
             sub.k_scale, sub.v_scale = cache.k_scale[h:h + 1], cache.v_scale[h:h + 1]
         K = sub.dequant("k", length)
         V = sub.dequant("v", length)
@@ -61,7 +61,7 @@ def test_single_cell_is_exactly_the_value_row(fmt):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("fmt", [F16, Q8, K4])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 def test_every_head_ratio(fmt, G):
     """Each supported query heads per kv head (the K-pass reduction and the logit

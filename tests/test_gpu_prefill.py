@@ -10,7 +10,7 @@ import quantized_kv_cache_q8_amd as kq
 from gpu_util import DEV, append_bulk, check_close, oracle_cache, say, shape, sm_scale, to_dev
 
 pytestmark = pytest.mark.gpu
-F16, Q8 = kq.KV_FMT_F16, kq.KV_FMT_Q8
+F16, Q8, K4 = kq.KV_FMT_F16, kq.KV_FMT_Q8, kq.KV_FMT_K8V4
 
 
 def build(fmt, kvh, P, cap, seed, outliers=True):
@@ -21,7 +21,7 @@ def build(fmt, kvh, P, cap, seed, outliers=True):
     return s, oracle_cache(fmt, kvh, cap, 128, xk, xv)
 
 
-@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("fmt", [F16, Q8, K4])
 @pytest.mark.parametrize("P", [1, 63, 200, 1000])
 def test_compaction_bitexact(fmt, P):
     kvh = 3
@@ -46,7 +46,7 @@ def run_prefill(fmt, s, kvh, nqh, pos0, n_tok, q, sm):
     return out.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("fmt", [F16, Q8])
+@pytest.mark.parametrize("fmt", [F16, Q8, K4])
 @pytest.mark.parametrize("kvh,nqh,pos0,n_tok", [
     (2, 8, 100, 70),      # G=4, ragged chunk and key tail, several key tiles
     (2, 8, 0, 130),       # pure causal prompt from position 0
