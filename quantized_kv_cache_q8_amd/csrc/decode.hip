@@ -150,9 +150,6 @@ struct Chunk<KV_FMT_K8V4> {
   __device__ __forceinline__ float get(int i) const {  // int8 K code
     return (float)(int8_t)(w[i >> 2] >> (8 * (i & 3)));
   }
-  __device__ __forceinline__ float get_v(int i) const {  // V nibble, code + 8
-    return (float)((w[i >> 3] >> (4 * (i & 7))) & 15u);
-  }
 };
 
 template <>
@@ -169,6 +166,15 @@ struct Chunk<KV_FMT_F16> {
     return h2f((uint16_t)(v[j >> 1] >> (16 * (j & 1))));
   }
 };
+
+// x & 0x0F0F0F0F: the low nibble of each byte, in its byte.  Kept opaque to the
+// compiler, which would otherwise fold the mask into a 4-bit field extract per value
+// instead of one byte-to-float conversion (v_cvt_f32_ubyteN) per value.
+__device__ __forceinline__ uint32_t nibble_bytes(uint32_t x) {
+  uint32_t r;
+  asm("v_and_b32_e32 %0, 0x0f0f0f0f, %1" : "=v"(r) : "v"(x));
+  return r;
+}
 
 // Head dim of the i-th of the 16 values a lane (c = lane % 8) holds of a row.
 template <int FMT>
@@ -409,9 +415,15 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
         if constexpr (FMT == KV_FMT_K8V4) {
 #pragma unroll
           for (int g = 0; g < G; ++g) accw[g] += w[g];
+          // even and odd nibbles of each word moved into byte lanes: each value is
+          // then one byte-to-float conversion
+          const u32x4& cw = cur.ch[u].w;
+          const uint32_t nb[4] = {nibble_bytes(cw[0]), nibble_bytes(cw[0] >> 4),
+                                  nibble_bytes(cw[1]), nibble_bytes(cw[1] >> 4)};
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float vf = cur.ch[u].get_v(i);   // code + 8
+            const uint32_t src = nb[2 * (i >> 3) + (i & 1)];
+            const float vf = (float)((src >> (8 * ((i & 7) >> 1))) & 0xFFu);   // code + 8
 #pragma unroll
             for (int g = 0; g < G; ++g) acc[g][i] = fmaf(w[g], vf, acc[g][i]);
           }
