@@ -159,6 +159,32 @@ int kv_prefill_attn(const kv_shape* h_shape, const kv_session* h_sess, int pos0,
                     const float* d_q, float sm_scale, float* d_out, void* d_ws, size_t ws_bytes,
                     void* stream);
 
+/* Moving a session's rows, sized by the format ([P1, What changed]: the
+ * session-to-slot copy is sized in the format's elements, with a second copy for the
+ * scales under q8; [P2, Phased plan]: gather to the host and scatter back, the scales
+ * beside the KV body).  A packed block of n_rows rows holds, for each array of the
+ * format in the order K values, K scales, V values, V scales (absent arrays take no
+ * bytes), [n_kv_heads][n_rows][row bytes of that array]: F16 256 / - / 256 / -,
+ * Q8 128 / 4 / 128 / 4, K8V4 128 / 4 / 64 / 8 bytes per row of one head.
+ * kv_rows_bytes: the size of such a block; 0 on invalid arguments. */
+size_t kv_rows_bytes(const kv_shape* h_shape, int n_rows);
+
+/* Device copy of rows [src_row0, src_row0 + n_rows) of every kv head of h_src into rows
+ * [dst_row0, dst_row0 + n_rows) of h_dst (host structs holding device pointers), every
+ * array of the format.  The two row ranges must not overlap when h_src and h_dst share
+ * arrays.  KV_ERR_RANGE if a range leaves its session's capacity; n_rows == 0 is a no-op. */
+int kv_copy_rows(const kv_shape* h_shape, const kv_session* h_src, int src_row0,
+                 const kv_session* h_dst, int dst_row0, int n_rows, void* stream);
+
+/* Gather rows [row0, row0 + n_rows) of a session into the packed block at d_or_h_dst
+ * (device memory, or host memory allocated pinned, kv_rows_bytes(h_shape, n_rows)
+ * bytes), and scatter such a block back into rows [row0, row0 + n_rows).  Asynchronous
+ * on the stream; a host buffer must stay valid until the stream reaches the call. */
+int kv_gather_rows(const kv_shape* h_shape, const kv_session* h_sess, int row0, int n_rows,
+                   void* d_or_h_dst, void* stream);
+int kv_scatter_rows(const kv_shape* h_shape, const kv_session* h_sess, int row0, int n_rows,
+                    const void* d_or_h_src, void* stream);
+
 /* Static text for a KV_* status code. */
 const char* kv_status_str(int status);
 

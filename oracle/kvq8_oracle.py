@@ -230,6 +230,38 @@ class Cache:
 
 
 # ----------------------------------------------------------------------------
+# Moving a session's rows: the packed block of [P1, What changed] (the session-to-slot
+# copy sized in the format's elements, with the scales) and [P2, Phased plan]
+# (gather to the host, scatter back, the scales beside the KV body)
+# ----------------------------------------------------------------------------
+ROW_ARRAYS = ("k", "k_scale", "v", "v_scale")
+
+
+def pack_rows(cache: Cache, row0: int, n: int) -> np.ndarray:
+    """uint8: for each array of the format in the order K values, K scales, V values,
+    V scales (absent arrays skipped), its rows [row0, row0 + n) of every head as
+    [kvh][n][row bytes]."""
+    parts = [np.ascontiguousarray(getattr(cache, a)[:, row0:row0 + n]).view(np.uint8).reshape(-1)
+             for a in ROW_ARRAYS if getattr(cache, a) is not None]
+    return np.concatenate(parts) if parts else np.zeros(0, np.uint8)
+
+
+def unpack_rows(cache: Cache, row0: int, n: int, buf: np.ndarray) -> None:
+    """The inverse of pack_rows: write a packed block into rows [row0, row0 + n)."""
+    buf = np.asarray(buf, np.uint8)
+    off = 0
+    for a in ROW_ARRAYS:
+        arr = getattr(cache, a)
+        if arr is None:
+            continue
+        dst = arr[:, row0:row0 + n]
+        nb = dst.nbytes
+        dst[...] = buf[off:off + nb].view(arr.dtype).reshape(dst.shape)
+        off += nb
+    assert off == buf.size
+
+
+# ----------------------------------------------------------------------------
 # O4: compaction to the FP16 [kvh][P][HD] copy the prompt GEMMs read
 # ----------------------------------------------------------------------------
 def hadamard_f64(n: int) -> np.ndarray:

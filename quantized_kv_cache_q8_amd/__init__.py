@@ -27,7 +27,8 @@ KV_DEV_RANGE, KV_DEV_BAD_SESSION = 1, 2
 
 EXPORTED = ["kv_cache_bytes", "kv_append", "kv_decode_workspace_bytes", "kv_decode_attn",
             "kv_compact_f16", "kv_prefill_workspace_bytes", "kv_prefill_attn", "kv_status_str",
-            "kv_probe_stream_read"]
+            "kv_probe_stream_read", "kv_rows_bytes", "kv_copy_rows", "kv_gather_rows",
+            "kv_scatter_rows"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run quantized_kv_cache_q8_amd.build.build() "
@@ -62,6 +63,11 @@ _sig = {
                              ctypes.c_float, _P, _P, _SZ, _P]),
     "kv_status_str": (ctypes.c_char_p, [_I]),
     "kv_probe_stream_read": (_I, [_P, _SZ, _P, _P]),
+    "kv_rows_bytes": (_SZ, [ctypes.POINTER(kv_shape), _I]),
+    "kv_copy_rows": (_I, [ctypes.POINTER(kv_shape), ctypes.POINTER(kv_session), _I,
+                          ctypes.POINTER(kv_session), _I, _I, _P]),
+    "kv_gather_rows": (_I, [ctypes.POINTER(kv_shape), ctypes.POINTER(kv_session), _I, _I, _P, _P]),
+    "kv_scatter_rows": (_I, [ctypes.POINTER(kv_shape), ctypes.POINTER(kv_session), _I, _I, _P, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -227,6 +233,41 @@ def kv_probe_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> 
     _check(_lib.kv_probe_stream_read(_ptr(src, None, "src"), src.numel() * src.element_size(),
                                      _ptr(sink, torch.int32, "sink"), _stream(stream)),
            "kv_probe_stream_read")
+
+
+def _ptr_dev_or_pinned(t, name):
+    """Pointer of a contiguous GPU tensor or pinned host tensor."""
+    if not isinstance(t, torch.Tensor) or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous torch.Tensor")
+    if t.device.type != "cuda" and not t.is_pinned():
+        raise ValueError(f"{name}: must be a GPU tensor or pinned host memory")
+    return t.data_ptr()
+
+
+def kv_rows_bytes(shape: kv_shape, n_rows: int) -> int:
+    return int(_lib.kv_rows_bytes(ctypes.byref(shape), n_rows))
+
+
+def kv_copy_rows(shape: kv_shape, src: kv_session, src_row0: int, dst: kv_session, dst_row0: int,
+                 n_rows: int, stream=None) -> None:
+    _check(_lib.kv_copy_rows(ctypes.byref(shape), ctypes.byref(src), src_row0, ctypes.byref(dst),
+                             dst_row0, n_rows, _stream(stream)), "kv_copy_rows")
+
+
+def kv_gather_rows(shape: kv_shape, sess: kv_session, row0: int, n_rows: int, dst: torch.Tensor,
+                   stream=None) -> None:
+    if dst.numel() * dst.element_size() < kv_rows_bytes(shape, n_rows):
+        raise ValueError("kv_gather_rows: destination smaller than kv_rows_bytes")
+    _check(_lib.kv_gather_rows(ctypes.byref(shape), ctypes.byref(sess), row0, n_rows,
+                               _ptr_dev_or_pinned(dst, "dst"), _stream(stream)), "kv_gather_rows")
+
+
+def kv_scatter_rows(shape: kv_shape, sess: kv_session, row0: int, n_rows: int, src: torch.Tensor,
+                    stream=None) -> None:
+    if src.numel() * src.element_size() < kv_rows_bytes(shape, n_rows):
+        raise ValueError("kv_scatter_rows: source smaller than kv_rows_bytes")
+    _check(_lib.kv_scatter_rows(ctypes.byref(shape), ctypes.byref(sess), row0, n_rows,
+                                _ptr_dev_or_pinned(src, "src"), _stream(stream)), "kv_scatter_rows")
 
 
 def raw_lib() -> ctypes.CDLL:

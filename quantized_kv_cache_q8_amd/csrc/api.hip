@@ -40,6 +40,54 @@ int check_session(const kv_shape* s, const kv_session* e) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KV_OK : KV_ERR_HIP; }
 
+// The arrays of a session in packed order (K values, K scales, V values, V scales)
+// and the bytes of one head row of each (0: the format has no such array).
+void row_arrays(int fmt, const kv_session& e, char* ptr[4], size_t rb[4]) {
+  ptr[0] = static_cast<char*>(e.k);
+  ptr[1] = reinterpret_cast<char*>(e.k_scale);
+  ptr[2] = static_cast<char*>(e.v);
+  ptr[3] = reinterpret_cast<char*>(e.v_scale);
+  const bool f16 = fmt == KV_FMT_F16, k8v4 = fmt == KV_FMT_K8V4;
+  rb[0] = f16 ? HD * 2 : HD;
+  rb[1] = f16 ? 0 : NGRP * 2;
+  rb[2] = f16 ? HD * 2 : k8v4 ? HD / 2 : HD;
+  rb[3] = f16 ? 0 : (k8v4 ? NQ4 : NGRP) * 2;
+}
+
+// rows [row0, row0 + n) inside the session's capacity
+bool rows_fit(const kv_session& e, int row0, int n) {
+  return row0 >= 0 && n >= 0 && (long long)row0 + n <= e.cap;
+}
+
+// gather (to_packed) or scatter between rows of a session and a packed block
+int move_packed(const kv_shape* h_shape, const kv_session* h_sess, int row0, int n_rows,
+                char* packed, bool to_packed, void* stream) {
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  rc = check_session(h_shape, h_sess);
+  if (rc) return rc;
+  if (packed == nullptr || n_rows < 0) return KV_ERR_ARG;
+  if (!rows_fit(*h_sess, row0, n_rows)) return KV_ERR_RANGE;
+  if (n_rows == 0) return KV_OK;
+  char* ptr[4];
+  size_t rb[4];
+  row_arrays(h_shape->fmt, *h_sess, ptr, rb);
+  const size_t kvh = (size_t)h_shape->n_kv_heads, cap = (size_t)h_sess->cap;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  size_t off = 0;
+  for (int a = 0; a < 4; ++a) {
+    if (rb[a] == 0) continue;
+    const size_t w = (size_t)n_rows * rb[a];   // one head's rows, packed
+    char* rows = ptr[a] + (size_t)row0 * rb[a];
+    const hipError_t e =
+        to_packed ? hipMemcpy2DAsync(packed + off, w, rows, cap * rb[a], w, kvh, hipMemcpyDefault, st)
+                  : hipMemcpy2DAsync(rows, cap * rb[a], packed + off, w, w, kvh, hipMemcpyDefault, st);
+    if (e != hipSuccess) return KV_ERR_HIP;
+    off += w * kvh;
+  }
+  return KV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -160,6 +208,52 @@ int kv_probe_stream_read(const void* d_src, size_t bytes, uint32_t* d_sink, void
   if (!aligned16(d_src) || !aligned4(d_sink)) return KV_ERR_ALIGN;
   if (bytes == 0) return KV_OK;
   return hip_status(launch_stream_read(d_src, bytes, d_sink, static_cast<hipStream_t>(stream)));
+}
+
+size_t kv_rows_bytes(const kv_shape* h_shape, int n_rows) {
+  if (check_shape(h_shape) || n_rows < 0) return 0;
+  kv_session none{};
+  char* ptr[4];
+  size_t rb[4];
+  row_arrays(h_shape->fmt, none, ptr, rb);
+  return (size_t)h_shape->n_kv_heads * (size_t)n_rows * (rb[0] + rb[1] + rb[2] + rb[3]);
+}
+
+int kv_copy_rows(const kv_shape* h_shape, const kv_session* h_src, int src_row0,
+                 const kv_session* h_dst, int dst_row0, int n_rows, void* stream) {
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  if ((rc = check_session(h_shape, h_src)) || (rc = check_session(h_shape, h_dst))) return rc;
+  if (n_rows < 0) return KV_ERR_ARG;
+  if (!rows_fit(*h_src, src_row0, n_rows) || !rows_fit(*h_dst, dst_row0, n_rows))
+    return KV_ERR_RANGE;
+  if (n_rows == 0) return KV_OK;
+  char *ps[4], *pd[4];
+  size_t rb[4];
+  row_arrays(h_shape->fmt, *h_src, ps, rb);
+  row_arrays(h_shape->fmt, *h_dst, pd, rb);
+  const size_t kvh = (size_t)h_shape->n_kv_heads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int a = 0; a < 4; ++a) {
+    if (rb[a] == 0) continue;
+    const hipError_t e = hipMemcpy2DAsync(
+        pd[a] + (size_t)dst_row0 * rb[a], (size_t)h_dst->cap * rb[a],
+        ps[a] + (size_t)src_row0 * rb[a], (size_t)h_src->cap * rb[a], (size_t)n_rows * rb[a],
+        kvh, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return KV_ERR_HIP;
+  }
+  return KV_OK;
+}
+
+int kv_gather_rows(const kv_shape* h_shape, const kv_session* h_sess, int row0, int n_rows,
+                   void* d_or_h_dst, void* stream) {
+  return move_packed(h_shape, h_sess, row0, n_rows, static_cast<char*>(d_or_h_dst), true, stream);
+}
+
+int kv_scatter_rows(const kv_shape* h_shape, const kv_session* h_sess, int row0, int n_rows,
+                    const void* d_or_h_src, void* stream) {
+  return move_packed(h_shape, h_sess, row0, n_rows,
+                     const_cast<char*>(static_cast<const char*>(d_or_h_src)), false, stream);
 }
 
 const char* kv_status_str(int status) {

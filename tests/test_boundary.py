@@ -207,3 +207,31 @@ def test_probe_validation():
     assert P(A + 8, 64, B, None) == kq.KV_ERR_ALIGN
     assert P(A, 64, B + 2, None) == kq.KV_ERR_ALIGN
     assert P(A, 0, B, None) == kq.KV_OK                # nothing to read, nothing launched
+
+
+def test_row_moves_validation():
+    sh, s = shape(), sess()
+    P = ctypes.POINTER(kq.kv_session)
+    cp = lambda src, r0, dst, r1, n, sh=sh: L.kv_copy_rows(  # noqa: E731
+        ctypes.byref(sh), ctypes.byref(src), r0, ctypes.byref(dst), r1, n, None)
+    ga = lambda e, r0, n, buf=A, sh=sh: L.kv_gather_rows(  # noqa: E731
+        ctypes.byref(sh), ctypes.byref(e), r0, n, buf, None)
+    sc = lambda e, r0, n, buf=A, sh=sh: L.kv_scatter_rows(  # noqa: E731
+        ctypes.byref(sh), ctypes.byref(e), r0, n, buf, None)
+    assert cp(s, 0, sess(cap=512), 0, 513) == kq.KV_ERR_RANGE      # past the destination
+    assert cp(s, 1000, s, 0, 25) == kq.KV_ERR_RANGE                # past the source
+    assert cp(s, -1, s, 0, 1) == kq.KV_ERR_RANGE
+    assert cp(s, 0, s, 0, -1) == kq.KV_ERR_ARG
+    assert cp(s, 0, sess(ks=None), 0, 1) == kq.KV_ERR_FMT          # int8 without scales
+    assert cp(s, 0, s, 512, 0) == kq.KV_OK                         # nothing to move
+    assert ga(s, 1000, 25) == kq.KV_ERR_RANGE
+    assert ga(s, 0, 1, buf=None) == kq.KV_ERR_ARG
+    assert sc(s, 0, 1, buf=None) == kq.KV_ERR_ARG
+    assert sc(sess(fmt=F16), 0, 1, sh=shape(fmt=Q8)) == kq.KV_ERR_FMT
+    assert ga(s, 0, 0) == kq.KV_OK
+    assert L.kv_rows_bytes(ctypes.byref(shape(fmt=7)), 4) == 0
+    assert L.kv_rows_bytes(ctypes.byref(sh), -1) == 0
+    # per row of one head: Q8 128 + 4 + 128 + 4, F16 256 + 256, K8V4 128 + 4 + 64 + 8
+    assert L.kv_rows_bytes(ctypes.byref(sh), 1) == 8 * 264
+    assert L.kv_rows_bytes(ctypes.byref(shape(fmt=F16)), 1) == 8 * 512
+    assert L.kv_rows_bytes(ctypes.byref(shape(fmt=kq.KV_FMT_K8V4)), 1) == 8 * 204
