@@ -537,6 +537,8 @@ def main():
     ap.add_argument("--seed", type=int, default=44)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-side-configs", action="store_true",
+                    help="skip the smaller workloads (batch, short contexts, K8V4)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prompt-chunk side (compaction + attention, 2 timed "
                          "calls), e.g. under rocprofv3 counters")
@@ -638,7 +640,7 @@ def main():
         log(f"stream ceiling {key}: {ceiling[key]['GB_s']:.0f} GB/s over {ceiling[key]['bytes']} B; "
             f"decode at {roof[fmt]['vs_stream_ceiling']:.1%} of it")
 
-    sides = side_configs(kq, torch)
+    sides = None if args.no_side_configs else side_configs(kq, torch)
 
     prefill = None
     if not args.no_prefill:
