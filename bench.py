@@ -128,31 +128,64 @@ def build_model(kq, torch, seed, cap, warm_len):
     return model, append_rate
 
 
+def one_step(kq, torch, model, lens_w, lens_d, q, xk_new, xv_new, ws, out, events=None):
+    """One step: for each format and each of the 48 layers, a one-token append at
+    lens_w, then a decode over lens_d cells (max_len = the full context, a bound on
+    every length); then both lengths advance on the device.  Launches only, so a
+    step can be captured as a HIP graph."""
+    for fmt, m in model.items():
+        sh = m["shape"]
+        for li in range(LAYERS):
+            tab = m["tabs"][li]
+            kq.kv_append(sh, tab, lens_w, 1, 1, xk_new[li], xv_new[li])
+            if events is not None:
+                e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                e[0].record()
+            kq.kv_decode_attn(sh, tab, lens_d, 1, CTX, q[li], 1 / math.sqrt(HD), out, ws[fmt])
+            if events is not None:
+                e[1].record()
+                events[fmt].append(e)
+    lens_w += 1
+    lens_d += 1
+
+
 def run_steps(kq, torch, model, n_steps, len0, q, xk_new, xv_new, ws, events=None):
-    """n_steps decode steps starting with len0 cached cells; returns the final length."""
+    """n_steps eager steps starting with len0 cached cells; returns the final length."""
     # lens_w: where the new token goes (cells before it); lens_d: cells the decode reads
     lens_w = torch.full((1,), len0, dtype=torch.int32, device="cuda")
     lens_d = torch.full((1,), len0 + 1, dtype=torch.int32, device="cuda")
     out = torch.empty((1, NQH, HD), device="cuda")
-    length = len0
-    for step in range(n_steps):
-        for fmt, m in model.items():
-            sh = m["shape"]
-            for li in range(LAYERS):
-                tab = m["tabs"][li]
-                kq.kv_append(sh, tab, lens_w, 1, 1, xk_new[li], xv_new[li])
-                if events is not None:
-                    e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                    e[0].record()
-                kq.kv_decode_attn(sh, tab, lens_d, 1, length + 1, q[li], 1 / math.sqrt(HD), out,
-                                  ws[fmt])
-                if events is not None:
-                    e[1].record()
-                    events[fmt].append(e)
-        lens_w += 1
-        lens_d += 1
-        length += 1
-    return length
+    for _ in range(n_steps):
+        one_step(kq, torch, model, lens_w, lens_d, q, xk_new, xv_new, ws, out, events)
+    return len0 + n_steps
+
+
+def graph_steps(kq, torch, model, n_warm, n_steps, len0, q, xk_new, xv_new, ws):
+    """The same steps with one step captured once as a HIP graph and replayed: n_warm
+    untimed replays from len0 cells, then n_steps timed ones (synchronised on both
+    sides).  Returns the seconds of the timed replays."""
+    lens_w = torch.full((1,), len0, dtype=torch.int32, device="cuda")
+    lens_d = torch.full((1,), len0 + 1, dtype=torch.int32, device="cuda")
+    out = torch.empty((1, NQH, HD), device="cuda")
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            one_step(kq, torch, model, lens_w, lens_d, q, xk_new, xv_new, ws, out)
+    torch.cuda.synchronize()
+    assert int(lens_w.item()) == len0          # capturing runs nothing
+    for _ in range(n_warm):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n_steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    assert int(lens_w.item()) == len0 + n_warm + n_steps
+    assert torch.isfinite(out).all().item()
+    return t1 - t0
 
 
 def prefill_side(kq, torch, seed, steps, warmup):
@@ -599,10 +632,18 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     assert end_len == CTX
-    step_s = (t1 - t0) / n_steps
+    eager_step_s = (t1 - t0) / n_steps
     bytes_total = sum(decode_bytes(fmt, length + s + 1) * LAYERS for fmt in (F16, Q8)
                       for s in range(n_steps))
-    value = bytes_total / (t1 - t0) / 1e9
+    eager_value = bytes_total / (t1 - t0) / 1e9
+    log(f"eager steps: {eager_step_s * 1e3:.2f} ms per step, {eager_value:.0f} GB/s")
+    # the same steps again (lengths reset: the appends rewrite the same cells), one step
+    # captured as a HIP graph and replayed: the timed value
+    log(f"graph: warmup {n_warm}, timing {n_steps} replays")
+    g_s = graph_steps(kq, torch, model, n_warm, n_steps, len0, q, xk_new, xv_new, ws)
+    step_s = g_s / n_steps
+    value = bytes_total / g_s / 1e9
+    log(f"graph steps: {step_s * 1e3:.2f} ms per step, {value:.0f} GB/s")
 
     roof = {}
     for fmt in (F16, Q8):
@@ -661,7 +702,9 @@ def main():
                                "head_dim 128), 262144 cells, batch 1, FP16 cache and int8 cache; "
                                "a step appends one token per layer and decodes, both formats",
                    "layers": LAYERS, "kv_heads": KVH, "q_heads": NQH, "head_dim": HD,
-                   "context": CTX, "batch": 1, "formats": ["f16", "int8"]},
+                   "context": CTX, "batch": 1, "formats": ["f16", "int8"],
+                   "launch": "one step captured as a HIP graph, replayed per step"},
+        "eager": {"value": eager_value, "ms_per_step": eager_step_s * 1e3},
         "frac_hbm": value / HBM_PEAK_GBS,
         "roofline": roof[dominant],
         "roofline_int8" if dominant == F16 else "roofline_f16": roof[Q8 if dominant == F16 else F16],
