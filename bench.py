@@ -484,9 +484,30 @@ def side_configs(kq, torch, steps=10, warmup=3):
                     "decode_GB_s": nb / t / 1e9, "decode_frac_hbm": nb / t / 1e9 / HBM_PEAK_GBS,
                     "bulk_append_cells_per_s": ctx / app}
         log(f"{key}: decode {t * 1e6:.1f} us = {nb / t / 1e9:.0f} GB/s")
+        if fmt == Q8:
+            out["row_moves_int8"] = row_moves(kq, torch, sh, copies[0], copies[1], ctx)
         del copies, tabs, ws
         torch.cuda.empty_cache()
     return out
+
+
+def row_moves(kq, torch, sh, src, dst, n, reps=5):
+    """Moving all n rows of one int8 layer (every array, codes and scales): a device
+    copy into another session, a gather into pinned host memory and the scatter back;
+    HIP events on the launch stream, bytes moved per second."""
+    nbytes = kq.kv_rows_bytes(sh, n)
+    host = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
+    calls = [lambda: kq.kv_copy_rows(sh, src.entry(), 0, dst.entry(), 0, n),
+             lambda: kq.kv_gather_rows(sh, src.entry(), 0, n, host),
+             lambda: kq.kv_scatter_rows(sh, dst.entry(), 0, n, host)]
+    _time_calls(torch, calls, 1)
+    t = _time_calls(torch, calls, reps)
+    res = {"rows": n, "bytes": nbytes}
+    for name, ti in zip(("device_copy", "gather_to_pinned_host", "scatter_from_pinned_host"), t):
+        res[name] = {"us": ti * 1e6, "GB_s": nbytes / ti / 1e9}
+    log("row moves int8: " + ", ".join(f"{k} {v['GB_s']:.0f} GB/s" for k, v in res.items()
+                                        if isinstance(v, dict)))
+    return res
 
 
 def cpu_prefill_sample(cache, seed, n_rows=64):
