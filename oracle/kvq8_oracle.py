@@ -262,6 +262,70 @@ def unpack_rows(cache: Cache, row0: int, n: int, buf: np.ndarray) -> None:
 
 
 # ----------------------------------------------------------------------------
+# A saved session image: [P2, Scope] lays a saved KV file out as a 128-byte header,
+# the token ids (4 B each), the KV body and then, new in its version 3, a scales body;
+# version 3 is written only when the cache has scales, and version-2 files (no
+# scales) stay loadable for FP16 but are refused for an int8 cache [P2, Phased plan
+# and Not in scope].  Here the scales body holds the format's fp16 scale arrays
+# rather than one fp32 per token, head and K/V.  Header (little-endian): magic
+# b"KVQ8", u32 version, u32 format, u32 kv heads, u32 head_dim, u32 tokens, u64 body
+# bytes, u64 scales bytes, zeros to 128 bytes.  Body: K values then V values; scales
+# body: K scales then V scales; each array's rows [0, n) as [kvh][n][row bytes].
+# ----------------------------------------------------------------------------
+IMAGE_MAGIC = b"KVQ8"
+IMAGE_VERSION = 3
+IMAGE_HEADER = 128
+
+
+def save_image(cache: Cache, n: int, tokens) -> bytes:
+    def rows(name):
+        a = getattr(cache, name)
+        return b"" if a is None else np.ascontiguousarray(a[:, :n]).tobytes()
+    body = rows("k") + rows("v")
+    scales = rows("k_scale") + rows("v_scale")
+    version = IMAGE_VERSION if scales else 2
+    head = (IMAGE_MAGIC + np.array([version, cache.fmt, cache.kvh, cache.hd, n], "<u4").tobytes()
+            + np.array([len(body), len(scales)], "<u8").tobytes())
+    head += bytes(IMAGE_HEADER - len(head))
+    return head + np.asarray(tokens, "<i4").tobytes() + body + scales
+
+
+def load_image(image: bytes, fmt: int, kvh: int, cap: int, hd: int):
+    """Parse an image written by save_image into a fresh Cache; returns (cache, n,
+    tokens), or raises ValueError for a wrong magic, version, format or shape, a
+    version-2 image (no scales body) of a format with scales, or a short image."""
+    b = bytes(image)
+    if len(b) < IMAGE_HEADER or b[:4] != IMAGE_MAGIC:
+        raise ValueError("not an image")
+    version, f, h, d, n = np.frombuffer(b[4:24], "<u4").tolist()
+    body_bytes, scale_bytes = np.frombuffer(b[24:40], "<u8").tolist()
+    if (f, h, d) != (fmt, kvh, hd):
+        raise ValueError("format or shape differs")
+    if version not in (2, IMAGE_VERSION) or (version == 2 and fmt != FMT_F16):
+        raise ValueError(f"version {version} cannot hold this format")
+    if n > cap:
+        raise ValueError("more tokens than the capacity")
+    c = Cache(fmt, kvh, cap, hd)
+    want_body = sum(getattr(c, a)[:, :n].nbytes for a in ("k", "v"))
+    want_sc = sum(getattr(c, a)[:, :n].nbytes for a in ("k_scale", "v_scale")
+                  if getattr(c, a) is not None)
+    if body_bytes != want_body or scale_bytes != want_sc or \
+            len(b) < IMAGE_HEADER + 4 * n + want_body + want_sc:
+        raise ValueError("sizes differ")
+    off = IMAGE_HEADER
+    tokens = np.frombuffer(b[off:off + 4 * n], "<i4").copy()
+    off += 4 * n
+    for name in ("k", "v", "k_scale", "v_scale"):
+        a = getattr(c, name)
+        if a is None:
+            continue
+        dst = a[:, :n]
+        dst[...] = np.frombuffer(b[off:off + dst.nbytes], a.dtype).reshape(dst.shape)
+        off += dst.nbytes
+    return c, n, tokens
+
+
+# ----------------------------------------------------------------------------
 # O4: compaction to the FP16 [kvh][P][HD] copy the prompt GEMMs read
 # ----------------------------------------------------------------------------
 def hadamard_f64(n: int) -> np.ndarray:

@@ -28,6 +28,11 @@ What pins what:
     against SciPy's matrix and a closed-form error bound; the compacted V exact
     on dyadic inputs and per row against the fraction butterflies; the byte
     count against the 816 B per cell of PR #711, section What.
+  * saved image: the layout of Issue #67, section Scope (128-byte header, 4 bytes
+    per token, body, scales body; 8 scale bytes per token and kv head for q8 at
+    head_dim 128), the version rule of its Phased plan, the header read at its
+    stated offsets, the body read back against the inputs within the quantiser
+    bound, a round trip, and each refusal.
 """
 from __future__ import annotations
 
@@ -559,3 +564,86 @@ def pin_cache_bytes_k8v4(cache_bytes, FMT_K8V4):
         assert per_cell == gold["bytes_per_cell"], (kvh, hd, per_cell)
     assert cache_bytes(FMT_K8V4, 8, 1, 128, 2) == 8 * 64
     assert cache_bytes(FMT_K8V4, 8, 1, 128, 3) == 8 * 4 * 2
+
+
+# ----------------------------------------------------------------------------
+# saved session image
+# ----------------------------------------------------------------------------
+def _image_fields(img):
+    """The header read field by field at its stated offsets (independent of the
+    oracle's parser): version, fmt, kvh, hd, n, body bytes, scales bytes."""
+    assert img[:4] == b"KVQ8"
+    u32 = [int.from_bytes(img[4 + 4 * i:8 + 4 * i], "little") for i in range(5)]
+    u64 = [int.from_bytes(img[24 + 8 * i:32 + 8 * i], "little") for i in range(2)]
+    return (*u32, *u64)
+
+
+def pin_image(save, load, Cache, cache_bytes, FMT_F16, FMT_Q8, FMT_K8V4):
+    gold = _load("image_pages.json")
+    H, T = gold["header_bytes"], gold["token_bytes"]
+    r = np.random.default_rng(67)
+    kvh, cap, hd, n = 3, 128, 128, 37
+    xk = (r.standard_normal((n, kvh, hd)) * 2).astype(np.float32)
+    xv = (r.standard_normal((n, kvh, hd)) * 0.5 + 1).astype(np.float32)
+    tokens = r.integers(-2**31, 2**31, n, dtype=np.int64).astype(np.int32)
+    for fmt in (FMT_F16, FMT_Q8, FMT_K8V4):
+        c = Cache(fmt, kvh, cap, hd)
+        assert c.append(0, xk, xv)
+        img = save(c, n, tokens)
+        version, f, h, d, nn, body, scales = _image_fields(img)
+        assert (f, h, d, nn) == (fmt, kvh, hd, n), fmt
+        # version 3 exactly when the cache has scales; the header is 128 bytes, then
+        # 4 bytes per token, the body and the scales, sized by the pinned accounting
+        assert version == (gold["version_f16"] if fmt == FMT_F16 else gold["version_int8"])
+        assert not any(img[40:H])
+        parts = [cache_bytes(fmt, kvh, n, hd, p) for p in range(4)]
+        assert body == parts[0] + parts[2] and scales == parts[1] + parts[3], fmt
+        assert len(img) == H + T * n + body + scales
+        assert np.array_equal(np.frombuffer(img[H:H + T * n], "<i4"), tokens)
+        # the regions read back as the inputs: K then V in the body, K scales then V
+        # scales in the scales body, each [kvh][n][row]
+        b0, s0 = H + T * n, H + T * n + body
+        kx = np.transpose(xk, (1, 0, 2))
+        vx = np.transpose(xv, (1, 0, 2))
+        if fmt == FMT_F16:
+            assert scales == 0
+            k = np.frombuffer(img[b0:b0 + parts[0]], "<f2").reshape(kvh, n, hd)
+            v = np.frombuffer(img[b0 + parts[0]:s0], "<f2").reshape(kvh, n, hd)
+            assert np.array_equal(k, kx.astype(np.float16)) and np.array_equal(v, vx.astype(np.float16))
+        else:
+            k = np.frombuffer(img[b0:b0 + parts[0]], np.int8).reshape(kvh, n, hd // 64, 64)
+            ks = np.frombuffer(img[s0:s0 + parts[1]], "<f2").reshape(kvh, n, hd // 64, 1).astype(np.float64)
+            err = np.abs(k * ks - kx.reshape(k.shape))
+            assert np.all(err <= ks * (0.5 + 2.0**-16)), fmt
+            assert np.all(np.abs(k).max(-1) == 127), fmt
+            if fmt == FMT_Q8:
+                # the pages' scales body: 2 x 4 bytes per token and kv head at hd 128
+                assert scales == gold["scales_bytes_per_token_head"] * n * kvh
+                v = np.frombuffer(img[b0 + parts[0]:s0], np.int8).reshape(kvh, n, hd // 64, 64)
+                vs = np.frombuffer(img[s0 + parts[1]:], "<f2").reshape(kvh, n, hd // 64, 1).astype(np.float64)
+                assert np.all(np.abs(v * vs - vx.reshape(v.shape)) <= vs * (0.5 + 2.0**-16))
+        # a round trip rebuilds rows [0, n) and leaves the rest zero
+        d, m, toks = load(img, fmt, kvh, cap, hd)
+        assert m == n and np.array_equal(toks, tokens)
+        for a in ("k", "v", "k_scale", "v_scale"):
+            if getattr(c, a) is not None:
+                assert np.array_equal(getattr(d, a), getattr(c, a)), (fmt, a)
+        # refusals: a version-2 image of an int8 cache, another format or shape, a
+        # short image, a bad magic, more tokens than the capacity
+        def refused(b, f=fmt, h=kvh, cp=cap):
+            try:
+                load(b, f, h, cp, hd)
+            except ValueError:
+                return True
+            return False
+        v2 = img[:4] + (2).to_bytes(4, "little") + img[8:]
+        assert refused(v2) == (fmt != FMT_F16), fmt
+        if fmt != FMT_F16:
+            assert not refused(img)
+        assert refused(img, f=(fmt + 1) % 3) and refused(img, h=kvh + 1)
+        assert refused(img[:-1]) and refused(b"KVQ9" + img[4:])
+        assert refused(img, cp=32)
+    # an empty image: header only
+    c = Cache(FMT_Q8, kvh, cap, hd)
+    img = save(c, 0, np.zeros(0, np.int32))
+    assert len(img) == H and _image_fields(img)[4:] == (0, 0, 0)

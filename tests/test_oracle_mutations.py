@@ -333,3 +333,58 @@ def test_k8v4_bytes_mutant_caught():
         return oracle.cache_bytes(fmt, kvh, cap, hd, part)
 
     assert _fails(pins.pin_cache_bytes_k8v4, v_scales_per_64, _o.FMT_K8V4)
+
+
+# ----------------------------------------------------------------------------
+# saved image mutants: region order, scale interleave, version rule, token width
+# ----------------------------------------------------------------------------
+def _save_template(cache, n, tokens, order=("k", "v"), sc_order=("k_scale", "v_scale"),
+                   interleave=False, always_v3=False, tok_dtype="<i4"):
+    def rows(name):
+        a = getattr(cache, name)
+        return b"" if a is None else np.ascontiguousarray(a[:, :n]).tobytes()
+    body = b"".join(rows(a) for a in order)
+    if interleave and cache.k_scale is not None:
+        scales = b"".join(np.ascontiguousarray(getattr(cache, a)[h, :n]).tobytes()
+                          for h in range(cache.kvh) for a in sc_order)
+    else:
+        scales = b"".join(rows(a) for a in sc_order)
+    version = 3 if (scales or always_v3) else 2
+    head = (b"KVQ8" + np.array([version, cache.fmt, cache.kvh, cache.hd, n], "<u4").tobytes()
+            + np.array([len(body), len(scales)], "<u8").tobytes())
+    head += bytes(128 - len(head))
+    return head + np.asarray(tokens, tok_dtype).tobytes() + body + scales
+
+
+def _pin_image_with(save=None, load=None):
+    return _fails(pins.pin_image, save or oracle.save_image, load or oracle.load_image,
+                  oracle.Cache, oracle.cache_bytes, oracle.FMT_F16, oracle.FMT_Q8,
+                  oracle.FMT_K8V4)
+
+
+IMAGE_MUTANTS = {
+    "V body before K": dict(order=("v", "k")),
+    "V scales before K scales": dict(sc_order=("v_scale", "k_scale")),
+    "scales interleaved per head": dict(interleave=True),
+    "version 3 for FP16": dict(always_v3=True),
+    "8-byte token ids": dict(tok_dtype="<i8"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(IMAGE_MUTANTS))
+def test_image_save_mutant_is_caught(name):
+    kw = IMAGE_MUTANTS[name]
+    assert _pin_image_with(save=lambda c, n, t: _save_template(c, n, t, **kw)), name
+
+
+def test_unmutated_image_template_passes():
+    assert not _pin_image_with(save=_save_template)
+
+
+def test_image_load_accepting_v2_for_int8_is_caught():
+    def lenient(img, fmt, kvh, cap, hd):
+        b = bytearray(img)
+        if int.from_bytes(b[4:8], "little") == 2:
+            b[4:8] = (3).to_bytes(4, "little")
+        return oracle.load_image(bytes(b), fmt, kvh, cap, hd)
+    assert _pin_image_with(load=lenient)
