@@ -493,18 +493,27 @@ def side_configs(kq, torch, steps=10, warmup=3):
 
 def row_moves(kq, torch, sh, src, dst, n, reps=5):
     """Moving all n rows of one int8 layer (every array, codes and scales): a device
-    copy into another session, a gather into pinned host memory and the scatter back;
-    HIP events on the launch stream, bytes moved per second."""
+    copy into another session, a gather into pinned host memory and the scatter back,
+    and a saved image of the session (header and token ids written by the host, body
+    and scales copied) built and loaded back; HIP events on the launch stream, bytes
+    moved (the image's whole size for the image calls) per second."""
     nbytes = kq.kv_rows_bytes(sh, n)
     host = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
+    ibytes = kq.kv_image_bytes(sh, n)
+    image = torch.empty(ibytes, dtype=torch.uint8).pin_memory()
+    tokens = torch.arange(n, dtype=torch.int32)
     calls = [lambda: kq.kv_copy_rows(sh, src.entry(), 0, dst.entry(), 0, n),
              lambda: kq.kv_gather_rows(sh, src.entry(), 0, n, host),
-             lambda: kq.kv_scatter_rows(sh, dst.entry(), 0, n, host)]
+             lambda: kq.kv_scatter_rows(sh, dst.entry(), 0, n, host),
+             lambda: kq.kv_image_save(sh, src.entry(), n, tokens, image),
+             lambda: kq.kv_image_load(sh, dst.entry(), image)]
     _time_calls(torch, calls, 1)
     t = _time_calls(torch, calls, reps)
-    res = {"rows": n, "bytes": nbytes}
-    for name, ti in zip(("device_copy", "gather_to_pinned_host", "scatter_from_pinned_host"), t):
-        res[name] = {"us": ti * 1e6, "GB_s": nbytes / ti / 1e9}
+    res = {"rows": n, "bytes": nbytes, "image_bytes": ibytes}
+    names = ("device_copy", "gather_to_pinned_host", "scatter_from_pinned_host",
+             "image_save_to_pinned_host", "image_load_from_pinned_host")
+    for name, ti, b in zip(names, t, (nbytes,) * 3 + (ibytes,) * 2):
+        res[name] = {"us": ti * 1e6, "GB_s": b / ti / 1e9}
     log("row moves int8: " + ", ".join(f"{k} {v['GB_s']:.0f} GB/s" for k, v in res.items()
                                         if isinstance(v, dict)))
     return res

@@ -79,7 +79,8 @@ enum {
   KV_ERR_UNSUPPORTED = -4, /* head_dim != 128, or G not in {1, 2, 4, 8} */
   KV_ERR_WORKSPACE = -5,   /* workspace null or smaller than the *_workspace_bytes value */
   KV_ERR_RANGE = -6,       /* rows outside [0, cap), or cap above 2^24 (host-checkable cases) */
-  KV_ERR_HIP = -7          /* a kernel launch failed */
+  KV_ERR_HIP = -7,         /* a kernel launch or copy failed */
+  KV_ERR_IMAGE = -8        /* a saved image refused: magic, version, format, shape or size */
 };
 
 /* bits OR-ed into *d_status by kernels */
@@ -184,6 +185,46 @@ int kv_gather_rows(const kv_shape* h_shape, const kv_session* h_sess, int row0, 
                    void* d_or_h_dst, void* stream);
 int kv_scatter_rows(const kv_shape* h_shape, const kv_session* h_sess, int row0, int n_rows,
                     const void* d_or_h_src, void* stream);
+
+/* Saved session image ([P2, Scope]: a header, the token ids, the KV body, then the
+ * scales body; [P2, Phased plan]: version 3 carries the scales, and a version-2 image
+ * is refused for an int8 cache).  The calls build and read an image in caller-owned
+ * host memory; writing it to a file, or reading it back, is the caller's.  Layout:
+ *   bytes [0, 128)  header, little-endian: "KVQ8", u32 version (3 when the format has
+ *                   scales, else 2), u32 fmt, u32 n_kv_heads, u32 head_dim,
+ *                   u32 n_tokens, u64 body bytes, u64 scales bytes, zeros;
+ *   then            n_tokens int32 token ids;
+ *   then the body   K values, then V values, of rows [0, n_tokens);
+ *   then the scales K scales, then V scales (absent for F16);
+ * each array's rows as [n_kv_heads][n_tokens][row bytes] (row bytes as for
+ * kv_rows_bytes).  The scale arrays are the format's fp16 ones, in place of one
+ * fp32 per token, head and K/V.
+ * kv_image_bytes: the image size for n_tokens rows; 0 on invalid arguments. */
+size_t kv_image_bytes(const kv_shape* h_shape, int n_tokens);
+
+/* Build the image of rows [0, n_tokens) of a session in h_image (host memory
+ * allocated pinned, at least kv_image_bytes bytes).  The header and the token ids
+ * (h_tokens: host int32 [n_tokens], may be NULL when n_tokens == 0) are written
+ * before the call returns; the body and scales are copied asynchronously on the
+ * stream, so the image is complete once the stream reaches the call.
+ * KV_ERR_RANGE if n_tokens exceeds the capacity, KV_ERR_ARG for a short image. */
+int kv_image_save(const kv_shape* h_shape, const kv_session* h_sess, int n_tokens,
+                  const int32_t* h_tokens, void* h_image, size_t image_bytes, void* stream);
+
+/* Check an image's header against h_shape and image_bytes; the number of tokens it
+ * holds, or KV_ERR_IMAGE (bad magic, version 2 with a format that has scales, an
+ * unknown version, another format, n_kv_heads or head_dim, region sizes that do not
+ * match them, or an image shorter than its regions).  Host only. */
+int kv_image_tokens(const kv_shape* h_shape, const void* h_image, size_t image_bytes);
+
+/* Load an image into rows [0, n) of a session: checks as kv_image_tokens, then
+ * KV_ERR_RANGE if n exceeds the capacity; copies the token ids to h_tokens (host,
+ * room for n; may be NULL) before returning, and enqueues the copies of the body and
+ * scales into the session on the stream (h_image: host memory allocated pinned,
+ * valid until the stream reaches the call).  Returns n >= 0 on success.  Rows at and
+ * above n are left as they were. */
+int kv_image_load(const kv_shape* h_shape, const kv_session* h_sess, const void* h_image,
+                  size_t image_bytes, int32_t* h_tokens, void* stream);
 
 /* Static text for a KV_* status code. */
 const char* kv_status_str(int status);

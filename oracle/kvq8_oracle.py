@@ -12,6 +12,8 @@ which the GPU kernel takes the same integer decisions).
 Sources (web pages; cited by title and section):
   [P1] PR #3084 "FP16 K/V cache by default, int8 with --kv-q8 (262144 fits a
        16 GiB card)": sections Summary, What changed, Extra Notes.
+  [P2] Issue #67 "Path F format v3: persist per-head INT8 KV scales": sections
+       Scope, Phased plan, Not in scope.
   [P3] PR #711 "kv: --kv k8v4 streams with --kv-resident": sections What, How.
 
 Readings where the pages are silent (all listed in the design doc):
@@ -33,6 +35,11 @@ Readings where the pages are silent (all listed in the design doc):
   * query head q reads kv head q // G, G = n_q_heads / n_kv_heads.
   * the prompt chunk rounds its queries to fp16 before Q K^T, as the GEMMs read
     halves; row i of a chunk at position pos0 attends keys [0, pos0 + i].
+  * saved image ([P2]): the header's fields are not on the pages, so they are this
+    module's own (magic, version, format, shape, token count, region sizes); the
+    scales body holds the fp16 scale arrays of the format in place of one fp32 per
+    token, head and K/V; the version is 3 for every format with scales (also with
+    zero tokens) and 2 for FP16.
 
 Parity pins: every function here is checked by ``tests/test_oracle_*.py``
 against closed forms, invariants, brute force with exact rational arithmetic and
@@ -283,7 +290,7 @@ def save_image(cache: Cache, n: int, tokens) -> bytes:
         return b"" if a is None else np.ascontiguousarray(a[:, :n]).tobytes()
     body = rows("k") + rows("v")
     scales = rows("k_scale") + rows("v_scale")
-    version = IMAGE_VERSION if scales else 2
+    version = 2 if cache.fmt == FMT_F16 else IMAGE_VERSION
     head = (IMAGE_MAGIC + np.array([version, cache.fmt, cache.kvh, cache.hd, n], "<u4").tobytes()
             + np.array([len(body), len(scales)], "<u8").tobytes())
     head += bytes(IMAGE_HEADER - len(head))

@@ -22,13 +22,14 @@ KV_FMT_F16, KV_FMT_Q8, KV_FMT_K8V4 = 0, 1, 2
 KV_GROUP = 64
 KV_Q4_BLOCK = 32
 KV_OK, KV_ERR_ARG, KV_ERR_FMT, KV_ERR_ALIGN, KV_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
-KV_ERR_WORKSPACE, KV_ERR_RANGE, KV_ERR_HIP = -5, -6, -7
+KV_ERR_WORKSPACE, KV_ERR_RANGE, KV_ERR_HIP, KV_ERR_IMAGE = -5, -6, -7, -8
 KV_DEV_RANGE, KV_DEV_BAD_SESSION = 1, 2
 
 EXPORTED = ["kv_cache_bytes", "kv_append", "kv_decode_workspace_bytes", "kv_decode_attn",
             "kv_compact_f16", "kv_prefill_workspace_bytes", "kv_prefill_attn", "kv_status_str",
             "kv_probe_stream_read", "kv_rows_bytes", "kv_copy_rows", "kv_gather_rows",
-            "kv_scatter_rows"]
+            "kv_scatter_rows", "kv_image_bytes", "kv_image_save", "kv_image_tokens",
+            "kv_image_load"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run quantized_kv_cache_q8_amd.build.build() "
@@ -68,6 +69,11 @@ _sig = {
                           ctypes.POINTER(kv_session), _I, _I, _P]),
     "kv_gather_rows": (_I, [ctypes.POINTER(kv_shape), ctypes.POINTER(kv_session), _I, _I, _P, _P]),
     "kv_scatter_rows": (_I, [ctypes.POINTER(kv_shape), ctypes.POINTER(kv_session), _I, _I, _P, _P]),
+    "kv_image_bytes": (_SZ, [ctypes.POINTER(kv_shape), _I]),
+    "kv_image_save": (_I, [ctypes.POINTER(kv_shape), ctypes.POINTER(kv_session), _I, _P, _P, _SZ,
+                           _P]),
+    "kv_image_tokens": (_I, [ctypes.POINTER(kv_shape), _P, _SZ]),
+    "kv_image_load": (_I, [ctypes.POINTER(kv_shape), ctypes.POINTER(kv_session), _P, _SZ, _P, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -268,6 +274,54 @@ def kv_scatter_rows(shape: kv_shape, sess: kv_session, row0: int, n_rows: int, s
         raise ValueError("kv_scatter_rows: source smaller than kv_rows_bytes")
     _check(_lib.kv_scatter_rows(ctypes.byref(shape), ctypes.byref(sess), row0, n_rows,
                                 _ptr_dev_or_pinned(src, "src"), _stream(stream)), "kv_scatter_rows")
+
+
+def _host_u8(t, name, pinned):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cpu" or not t.is_contiguous() \
+            or t.dtype != torch.uint8:
+        raise ValueError(f"{name}: expected a contiguous uint8 host tensor")
+    if pinned and not t.is_pinned():
+        raise ValueError(f"{name}: must be pinned host memory")
+    return t.data_ptr()
+
+
+def _host_i32(t, n, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cpu" or not t.is_contiguous() \
+            or t.dtype != torch.int32 or t.numel() < n:
+        raise ValueError(f"{name}: expected a contiguous int32 host tensor of at least {n} entries")
+    return t.data_ptr()
+
+
+def kv_image_bytes(shape: kv_shape, n_tokens: int) -> int:
+    return int(_lib.kv_image_bytes(ctypes.byref(shape), n_tokens))
+
+
+def kv_image_save(shape: kv_shape, sess: kv_session, n_tokens: int, tokens, image: torch.Tensor,
+                  stream=None) -> None:
+    """Saved image of rows [0, n_tokens) into a pinned uint8 host tensor; complete once
+    the stream reaches the call."""
+    _check(_lib.kv_image_save(ctypes.byref(shape), ctypes.byref(sess), n_tokens,
+                              _host_i32(tokens, n_tokens, "tokens"),
+                              _host_u8(image, "image", True), image.numel(), _stream(stream)),
+           "kv_image_save")
+
+
+def kv_image_tokens(shape: kv_shape, image: torch.Tensor) -> int:
+    n = _lib.kv_image_tokens(ctypes.byref(shape), _host_u8(image, "image", False), image.numel())
+    _check(min(n, 0), "kv_image_tokens")
+    return n
+
+
+def kv_image_load(shape: kv_shape, sess: kv_session, image: torch.Tensor, tokens=None,
+                  stream=None) -> int:
+    """Load a saved image (pinned uint8 host tensor) into rows [0, n); returns n."""
+    need = kv_image_tokens(shape, image) if tokens is not None else 0
+    n = _lib.kv_image_load(ctypes.byref(shape), ctypes.byref(sess), _host_u8(image, "image", True),
+                           image.numel(), _host_i32(tokens, need, "tokens"), _stream(stream))
+    _check(min(n, 0), "kv_image_load")
+    return n
 
 
 def raw_lib() -> ctypes.CDLL:

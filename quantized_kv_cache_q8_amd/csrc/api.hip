@@ -1,6 +1,7 @@
 // The C ABI of libkvq8: argument validation (before any HIP call) and launches.
 // Declarations and their contracts are in include/kvq8.h.
 #include <cmath>
+#include <cstring>
 
 #include "kvq8_internal.h"
 
@@ -59,9 +60,15 @@ bool rows_fit(const kv_session& e, int row0, int n) {
   return row0 >= 0 && n >= 0 && (long long)row0 + n <= e.cap;
 }
 
-// gather (to_packed) or scatter between rows of a session and a packed block
+// packed block order: K values, K scales, V values, V scales
+constexpr int kRowOrder[4] = {0, 1, 2, 3};
+// saved image order: the body (K values, V values), then the scales body
+constexpr int kImageOrder[4] = {0, 2, 1, 3};
+
+// gather (to_packed) or scatter between rows of a session and a packed block whose
+// arrays follow `order`
 int move_packed(const kv_shape* h_shape, const kv_session* h_sess, int row0, int n_rows,
-                char* packed, bool to_packed, void* stream) {
+                char* packed, bool to_packed, void* stream, const int* order = kRowOrder) {
   int rc = check_shape(h_shape);
   if (rc) return rc;
   rc = check_session(h_shape, h_sess);
@@ -75,7 +82,8 @@ int move_packed(const kv_shape* h_shape, const kv_session* h_sess, int row0, int
   const size_t kvh = (size_t)h_shape->n_kv_heads, cap = (size_t)h_sess->cap;
   hipStream_t st = static_cast<hipStream_t>(stream);
   size_t off = 0;
-  for (int a = 0; a < 4; ++a) {
+  for (int i = 0; i < 4; ++i) {
+    const int a = order[i];
     if (rb[a] == 0) continue;
     const size_t w = (size_t)n_rows * rb[a];   // one head's rows, packed
     char* rows = ptr[a] + (size_t)row0 * rb[a];
@@ -86,6 +94,53 @@ int move_packed(const kv_shape* h_shape, const kv_session* h_sess, int row0, int
     off += w * kvh;
   }
   return KV_OK;
+}
+
+// Saved session image: a 128-byte little-endian header (magic "KVQ8", u32 version,
+// fmt, kv heads, head_dim, tokens, u64 body bytes, u64 scales bytes, zeros), the
+// token ids as int32, the body, the scales body.
+constexpr size_t kImageHeader = 128;
+constexpr uint32_t kImageV2 = 2, kImageV3 = 3;
+
+void put_le(unsigned char* p, uint64_t v, int bytes) {
+  for (int i = 0; i < bytes; ++i) p[i] = (unsigned char)(v >> (8 * i));
+}
+uint64_t get_le(const unsigned char* p, int bytes) {
+  uint64_t v = 0;
+  for (int i = 0; i < bytes; ++i) v |= (uint64_t)p[i] << (8 * i);
+  return v;
+}
+
+// body and scales-body bytes of n rows of a valid shape
+void image_regions(const kv_shape* s, int n, size_t* body, size_t* scales) {
+  kv_session none{};
+  char* ptr[4];
+  size_t rb[4];
+  row_arrays(s->fmt, none, ptr, rb);
+  const size_t rows = (size_t)s->n_kv_heads * (size_t)n;
+  *body = rows * (rb[0] + rb[2]);
+  *scales = rows * (rb[1] + rb[3]);
+}
+
+// Parse and check a header against the shape and the image size; the token count,
+// or a negative KV_ERR_*.
+int image_header(const kv_shape* s, const unsigned char* img, size_t image_bytes) {
+  if (image_bytes < kImageHeader || img[0] != 'K' || img[1] != 'V' || img[2] != 'Q' ||
+      img[3] != '8')
+    return KV_ERR_IMAGE;
+  const uint64_t version = get_le(img + 4, 4), fmt = get_le(img + 8, 4),
+                 kvh = get_le(img + 12, 4), hd = get_le(img + 16, 4), n = get_le(img + 20, 4),
+                 body = get_le(img + 24, 8), scales = get_le(img + 32, 8);
+  if (fmt != (uint64_t)s->fmt || kvh != (uint64_t)s->n_kv_heads || hd != (uint64_t)s->head_dim)
+    return KV_ERR_IMAGE;
+  // version 2 carries no scales: loadable for FP16 only
+  if (version != kImageV3 && !(version == kImageV2 && s->fmt == KV_FMT_F16)) return KV_ERR_IMAGE;
+  if (n > (uint64_t)KV_MAX_CAP) return KV_ERR_IMAGE;
+  size_t want_body, want_scales;
+  image_regions(s, (int)n, &want_body, &want_scales);
+  if (body != want_body || scales != want_scales) return KV_ERR_IMAGE;
+  if (image_bytes < kImageHeader + 4 * n + want_body + want_scales) return KV_ERR_IMAGE;
+  return (int)n;
 }
 
 }  // namespace
@@ -256,6 +311,66 @@ int kv_scatter_rows(const kv_shape* h_shape, const kv_session* h_sess, int row0,
                      const_cast<char*>(static_cast<const char*>(d_or_h_src)), false, stream);
 }
 
+size_t kv_image_bytes(const kv_shape* h_shape, int n_tokens) {
+  if (check_shape(h_shape) || n_tokens < 0 || n_tokens > KV_MAX_CAP) return 0;
+  size_t body, scales;
+  image_regions(h_shape, n_tokens, &body, &scales);
+  return kImageHeader + 4 * (size_t)n_tokens + body + scales;
+}
+
+int kv_image_save(const kv_shape* h_shape, const kv_session* h_sess, int n_tokens,
+                  const int32_t* h_tokens, void* h_image, size_t image_bytes, void* stream) {
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  if ((rc = check_session(h_shape, h_sess))) return rc;
+  if (h_image == nullptr || n_tokens < 0 || (n_tokens > 0 && h_tokens == nullptr))
+    return KV_ERR_ARG;
+  if (!rows_fit(*h_sess, 0, n_tokens)) return KV_ERR_RANGE;
+  if (image_bytes < kv_image_bytes(h_shape, n_tokens)) return KV_ERR_ARG;
+  size_t body, scales;
+  image_regions(h_shape, n_tokens, &body, &scales);
+  unsigned char* img = static_cast<unsigned char*>(h_image);
+  memset(img, 0, kImageHeader);
+  memcpy(img, "KVQ8", 4);
+  put_le(img + 4, h_shape->fmt == KV_FMT_F16 ? kImageV2 : kImageV3, 4);
+  put_le(img + 8, (uint32_t)h_shape->fmt, 4);
+  put_le(img + 12, (uint32_t)h_shape->n_kv_heads, 4);
+  put_le(img + 16, (uint32_t)h_shape->head_dim, 4);
+  put_le(img + 20, (uint32_t)n_tokens, 4);
+  put_le(img + 24, body, 8);
+  put_le(img + 32, scales, 8);
+  for (int t = 0; t < n_tokens; ++t) put_le(img + kImageHeader + 4 * (size_t)t, (uint32_t)h_tokens[t], 4);
+  return move_packed(h_shape, h_sess, 0, n_tokens,
+                     reinterpret_cast<char*>(img + kImageHeader + 4 * (size_t)n_tokens), true,
+                     stream, kImageOrder);
+}
+
+int kv_image_tokens(const kv_shape* h_shape, const void* h_image, size_t image_bytes) {
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  if (h_image == nullptr) return KV_ERR_ARG;
+  return image_header(h_shape, static_cast<const unsigned char*>(h_image), image_bytes);
+}
+
+int kv_image_load(const kv_shape* h_shape, const kv_session* h_sess, const void* h_image,
+                  size_t image_bytes, int32_t* h_tokens, void* stream) {
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  if ((rc = check_session(h_shape, h_sess))) return rc;
+  if (h_image == nullptr) return KV_ERR_ARG;
+  const unsigned char* img = static_cast<const unsigned char*>(h_image);
+  const int n = image_header(h_shape, img, image_bytes);
+  if (n < 0) return n;
+  if (!rows_fit(*h_sess, 0, n)) return KV_ERR_RANGE;
+  if (h_tokens != nullptr)
+    for (int t = 0; t < n; ++t)
+      h_tokens[t] = (int32_t)(uint32_t)get_le(img + kImageHeader + 4 * (size_t)t, 4);
+  rc = move_packed(h_shape, h_sess, 0, n,
+                   const_cast<char*>(reinterpret_cast<const char*>(img + kImageHeader + 4 * (size_t)n)),
+                   false, stream, kImageOrder);
+  return rc ? rc : n;
+}
+
 const char* kv_status_str(int status) {
   switch (status) {
     case KV_OK: return "ok";
@@ -265,7 +380,8 @@ const char* kv_status_str(int status) {
     case KV_ERR_UNSUPPORTED: return "unsupported head_dim or query/kv head ratio";
     case KV_ERR_WORKSPACE: return "workspace missing or too small";
     case KV_ERR_RANGE: return "rows outside the session's capacity";
-    case KV_ERR_HIP: return "HIP kernel launch failed";
+    case KV_ERR_HIP: return "HIP kernel launch or copy failed";
+    case KV_ERR_IMAGE: return "saved image refused (magic, version, format, shape or size)";
     default: return "unknown status";
   }
 }

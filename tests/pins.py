@@ -643,7 +643,11 @@ def pin_image(save, load, Cache, cache_bytes, FMT_F16, FMT_Q8, FMT_K8V4):
         assert refused(img, f=(fmt + 1) % 3) and refused(img, h=kvh + 1)
         assert refused(img[:-1]) and refused(b"KVQ9" + img[4:])
         assert refused(img, cp=32)
-    # an empty image: header only
-    c = Cache(FMT_Q8, kvh, cap, hd)
-    img = save(c, 0, np.zeros(0, np.int32))
-    assert len(img) == H and _image_fields(img)[4:] == (0, 0, 0)
+    # an empty image: header only, its version still set by the format, and loadable
+    for fmt in (FMT_F16, FMT_Q8, FMT_K8V4):
+        c = Cache(fmt, kvh, cap, hd)
+        img = save(c, 0, np.zeros(0, np.int32))
+        fields = _image_fields(img)
+        assert len(img) == H and fields[4:] == (0, 0, 0)
+        assert fields[0] == (gold["version_f16"] if fmt == FMT_F16 else gold["version_int8"])
+        assert load(img, fmt, kvh, cap, hd)[1] == 0

@@ -339,7 +339,7 @@ def test_k8v4_bytes_mutant_caught():
 # saved image mutants: region order, scale interleave, version rule, token width
 # ----------------------------------------------------------------------------
 def _save_template(cache, n, tokens, order=("k", "v"), sc_order=("k_scale", "v_scale"),
-                   interleave=False, always_v3=False, tok_dtype="<i4"):
+                   interleave=False, always_v3=False, tok_dtype="<i4", version_from_bytes=False):
     def rows(name):
         a = getattr(cache, name)
         return b"" if a is None else np.ascontiguousarray(a[:, :n]).tobytes()
@@ -349,7 +349,9 @@ def _save_template(cache, n, tokens, order=("k", "v"), sc_order=("k_scale", "v_s
                           for h in range(cache.kvh) for a in sc_order)
     else:
         scales = b"".join(rows(a) for a in sc_order)
-    version = 3 if (scales or always_v3) else 2
+    version = 3 if (cache.fmt != oracle.FMT_F16 or always_v3) else 2
+    if version_from_bytes:
+        version = 3 if scales else 2
     head = (b"KVQ8" + np.array([version, cache.fmt, cache.kvh, cache.hd, n], "<u4").tobytes()
             + np.array([len(body), len(scales)], "<u8").tobytes())
     head += bytes(128 - len(head))
@@ -368,6 +370,7 @@ IMAGE_MUTANTS = {
     "scales interleaved per head": dict(interleave=True),
     "version 3 for FP16": dict(always_v3=True),
     "8-byte token ids": dict(tok_dtype="<i8"),
+    "version from the scale bytes": dict(version_from_bytes=True),
 }
 
 
