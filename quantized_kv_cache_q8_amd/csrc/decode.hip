@@ -74,7 +74,7 @@ __device__ __forceinline__ u32x2 ldkv64(const char* base, uint32_t off) {
 #endif
 // share (sixteenths) of a head's steps taken by the leading group of waves
 #ifndef KVQ8_DEC_LEAD16_Q8
-#define KVQ8_DEC_LEAD16_Q8 12
+#define KVQ8_DEC_LEAD16_Q8 8
 #endif
 #ifndef KVQ8_DEC_LEAD16_F16
 #define KVQ8_DEC_LEAD16_F16 8
@@ -176,6 +176,19 @@ __device__ __forceinline__ uint32_t nibble_bytes(uint32_t x) {
   return r;
 }
 
+// Signed byte k of w as fp32, in one instruction (a byte-select conversion with sign
+// extension); written out because the compiler sometimes extracts the byte first.
+__device__ __forceinline__ float i8_to_f32(uint32_t w, int k) {
+  float r;
+  switch (k) {
+    case 0: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0" : "=v"(r) : "v"(w)); break;
+    case 1: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(w)); break;
+    case 2: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(w)); break;
+    default: asm("v_cvt_f32_i32_sdwa %0, sext(%1) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(w)); break;
+  }
+  return r;
+}
+
 // Head dim of the i-th of the 16 values a lane (c = lane % 8) holds of a row.
 template <int FMT>
 __device__ __forceinline__ int lane_dim(int c, int i) {
@@ -206,9 +219,10 @@ __device__ __forceinline__ void load_p(const float* src, float (&p)[G]) {
 template <int G>
 __host__ __device__ constexpr int ch_steps() { return G >= 8 ? 56 : KVQ8_DEC_CH; }
 // logits budget of a wave of group 0 and of group 1, in proportion to their shares
+// (group 0's rounded down to whole pairs of the largest load batch with 8 heads)
 template <int FMT, int G>
 __host__ __device__ constexpr int ch0() {
-  return GROUPED ? 2 * ch_steps<G>() * lead16<FMT>() / 16 : ch_steps<G>();
+  return GROUPED ? 2 * ch_steps<G>() * lead16<FMT>() / 16 / 8 * 8 : ch_steps<G>();
 }
 template <int FMT, int G>
 __host__ __device__ constexpr int ch1() { return GROUPED ? 2 * ch_steps<G>() - ch0<FMT, G>() : 0; }
@@ -225,12 +239,13 @@ struct Batch {
   // and are masked by the callers
   // vals, scales: the head's first row of values and of scales
   // V: the V array (only K8V4 lays it out differently from K)
+  // kmax: steps past it re-read step kmax (a row of this wave's, still in cache)
   template <bool V>
   __device__ __forceinline__ void load(const char* vals, const char* scales, int gw, int W, int k,
-                                       int len, int r, int c) {
+                                       int len, int r, int c, int kmax = 1 << 30) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t row = (uint32_t)min((gw + (k + u) * W) * 8 + r, len - 1);
+      const uint32_t row = (uint32_t)min((gw + min(k + u, kmax) * W) * 8 + r, len - 1);
       if constexpr (FMT == KV_FMT_K8V4 && V) {
         ch[u].load_v(vals, row, c);
         sc[u] = ldg16(scales + (row * NQ4 + (c >> 1)) * 2);   // lane c: dims of block c / 2
@@ -277,6 +292,66 @@ __device__ __forceinline__ void fold_stage(float (&x)[U][G]) {
   }
 }
 
+// The int8 K pass on the matrix cores.  The logits of G query heads against 16
+// tokens are a small integer product per 64-dim scale group: the query, in log2
+// units, is split per (head, group) into three int8 levels,
+//   q = s (a + b / 254 + c / 254^2),  s = max|q| / 127 over the group,
+// so each level's dot products with the raw codes are exact integers, and the
+// residual after three levels is at most s / (2 * 254^2), about 2^-24 of the group's
+// largest query value (the precision of fp32).  One v_mfma_i32_16x16x64_i8 per group
+// and 4 heads takes A = the query levels (row 4 * head + level, the fourth row of a
+// head zero) and B = the codes of 16 tokens (column = token), so that lane l receives
+// the three level sums of head l / 16 and token l % 16 and turns them into one logit.
+// Any assignment of dims to k-slots is a valid contraction as long as A and B use
+// the same one: lane l's byte j of both operands is dim 64 * group + 16 * (l / 16) + j.
+#ifndef KVQ8_DEC_KMFMA
+#define KVQ8_DEC_KMFMA 1
+#endif
+// 8-token steps per K batch of the matrix-core pass (two batches alternate)
+#ifndef KVQ8_DEC_UK_Q8
+#define KVQ8_DEC_UK_Q8 8
+#endif
+template <int G>
+__host__ __device__ constexpr int k_batch_rows() { return G >= 8 ? 4 : KVQ8_DEC_UK_Q8; }
+template <int FMT>
+__host__ __device__ constexpr bool kmfma() { return KVQ8_DEC_KMFMA && FMT != KV_FMT_F16; }
+constexpr int QLEV = 3;
+constexpr float QBASE_INV = 1.f / 254.f;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// one int8 level of a value: clamp(rint(r / s)), and the residual it leaves
+__device__ __forceinline__ int q_level(float& r, float s) {
+  const float a = fminf(fmaxf(rintf(r / s), -127.f), 127.f);
+  r = fmaf(-a, s, r);
+  return (int)a;
+}
+
+// A K batch for the matrix-core pass: U 8-token steps as U/2 blocks of 16 tokens;
+// per block and group, lane l holds the 16 codes of token n = l % 16 at dims
+// 64 * group + 16 * (l / 16) .. + 15 and that token's group scale.  Token n of block
+// j is row n % 8 of step k + 2j + n / 8, so its logit goes where the 8-lane layout
+// of the other passes expects it.
+template <int U>
+struct KBatch {
+  static_assert(U % 2 == 0, "blocks of 16 tokens are pairs of steps");
+  u32x4 w[U / 2][2];
+  uint16_t sc[U / 2][2];
+  __device__ __forceinline__ void load(const char* kb, const char* ksb, int gw, int W, int k,
+                                       int len, int lane, int kmax = 1 << 30) {
+    const int n = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < U / 2; ++j) {
+      const uint32_t row =
+          (uint32_t)min((gw + min(k + 2 * j + (n >> 3), kmax) * W) * 8 + (n & 7), len - 1);
+#pragma unroll
+      for (int grp = 0; grp < NGRP; ++grp) {
+        w[j][grp] = ldkv(kb, row * HD + grp * 64 + kq * 16);
+        sc[j][grp] = ldg16(ksb + (row * NGRP + grp) * 2);
+      }
+    }
+  }
+};
+
 // LDS of one split workgroup: per-wave logits (ch0 + ch1 = 2 ch_steps per pair of
 // waves sharing a SIMD, whatever the format), the wave partials (o, m, l) and one
 // discarded-store slot per lane
@@ -296,7 +371,10 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     const float* __restrict__ q, float qscale, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, int S) {
   constexpr int CH0 = ch0<FMT, G>(), CH1 = ch1<FMT, G>();
+  constexpr int UK = k_batch_rows<G>();
   static_assert(CH0 % (2 * U) == 0 && CH1 % (2 * U) == 0, "a chunk holds whole pairs of load batches");
+  static_assert(!kmfma<FMT>() || (CH0 % (2 * UK) == 0 && CH1 % (2 * UK) == 0),
+                "a chunk holds whole pairs of K batches");
   static_assert(CH0 >= KVQ8_DEC_MIN_STEPS && (!GROUPED || CH1 >= KVQ8_DEC_MIN_STEPS),
                 "a short session's waves (at most KVQ8_DEC_MIN_STEPS steps) fit the logits budget");
   const int s_idx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -346,15 +424,70 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
 
   if (n_steps > 0) {
     const int hsel = head_map<G>(c);
-    float qv[G][16];  // slot g: head g ^ hsel
+    constexpr bool MF = kmfma<FMT>();
+    float qv[G][16];  // slot g: head g ^ hsel (the vector K pass)
+    if constexpr (!MF) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float* qp = q + ((long long)b * nqh + h * G + (g ^ hsel)) * HD;
+      for (int g = 0; g < G; ++g) {
+        const float* qp = q + ((long long)b * nqh + h * G + (g ^ hsel)) * HD;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const u32x4 v = ldg128(qp + lane_dim<FMT>(c, 4 * k));   // 4 consecutive dims
+        for (int k = 0; k < 4; ++k) {
+          const u32x4 v = ldg128(qp + lane_dim<FMT>(c, 4 * k));   // 4 consecutive dims
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qv[g][4 * k + e] = as_f32(v[e]) * qscale;
+          for (int e = 0; e < 4; ++e) qv[g][4 * k + e] = as_f32(v[e]) * qscale;
+        }
+      }
+    }
+    // matrix-core K pass: A operands (per block of 4 heads and group) and the level
+    // scales of the head whose logits this lane receives
+    constexpr int NHB = G > 4 ? 2 : 1;
+    i32x4 aq[MF ? NHB : 1][NGRP];
+    float qs[MF ? NHB : 1][NGRP][QLEV];
+    if constexpr (MF) {
+      const int m = lane & 15, kq = lane >> 4;
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        const int ga = hb * 4 + (m >> 2), lev = m & 3;   // this lane's A row: head, level
+#pragma unroll
+        for (int grp = 0; grp < NGRP; ++grp) {
+          const float* qp =
+              q + ((long long)b * nqh + h * G + min(ga, G - 1)) * HD + grp * 64 + kq * 16;
+          float x[16];
+          float mx = 0.f;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const u32x4 v = ldg128(qp + 4 * k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[4 * k + e] = as_f32(v[e]) * qscale;
+              mx = fmaxf(mx, fabsf(x[4 * k + e]));
+            }
+          }
+          // lanes m, m + 16, m + 32, m + 48 hold the group's 64 dims
+          mx = fmaxf(mx, shfl_xor(mx, 16));
+          mx = fmaxf(mx, shfl_xor(mx, 32));
+          float sl[QLEV];
+          sl[0] = mx > 0.f ? mx / 127.f : 1.f;   // an all-zero group: any s, levels 0
+#pragma unroll
+          for (int l = 1; l < QLEV; ++l) sl[l] = sl[l - 1] * QBASE_INV;
+          const bool live = ga < G && lev < QLEV;
+          uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float rr = x[i];
+            int a = 0;
+#pragma unroll
+            for (int l = 0; l < QLEV; ++l) {
+              const int al = q_level(rr, sl[l]);
+              a = l == lev ? al : a;
+            }
+            wd[i >> 2] |= (uint32_t)((live ? a : 0) & 0xFF) << (8 * (i & 3));
+          }
+          aq[hb][grp] = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+          // lane 4 * kq holds row 4 * kq (head hb * 4 + kq, level 0): its scales
+#pragma unroll
+          for (int l = 0; l < QLEV; ++l) qs[hb][grp][l] = __shfl(sl[l], 4 * kq, 64);
+        }
       }
     }
     // U x G independent dot products, interleaved so that no FMA waits on the one
@@ -362,7 +495,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     // a lane holds head j ^ hsel (see head_map), so the reduction folds: each DPP
     // stage adds the partner's upper slots to this lane's lower ones and halves
     // the values carried (4 DPP adds per step for G = 4 instead of 12).
-    auto kstep = [&](const Batch<FMT, U>& cur, int k0, int it0, int n_it) {
+    auto kstep = [&](const Batch<FMT, U>& cur, int k0, int it0, int n_it) __attribute__((always_inline)) {
       float part[U][G];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -401,7 +534,34 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
         *dst = part[u][0];
       }
     };
-    auto vstep = [&](const Batch<FMT, U>& cur, int it0, int n_it) {
+    // matrix-core K step: per block of 16 tokens, per group of 4 heads, one product
+    // per scale group; lane l turns the level sums of (head, token l % 16) into the
+    // logit, sum over groups of K scale x (A s0 + B s1 + C s2)
+    auto kstep_m = [&](const KBatch<UK>& cur, int it0) __attribute__((always_inline)) {
+      if constexpr (MF) {
+#pragma unroll
+        for (int j = 0; j < UK / 2; ++j) {
+#pragma unroll
+          for (int hb = 0; hb < NHB; ++hb) {
+            float v = 0.f;
+#pragma unroll
+            for (int grp = 0; grp < NGRP; ++grp) {
+              const u32x4& bw = cur.w[j][grp];
+              const i32x4 bk = i32x4{(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3]};
+              const i32x4 d =
+                  __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[hb][grp], bk, i32x4{0, 0, 0, 0}, 0, 0, 0);
+              const float lv = fmaf((float)d[2], qs[hb][grp][2],
+                                    fmaf((float)d[1], qs[hb][grp][1], (float)d[0] * qs[hb][grp][0]));
+              v = fmaf(lv, h2f(cur.sc[j][grp]), v);
+            }
+            const int g = hb * 4 + (lane >> 4);
+            float* dst = g < G ? lg + ((it0 + 2 * j) * 8 + (lane & 15)) * G + g : junk + lane;
+            *dst = v;
+          }
+        }
+      }
+    };
+    auto vstep = [&](const Batch<FMT, U>& cur, int it0, int n_it) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int it = it0 + u;
@@ -446,50 +606,87 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     // softmax.  The plan gives every wave at most its group's budget (CH0 or CH1) of steps.
     const int n_it = n_steps;
     Batch<FMT, U> A, B;
-    A.template load<false>(kb, ksb, gw, W, 0, len, r, c);
-    // ---- K pass ---------------------------------------------------------------
-    for (int it0 = 0; it0 < n_it; it0 += 2 * U) {
-      B.template load<false>(kb, ksb, gw, W, it0 + U, len, r, c);
-      kstep(A, 0, it0, n_it);
-      if (it0 + 2 * U < n_it)
-        A.template load<false>(kb, ksb, gw, W, it0 + 2 * U, len, r, c);
-      else
-        A.template load<true>(vb, vsb, gw, W, 0, len, r, c);
-      kstep(B, 0, it0 + U, n_it);
-    }
-    wave_lds_fence();
-    // ---- softmax over the wave's tokens ---------------------------------------
-    const int n_loc = n_it * 8;
-    const int n_pad = (n_it + 2 * U - 1) / (2 * U) * (2 * U);
-    for (int tl = lane; tl < n_loc; tl += 64) {
-      const int t = (gw + (tl >> 3) * W) * 8 + (tl & 7);
-      if (t < len) {
+    // Softmax of the logits of steps [s0, s1): the running max m moves to cover them,
+    // l and the accumulators are rescaled to it, and p = 2^(logit - m) replaces each
+    // logit; slots up to s_pad (the V pass reads whole pairs of batches) get p = 0.
+    auto softmax = [&](int s0, int s1, int s_pad) __attribute__((always_inline)) {
+      float mc[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) m[g] = fmaxf(m[g], lg[tl * G + g]);
+      for (int g = 0; g < G; ++g) mc[g] = -INFINITY;
+      for (int tl = s0 * 8 + lane; tl < s1 * 8; tl += 64) {
+        const int t = (gw + (tl >> 3) * W) * 8 + (tl & 7);
+        if (t < len) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) mc[g] = fmaxf(mc[g], lg[tl * G + g]);
+        }
       }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) m[g] = wave_max(m[g]);   // finite: step 0 has token gw*8
-    for (int tl = lane; tl < n_pad * 8; tl += 64) {
-      const int t = (gw + (tl >> 3) * W) * 8 + (tl & 7);
-      const bool ok = tl < n_loc && t < len;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float p = ok ? exp2f(lg[tl * G + g] - m[g]) : 0.f;
-        lg[tl * G + g] = p;
-        l[g] += p;
+        // finite: every step of the wave holds a token below len
+        const float mn = fmaxf(m[g], wave_max(mc[g]));
+        const float f = exp2f(m[g] - mn);   // 0 on the first chunk (m = -inf)
+        m[g] = mn;
+        l[g] *= f;
+        accw[g] *= f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[g][i] *= f;
       }
+      for (int tl = s0 * 8 + lane; tl < s_pad * 8; tl += 64) {
+        const int t = (gw + (tl >> 3) * W) * 8 + (tl & 7);
+        const bool ok = tl < s1 * 8 && t < len;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float p = ok ? exp2f(lg[tl * G + g] - m[g]) : 0.f;
+          lg[tl * G + g] = p;
+          l[g] += p;
+        }
+      }
+    };
+    auto vpass = [&](int s0, int s1) __attribute__((always_inline)) {
+      for (int it0 = s0; it0 < s1; it0 += 2 * U) {
+        B.template load<true>(vb, vsb, gw, W, it0 + U, len, r, c);
+        vstep(A, it0, n_it);
+        if (it0 + 2 * U < s1) A.template load<true>(vb, vsb, gw, W, it0 + 2 * U, len, r, c);
+        vstep(B, it0 + U, n_it);
+      }
+    };
+    if constexpr (MF) {
+      // ---- K pass on the matrix cores ------------------------------------------
+      KBatch<UK> KA, KB;
+      KA.load(kb, ksb, gw, W, 0, len, lane);
+      for (int it0 = 0; it0 < n_it; it0 += 2 * UK) {
+        KB.load(kb, ksb, gw, W, it0 + UK, len, lane);
+        kstep_m(KA, it0);
+        if (it0 + 2 * UK < n_it) KA.load(kb, ksb, gw, W, it0 + 2 * UK, len, lane);
+        kstep_m(KB, it0 + UK);
+      }
+      // the first V batch after the loop: its registers are then not live across it
+      A.template load<true>(vb, vsb, gw, W, 0, len, r, c);
+      wave_lds_fence();
+      softmax(0, n_it, (n_it + 2 * U - 1) / (2 * U) * (2 * U));
+      wave_lds_fence();
+      // ---- V pass ---------------------------------------------------------------
+      vpass(0, n_it);
+    } else {
+      // ---- K pass ---------------------------------------------------------------
+      A.template load<false>(kb, ksb, gw, W, 0, len, r, c);
+      for (int it0 = 0; it0 < n_it; it0 += 2 * U) {
+        B.template load<false>(kb, ksb, gw, W, it0 + U, len, r, c);
+        kstep(A, 0, it0, n_it);
+        if (it0 + 2 * U < n_it)
+          A.template load<false>(kb, ksb, gw, W, it0 + 2 * U, len, r, c);
+        else
+          A.template load<true>(vb, vsb, gw, W, 0, len, r, c);
+        kstep(B, 0, it0 + U, n_it);
+      }
+      wave_lds_fence();
+      softmax(0, n_it, (n_it + 2 * U - 1) / (2 * U) * (2 * U));
+      wave_lds_fence();
+      // ---- V pass ---------------------------------------------------------------
+      vpass(0, n_it);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) l[g] = wave_sum(l[g]);
-    wave_lds_fence();
-    // ---- V pass ---------------------------------------------------------------
-    for (int it0 = 0; it0 < n_it; it0 += 2 * U) {
-      B.template load<true>(vb, vsb, gw, W, it0 + U, len, r, c);
-      vstep(A, it0, n_it);
-      if (it0 + 2 * U < n_it) A.template load<true>(vb, vsb, gw, W, it0 + 2 * U, len, r, c);
-      vstep(B, it0 + U, n_it);
-    }
     if constexpr (FMT == KV_FMT_K8V4) {  // sum_t w_t (n - 8) = sum_t w_t n - 8 sum_t w_t
 #pragma unroll
       for (int g = 0; g < G; ++g)
@@ -527,6 +724,336 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < DEC_WAVES; ++w) {
+      const float mw = m_l[w * G + g];
+      if (mw == -INFINITY) continue;
+      const float f = exp2f(mw - M);
+      L += l_l[w * G + g] * f;
+      O += o_l[(w * G + g) * HD + d] * f;
+    }
+    const long long qrow = ((long long)b * nqh + h * G + g) * S + s_idx;
+    ws_o[qrow * HD + d] = O / L;
+    if (d == 0) ws_lse[qrow] = M + log2f(L);
+  }
+}
+
+// k_decode_pair: the int8-K formats (q8, K8V4), with the waves of a workgroup in
+//   4 pairs.  A SIMD runs one pair: a V wave (waves 0-3, the older of the two, which
+//   the arbiter favours) and a K wave (waves 4-7) that share the pair's steps,
+//   gw, gw + W, gw + 2W, ... (W = 4 x the active splits), in chunks of PAIR_CH
+//   steps.  The K wave streams the K codes, computes the chunk's logits on the
+//   matrix cores and its softmax (running max m, rescale factor f, p = 2^(logit - m),
+//   running sum l) into one of two LDS buffers; the V wave, one chunk behind,
+//   rescales its accumulators by f and streams the V rows against p.  One workgroup
+//   barrier per chunk hands a buffer from the K wave to the V wave and back.  Each
+//   wave keeps one kind of load in flight all the time, and the V wave's arithmetic
+//   overlaps the K wave's loads on the same SIMD.
+#ifndef KVQ8_DEC_PAIR
+#define KVQ8_DEC_PAIR 1
+#endif
+#ifndef KVQ8_DEC_PAIR_CH
+#define KVQ8_DEC_PAIR_CH 16
+#endif
+// waves per SIMD the pair kernel's registers must allow (4: two workgroups per CU)
+#ifndef KVQ8_DEC_PAIR_WPE
+#define KVQ8_DEC_PAIR_WPE 4
+#endif
+constexpr int PAIRS = DEC_WAVES / 2;
+constexpr int PAIR_CH = KVQ8_DEC_PAIR_CH;
+// fewest steps a pair of a split is planned to take (the plan's cap on splits)
+constexpr int PAIR_MIN_STEPS = 32;
+// steps per pair the plan aims for at most, so that long sessions spread over many
+// workgroups (balance across CUs and sessions)
+constexpr int PAIR_TARGET_STEPS = 256;
+
+template <int G>
+__host__ __device__ constexpr size_t pair_lds_bytes() {
+  return sizeof(float) * ((size_t)PAIRS * 2 * PAIR_CH * 8 * G + PAIRS * 2 * G + PAIRS * G * HD +
+                          2 * PAIRS * G + DEC_WAVES * 64);
+}
+static_assert(pair_lds_bytes<8>() <= 160 * 1024, "a pair workgroup fits in one CU's LDS");
+
+template <int FMT, int G, int U>
+__global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 2 : KVQ8_DEC_PAIR_WPE))) void k_decode_pair(
+    const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int kvh,
+    const float* __restrict__ q, float qscale, float* __restrict__ ws_o,
+    float* __restrict__ ws_lse, int S) {
+  static_assert(FMT != KV_FMT_F16, "the pair kernel reads int8 K codes");
+  constexpr int UK = k_batch_rows<G>();
+  static_assert(PAIR_CH % (2 * UK) == 0 && PAIR_CH % (2 * U) == 0,
+                "a chunk holds whole pairs of K and of V batches");
+  constexpr int NHB = G > 4 ? 2 : 1;
+  const int s_idx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nqh = kvh * G;
+  const kv_session ss = tab[b];
+  const int len = lens[b];
+  // workgroup-uniform exits only (the loop below has barriers)
+  if (session_bad(ss, FMT) || len < 0 || len > ss.cap || len > max_len) return;  // merge flags
+  const int J = (len + 7) >> 3;
+  const int Sb = active_splits<FMT>(len, S);
+  if (s_idx >= Sb) return;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int r = lane >> 3, c = lane & 7;
+  const bool kw = wave >= PAIRS;                 // the K wave of its pair
+  const int pr = wave & (PAIRS - 1);
+  const int gw = s_idx * PAIRS + pr;             // first step of the pair
+  const int W = Sb * PAIRS;
+  const int n_steps = gw < J ? (J - 1 - gw) / W + 1 : 0;
+  const int n_first = s_idx * PAIRS < J ? (J - 1 - s_idx * PAIRS) / W + 1 : 0;  // pair 0's
+  const int n_chunks = (n_first + PAIR_CH - 1) / PAIR_CH;   // the same for every wave
+
+  extern __shared__ float smem[];
+  float* pb = smem + (size_t)pr * 2 * PAIR_CH * 8 * G;      // this pair's two chunk buffers
+  float* fb = smem + (size_t)PAIRS * 2 * PAIR_CH * 8 * G + pr * 2 * G;   // [2][G] factors
+  float* o_l = smem + (size_t)PAIRS * 2 * PAIR_CH * 8 * G + PAIRS * 2 * G;   // [pairs][G][HD]
+  float* m_l = o_l + PAIRS * G * HD;             // [pairs][G]
+  float* l_l = m_l + PAIRS * G;                  // [pairs][G]
+  float* junk = l_l + PAIRS * G + wave * 64;     // discarded stores
+
+  constexpr int VB = FMT == KV_FMT_K8V4 ? HD / 2 : HD;   // bytes per V row
+  constexpr int VSC = FMT == KV_FMT_K8V4 ? NQ4 : NGRP;    // V scales per row
+  const size_t hrow = (size_t)h * (size_t)ss.cap;
+  const char* kb = static_cast<const char*>(ss.k) + hrow * HD;
+  const char* vb = static_cast<const char*>(ss.v) + hrow * VB;
+  const char* ksb = reinterpret_cast<const char*>(ss.k_scale) + hrow * NGRP * 2;
+  const char* vsb = reinterpret_cast<const char*>(ss.v_scale) + hrow * VSC * 2;
+
+  float m[G], l[G];           // K wave: running max (wave-uniform), lane sums of p
+  float acc[G][16], accw[G];  // V wave
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+    accw[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
+  }
+
+  if (kw) {
+    // ================= K wave ===================================================
+    i32x4 aq[NHB][NGRP];
+    float qs[NHB][NGRP][QLEV];
+    {
+      const int mrow = lane & 15, kq = lane >> 4;
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) {
+        const int ga = hb * 4 + (mrow >> 2), lev = mrow & 3;   // this lane's A row
+#pragma unroll
+        for (int grp = 0; grp < NGRP; ++grp) {
+          const float* qp =
+              q + ((long long)b * nqh + h * G + min(ga, G - 1)) * HD + grp * 64 + kq * 16;
+          float x[16];
+          float mx = 0.f;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const u32x4 v = ldg128(qp + 4 * k);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[4 * k + e] = as_f32(v[e]) * qscale;
+              mx = fmaxf(mx, fabsf(x[4 * k + e]));
+            }
+          }
+          mx = fmaxf(mx, shfl_xor(mx, 16));
+          mx = fmaxf(mx, shfl_xor(mx, 32));
+          float sl[QLEV];
+          sl[0] = mx > 0.f ? mx / 127.f : 1.f;
+#pragma unroll
+          for (int lv = 1; lv < QLEV; ++lv) sl[lv] = sl[lv - 1] * QBASE_INV;
+          const bool live = ga < G && lev < QLEV;
+          uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float rr = x[i];
+            int a = 0;
+#pragma unroll
+            for (int lv = 0; lv < QLEV; ++lv) {
+              const int al = q_level(rr, sl[lv]);
+              a = lv == lev ? al : a;
+            }
+            wd[i >> 2] |= (uint32_t)((live ? a : 0) & 0xFF) << (8 * (i & 3));
+          }
+          aq[hb][grp] = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+#pragma unroll
+          for (int lv = 0; lv < QLEV; ++lv) qs[hb][grp][lv] = __shfl(sl[lv], 4 * kq, 64);
+        }
+      }
+    }
+    // logits of the 16-token blocks of a batch whose first step is k (chunk-relative
+    // k - c0) into the chunk buffer lc
+    auto kstep = [&](const KBatch<UK>& cur, float* lc, int kr) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < UK / 2; ++j) {
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+          float v = 0.f;
+#pragma unroll
+          for (int grp = 0; grp < NGRP; ++grp) {
+            const u32x4& bw = cur.w[j][grp];
+            const i32x4 bk = i32x4{(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3]};
+            const i32x4 d =
+                __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[hb][grp], bk, i32x4{0, 0, 0, 0}, 0, 0, 0);
+            const float lv = fmaf((float)d[2], qs[hb][grp][2],
+                                  fmaf((float)d[1], qs[hb][grp][1], (float)d[0] * qs[hb][grp][0]));
+            v = fmaf(lv, h2f(cur.sc[j][grp]), v);
+          }
+          const int g = hb * 4 + (lane >> 4);
+          float* dst = g < G ? lc + ((kr + 2 * j) * 8 + (lane & 15)) * G + g : junk + lane;
+          *dst = v;
+        }
+      }
+    };
+    // One loop over the chunks' steps, the same count for every wave of the
+    // workgroup; loads run on across chunk ends (steps past the pair's last one
+    // re-read it), and each chunk ends with its softmax and a barrier.
+    const int kmax = max(n_steps - 1, 0);
+    const int total = n_chunks * PAIR_CH;
+    KBatch<UK> KA, KB;
+    if (total > 0) KA.load(kb, ksb, gw, W, 0, len, lane, kmax);
+    for (int k0 = 0; k0 < total; k0 += 2 * UK) {
+      const int ch = k0 / PAIR_CH, kr = k0 - ch * PAIR_CH;
+      float* lc = pb + (ch & 1) * PAIR_CH * 8 * G;
+      KB.load(kb, ksb, gw, W, k0 + UK, len, lane, kmax);
+      kstep(KA, lc, kr);
+      KA.load(kb, ksb, gw, W, k0 + 2 * UK, len, lane, kmax);
+      kstep(KB, lc, kr + UK);
+      if (kr + 2 * UK == PAIR_CH) {
+        wave_lds_fence();
+        // softmax of the chunk: the max moves to cover it, l is rescaled, p replaces
+        // each logit (0 past the pair's last step, so the V wave may run whole chunks)
+        const int c0 = ch * PAIR_CH;
+        const int nl = max(0, min(n_steps, c0 + PAIR_CH) - c0) * 8;
+        float mc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) mc[g] = -INFINITY;
+        for (int tl = lane; tl < nl; tl += 64) {
+          const int t = (gw + (c0 + (tl >> 3)) * W) * 8 + (tl & 7);
+          if (t < len) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) mc[g] = fmaxf(mc[g], lc[tl * G + g]);
+          }
+        }
+        float* fc = fb + (ch & 1) * G;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float mn = fmaxf(m[g], wave_max(mc[g]));
+          // 0 on the pair's first chunk (m = -inf); 1 while the pair has no token yet
+          const float f = mn == -INFINITY ? 1.f : exp2f(m[g] - mn);
+          m[g] = mn;
+          l[g] *= f;
+          if (lane == g) fc[g] = f;
+        }
+        for (int tl = lane; tl < PAIR_CH * 8; tl += 64) {
+          const int t = (gw + (c0 + (tl >> 3)) * W) * 8 + (tl & 7);
+          const bool ok = tl < nl && t < len;
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            const float pv = ok ? exp2f(lc[tl * G + g] - m[g]) : 0.f;
+            lc[tl * G + g] = pv;
+            l[g] += pv;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    __syncthreads();   // the V wave's last chunk
+#pragma unroll
+    for (int g = 0; g < G; ++g) l[g] = wave_sum(l[g]);
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        m_l[pr * G + g] = m[g];
+        l_l[pr * G + g] = l[g];
+      }
+    }
+  } else {
+    // ================= V wave ===================================================
+    auto vstep = [&](const Batch<FMT, U>& cur, const float* pc, int kr) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float sc = cur.scale(u);
+        float w[G];
+        load_p<G>(pc + ((kr + u) * 8 + r) * G, w);
+#pragma unroll
+        for (int g = 0; g < G; ++g) w[g] *= sc;
+        if constexpr (FMT == KV_FMT_K8V4) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) accw[g] += w[g];
+          const u32x4& cw = cur.ch[u].w;
+          const uint32_t nb[4] = {nibble_bytes(cw[0]), nibble_bytes(cw[0] >> 4),
+                                  nibble_bytes(cw[1]), nibble_bytes(cw[1] >> 4)};
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const uint32_t src = nb[2 * (i >> 3) + (i & 1)];
+            const float vf = (float)((src >> (8 * ((i & 7) >> 1))) & 0xFFu);   // code + 8
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g][i] = fmaf(w[g], vf, acc[g][i]);
+          }
+        } else {
+          const u32x4& cw = cur.ch[u].w;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float vf = i8_to_f32(cw[i >> 2], i & 3);
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g][i] = fmaf(w[g], vf, acc[g][i]);
+          }
+        }
+      }
+    };
+    // the same single loop, one chunk behind the K wave
+    const int kmax = max(n_steps - 1, 0);
+    const int total = n_chunks * PAIR_CH;
+    Batch<FMT, U> A, B;
+    if (total > 0) A.template load<true>(vb, vsb, gw, W, 0, len, r, c, kmax);
+    __syncthreads();   // the K wave's first chunk
+    for (int k0 = 0; k0 < total; k0 += 2 * U) {
+      const int ch = k0 / PAIR_CH, kr = k0 - ch * PAIR_CH;
+      const float* pc = pb + (ch & 1) * PAIR_CH * 8 * G;
+      if (kr == 0) {
+        if (ch > 0) __syncthreads();   // the K wave's chunk ch
+        const float* fc = fb + (ch & 1) * G;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float f = fc[g];
+          accw[g] *= f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[g][i] *= f;
+        }
+      }
+      B.template load<true>(vb, vsb, gw, W, k0 + U, len, r, c, kmax);
+      vstep(A, pc, kr);
+      A.template load<true>(vb, vsb, gw, W, k0 + 2 * U, len, r, c, kmax);
+      vstep(B, pc, kr + U);
+    }
+    if (total > 0) __syncthreads();   // frees the K wave's last buffer
+    if constexpr (FMT == KV_FMT_K8V4) {  // sum_t w_t (n - 8) = sum_t w_t n - 8 sum_t w_t
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[g][i] = fmaf(-8.f, accw[g], acc[g][i]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[g][i] = sum_rows8(acc[g][i]);
+    if (r == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < 16; i += 4)
+          *reinterpret_cast<float4*>(o_l + (pr * G + g) * HD + lane_dim<FMT>(c, i)) =
+              make_float4(acc[g][i], acc[g][i + 1], acc[g][i + 2], acc[g][i + 3]);
+    }
+  }
+  // ---- combine the pair partials of the workgroup ----------------------------
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * HD; idx += DEC_THREADS) {
+    const int g = idx / HD, d = idx % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < PAIRS; ++w) M = fmaxf(M, m_l[w * G + g]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < PAIRS; ++w) {
       const float mw = m_l[w * G + g];
       if (mw == -INFINITY) continue;
       const float f = exp2f(mw - M);
@@ -624,6 +1151,10 @@ constexpr int batch_rows() {
   return FMT != KV_FMT_F16 ? (G >= 8 ? 2 : KVQ8_DEC_U_Q8) : KVQ8_DEC_U_F16;
 }
 
+template <int FMT>
+constexpr bool use_pair() { return KVQ8_DEC_PAIR && FMT != KV_FMT_F16; }
+
+
 // Split workgroups of one kernel instance that fit on the current device at once
 // (CUs x resident workgroups per CU), cached per device; 0 when unknown.
 template <int FMT, int G>
@@ -634,9 +1165,14 @@ int resident_splits() {
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v > 0) return v;
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, k_decode_split<FMT, G, batch_rows<FMT, G>()>, DEC_THREADS,
-          split_lds_bytes<G>()) != hipSuccess ||
+  hipError_t e;
+  if constexpr (use_pair<FMT>())
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, k_decode_pair<FMT, G, batch_rows<FMT, G>()>, DEC_THREADS, pair_lds_bytes<G>());
+  else
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, k_decode_split<FMT, G, batch_rows<FMT, G>()>, DEC_THREADS, split_lds_bytes<G>());
+  if (e != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
   v = per_cu * cus;
@@ -668,10 +1204,14 @@ hipError_t launch_g(const kv_session* tab, const int32_t* lens, int n_sess, int 
                     const float* q, float sm_scale, float* out, float* ws_o, float* ws_lse,
                     const DecodePlan& plan, int32_t* status, hipStream_t st) {
   constexpr int U = batch_rows<FMT, G>();
-  static_assert(U == 1 || U == 2 || U == 4, "U must divide the group budgets / 2");
+  static_assert(U == 1 || U == 2 || U == 4 || U == 8, "U must divide the group budgets / 2");
   dim3 grid(plan.S, kvh, n_sess), block(DEC_THREADS);
-  hipLaunchKernelGGL((k_decode_split<FMT, G, U>), grid, block, split_lds_bytes<G>(), st, tab, lens,
-                     max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S);
+  if constexpr (use_pair<FMT>())
+    hipLaunchKernelGGL((k_decode_pair<FMT, G, U>), grid, block, pair_lds_bytes<G>(), st, tab,
+                       lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S);
+  else
+    hipLaunchKernelGGL((k_decode_split<FMT, G, U>), grid, block, split_lds_bytes<G>(), st, tab,
+                       lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_rows = n_sess * kvh * G;
@@ -704,16 +1244,25 @@ DecodePlan decode_plan(int fmt, int kvh, int nqh, int n_sess, int max_len) {
 #undef KVQ8_CHB
   if (CH0 <= 0) CH0 = 1;  // unsupported G: rejected before any launch
   const long long P = (long long)kvh * n_sess;
-  // S0 keeps every wave within its group's LDS budget of logits (CH0 or CH1 steps)
-  long long S0 = std::max(1LL, (Jf + GRP_WAVES * CH0 - 1) / (GRP_WAVES * CH0));
-  if (CH1 > 0) S0 = std::max(S0, (J1 + GRP_WAVES * CH1 - 1) / (GRP_WAVES * CH1));
+  long long S0, Smax;
+  if (q8 && KVQ8_DEC_PAIR) {
+    // pairs take any number of steps (in chunks): aim at most PAIR_TARGET_STEPS per
+    // pair, and at least PAIR_MIN_STEPS
+    S0 = std::max(1LL, (J + PAIRS * PAIR_TARGET_STEPS - 1) / (PAIRS * PAIR_TARGET_STEPS));
+    Smax = std::max(S0, J / (PAIRS * PAIR_MIN_STEPS));
+  } else {
+    // every wave within its group's LDS budget of logits (CH0 or CH1 steps)
+    S0 = std::max(1LL, (Jf + GRP_WAVES * CH0 - 1) / (GRP_WAVES * CH0));
+    if (CH1 > 0) S0 = std::max(S0, (J1 + GRP_WAVES * CH1 - 1) / (GRP_WAVES * CH1));
+    Smax = std::max(S0, (Jf + GRP_WAVES - 1) / GRP_WAVES);
+  }
   long long S = S0;
   const long long C = resident(fmt, nqh / kvh);
   if (C > 0) {
     const long long rounds = (P * S0 + C - 1) / C;
     S = std::max(S0, (rounds * C + P - 1) / P);
   }
-  S = std::min(S, std::max(S0, (Jf + GRP_WAVES - 1) / GRP_WAVES));
+  S = std::min(S, Smax);
   DecodePlan p;
   p.S = (int)S;
   const size_t rows = (size_t)n_sess * nqh * p.S;
