@@ -908,13 +908,14 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
     const int kmax = max(n_steps - 1, 0);
     const int total = n_chunks * PAIR_CH;
     KBatch<UK> KA, KB;
-    if (total > 0) KA.load(kb, ksb, gw, W, 0, len, lane, kmax);
-    for (int k0 = 0; k0 < total; k0 += 2 * UK) {
+    // the loop body; pf: prefetch the next batch (not on the last iteration, so no
+    // load past the loop is issued)
+    auto kiter = [&](int k0, bool pf) __attribute__((always_inline)) {
       const int ch = k0 / PAIR_CH, kr = k0 - ch * PAIR_CH;
       float* lc = pb + (ch & 1) * PAIR_CH * 8 * G;
       KB.load(kb, ksb, gw, W, k0 + UK, len, lane, kmax);
       kstep(KA, lc, kr);
-      KA.load(kb, ksb, gw, W, k0 + 2 * UK, len, lane, kmax);
+      if (pf) KA.load(kb, ksb, gw, W, k0 + 2 * UK, len, lane, kmax);
       kstep(KB, lc, kr + UK);
       if (kr + 2 * UK == PAIR_CH) {
         wave_lds_fence();
@@ -954,6 +955,12 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
         }
         __syncthreads();
       }
+    };
+    if (total > 0) {
+      KA.load(kb, ksb, gw, W, 0, len, lane, kmax);
+      int k0 = 0;
+      for (; k0 + 2 * UK < total; k0 += 2 * UK) kiter(k0, true);
+      kiter(k0, false);
     }
     __syncthreads();   // the V wave's last chunk
 #pragma unroll
@@ -1003,9 +1010,7 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
     const int kmax = max(n_steps - 1, 0);
     const int total = n_chunks * PAIR_CH;
     Batch<FMT, U> A, B;
-    if (total > 0) A.template load<true>(vb, vsb, gw, W, 0, len, r, c, kmax);
-    __syncthreads();   // the K wave's first chunk
-    for (int k0 = 0; k0 < total; k0 += 2 * U) {
+    auto viter = [&](int k0, bool pf) __attribute__((always_inline)) {
       const int ch = k0 / PAIR_CH, kr = k0 - ch * PAIR_CH;
       const float* pc = pb + (ch & 1) * PAIR_CH * 8 * G;
       if (kr == 0) {
@@ -1021,8 +1026,15 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
       }
       B.template load<true>(vb, vsb, gw, W, k0 + U, len, r, c, kmax);
       vstep(A, pc, kr);
-      A.template load<true>(vb, vsb, gw, W, k0 + 2 * U, len, r, c, kmax);
+      if (pf) A.template load<true>(vb, vsb, gw, W, k0 + 2 * U, len, r, c, kmax);
       vstep(B, pc, kr + U);
+    };
+    if (total > 0) A.template load<true>(vb, vsb, gw, W, 0, len, r, c, kmax);
+    __syncthreads();   // the K wave's first chunk
+    if (total > 0) {
+      int k0 = 0;
+      for (; k0 + 2 * U < total; k0 += 2 * U) viter(k0, true);
+      viter(k0, false);
     }
     if (total > 0) __syncthreads();   // frees the K wave's last buffer
     if constexpr (FMT == KV_FMT_K8V4) {  // sum_t w_t (n - 8) = sum_t w_t n - 8 sum_t w_t
