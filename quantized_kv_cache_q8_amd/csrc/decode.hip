@@ -23,10 +23,16 @@
 //   written as one (o, lse) per query head and split (o normalised, lse in log2).
 //   Offsets are 32-bit, from per-head base pointers (a head holds at most 2^24
 //   cells).
+// k_decode_pair (the int8-K formats): the same splits, with the K logits on the
+//   matrix cores and the waves in pairs, one streaming K and one streaming V per
+//   SIMD (described at the kernel).  k_decode_split serves FP16 (and the int8
+//   formats when KVQ8_DEC_PAIR is 0).
 // k_decode_merge: out = sum_j 2^(lse_j - L) o_j with L = log2 sum_j 2^lse_j.
 //
 // Dequantised values are exact in fp32 (a 7-bit code times an 11-bit fp16
-// significand), so the only rounding is fp32 accumulation.
+// significand); the int8 K logits are exact integer sums of the codes against a
+// three-level int8 split of the query (residual about 2^-24 of the query); the rest
+// of the rounding is fp32 accumulation.
 #include <algorithm>
 #include <atomic>
 
