@@ -37,6 +37,7 @@ extern "C" {
 typedef enum { KV_FMT_F16 = 0, KV_FMT_Q8 = 1, KV_FMT_K8V4 = 2 } kv_fmt;
 
 #define KV_GROUP 64    /* dims per FP16 scale of the int8 codes [P1, Summary] */
+#define KV_PAGE_ROWS 64 /* cells per page of a paged session (kv_decode_attn_paged) */
 #define KV_Q4_BLOCK 32 /* values per FP16 scale of the K8V4 V codes [P3, What] */
 
 typedef struct {
@@ -80,14 +81,16 @@ enum {
   KV_ERR_WORKSPACE = -5,   /* workspace null or smaller than the *_workspace_bytes value */
   KV_ERR_RANGE = -6,       /* rows outside [0, cap), or cap above 2^24 (host-checkable cases) */
   KV_ERR_HIP = -7,         /* a kernel launch or copy failed */
-  KV_ERR_IMAGE = -8        /* a saved image refused: magic, version, format, shape or size */
+  KV_ERR_IMAGE = -8,       /* a saved image refused: magic, version, format, shape or size */
+  KV_ERR_WINDOW = -9       /* window state missing, too small or not initialised */
 };
 
 /* bits OR-ed into *d_status by kernels */
 enum {
-  KV_DEV_RANGE = 1,      /* len < 0, len + n_tok > cap (append), len > max_len or cap (decode) */
-  KV_DEV_BAD_SESSION = 2 /* table entry with null/unaligned pointers, scales inconsistent with
-                            the format, or cap not a positive multiple of 64 or above 2^24 */
+  KV_DEV_RANGE = 1,       /* len < 0, len + n_tok > cap (append), len > max_len or cap (decode) */
+  KV_DEV_BAD_SESSION = 2, /* table entry with null/unaligned pointers, scales inconsistent with
+                             the format, or cap not a positive multiple of 64 or above 2^24 */
+  KV_DEV_BAD_PAGE = 4     /* a page table entry outside the pool (kv_decode_attn_paged) */
 };
 
 /* Bytes of one array of one layer: part 0 the K values/codes, part 1 the K scales
@@ -185,6 +188,49 @@ int kv_gather_rows(const kv_shape* h_shape, const kv_session* h_sess, int row0, 
                    void* d_or_h_dst, void* stream);
 int kv_scatter_rows(const kv_shape* h_shape, const kv_session* h_sess, int row0, int n_rows,
                     const void* d_or_h_src, void* stream);
+
+/* Paged sessions and a streamed window ([P3, What / How]: the K/V of a session live in
+ * host memory and move to a device-resident window block by block, each block a list of
+ * byte runs, codes and scales alike; attention over the window equals attention over a
+ * resident cache bit for bit).  A page holds KV_PAGE_ROWS cells.  A pool is a kv_session
+ * whose cap is KV_PAGE_ROWS x slots; slot s holds rows [64 s, 64 s + 64) of each array.
+ *
+ * kv_decode_attn_paged: kv_decode_attn over sessions whose page p (cells [64 p, 64 p +
+ * 64)) lies in slot d_pages[b * page_stride + p] of d_tab[b] (usually one pool for every
+ * session).  The same plan, arithmetic and order as kv_decode_attn, so a paged session
+ * gives bitwise the output of the resident one.  page_stride >= ceil(max_len / 64), else
+ * KV_ERR_ARG; d_pages: int32, device, 4-byte aligned.  A table entry outside [0, cap/64)
+ * is read as slot 0 and flags KV_DEV_BAD_PAGE in *d_status.  Workspace as for
+ * kv_decode_attn (kv_decode_workspace_bytes). */
+int kv_decode_attn_paged(const kv_shape* h_shape, const kv_session* d_tab,
+                         const int32_t* d_pages, int page_stride, const int32_t* d_len, int n_sess,
+                         int max_len, const float* d_q, float sm_scale, float* d_out, void* d_ws,
+                         size_t ws_bytes, int32_t* d_status, void* stream);
+
+/* The window's bookkeeping, in caller-owned host memory of kv_window_bytes(n_slots) bytes
+ * (0 for n_slots outside 1 .. 2^18): which (session, page) each pool slot holds, and CLOCK
+ * replacement.  kv_window_init marks every slot free (KV_ERR_WINDOW if bytes is short).
+ * Calls on one state must not overlap. */
+size_t kv_window_bytes(int n_slots);
+int kv_window_init(void* h_state, size_t bytes, int n_slots);
+
+/* Make pages [0, n_pages) of session sess_id (a caller-chosen id >= 0) resident, host only:
+ * h_pages (host int32 [n_pages], the session's page table from its last call, or -1s) is
+ * updated in place; the pages that must be copied are listed in h_missed (host int32
+ * [n_pages]), *h_misses of them.  Pages already resident are kept; others take slots by
+ * CLOCK, never a slot this call keeps.  KV_ERR_RANGE if n_pages exceeds the slots. */
+int kv_window_plan(void* h_state, int sess_id, int n_pages, int32_t* h_pages, int32_t* h_missed,
+                   int* h_misses);
+
+/* kv_window_plan, then the copies: each missed page's rows from h_store (a session whose
+ * arrays are pinned host memory, cap >= 64 n_pages) into its pool slot of h_pool (device,
+ * cap >= 64 x slots), consecutive pages in consecutive slots as one copy per array, and
+ * h_pages (pinned) to d_pages (device int32 [n_pages]).  Asynchronous on the stream:
+ * h_pages and h_store must stay valid until the stream reaches the call; a decode of the
+ * session enqueued after it on the stream reads the pages. */
+int kv_window_map(const kv_shape* h_shape, void* h_state, const kv_session* h_store, int sess_id,
+                  int n_pages, const kv_session* h_pool, int32_t* h_pages, int32_t* h_missed,
+                  int32_t* d_pages, int* h_misses, void* stream);
 
 /* Saved session image ([P2, Scope]: a header, the token ids, the KV body, then the
  * scales body; [P2, Phased plan]: version 3 carries the scales, and a version-2 image

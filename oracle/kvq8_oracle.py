@@ -269,6 +269,29 @@ def unpack_rows(cache: Cache, row0: int, n: int, buf: np.ndarray) -> None:
 
 
 # ----------------------------------------------------------------------------
+# Paged sessions ([P3, How]: a session's K/V move block by block; attention over the
+# blocks in a window equals attention over the resident cache).  A page holds 64
+# cells; page p (cells 64p .. 64p + 63) lies in slot pages[p] of a pool, rows
+# 64 s .. 64 s + 63 of each array.  The session the pool holds is its pages read back
+# in order; decode over it is the decode above.
+# ----------------------------------------------------------------------------
+PAGE_ROWS = 64
+
+
+def paged_cache(pool: Cache, pages, length: int) -> Cache:
+    """The session of `length` cells that page table `pages` describes in `pool`."""
+    n_pages = (length + PAGE_ROWS - 1) // PAGE_ROWS
+    c = Cache(pool.fmt, pool.kvh, max(PAGE_ROWS, n_pages * PAGE_ROWS), pool.hd)
+    for p in range(n_pages):
+        s = int(pages[p])
+        for name in ROW_ARRAYS:
+            a = getattr(pool, name)
+            if a is not None:
+                getattr(c, name)[:, p * PAGE_ROWS:(p + 1) * PAGE_ROWS] = a[:, s * PAGE_ROWS:(s + 1) * PAGE_ROWS]
+    return c
+
+
+# ----------------------------------------------------------------------------
 # A saved session image: [P2, Scope] lays a saved KV file out as a 128-byte header,
 # the token ids (4 B each), the KV body and then, new in its version 3, a scales body;
 # version 3 is written only when the cache has scales, and version-2 files (no

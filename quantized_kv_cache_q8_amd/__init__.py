@@ -22,14 +22,16 @@ KV_FMT_F16, KV_FMT_Q8, KV_FMT_K8V4 = 0, 1, 2
 KV_GROUP = 64
 KV_Q4_BLOCK = 32
 KV_OK, KV_ERR_ARG, KV_ERR_FMT, KV_ERR_ALIGN, KV_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
-KV_ERR_WORKSPACE, KV_ERR_RANGE, KV_ERR_HIP, KV_ERR_IMAGE = -5, -6, -7, -8
-KV_DEV_RANGE, KV_DEV_BAD_SESSION = 1, 2
+KV_ERR_WORKSPACE, KV_ERR_RANGE, KV_ERR_HIP, KV_ERR_IMAGE, KV_ERR_WINDOW = -5, -6, -7, -8, -9
+KV_DEV_RANGE, KV_DEV_BAD_SESSION, KV_DEV_BAD_PAGE = 1, 2, 4
+KV_PAGE_ROWS = 64
 
 EXPORTED = ["kv_cache_bytes", "kv_append", "kv_decode_workspace_bytes", "kv_decode_attn",
             "kv_compact_f16", "kv_prefill_workspace_bytes", "kv_prefill_attn", "kv_status_str",
             "kv_probe_stream_read", "kv_rows_bytes", "kv_copy_rows", "kv_gather_rows",
             "kv_scatter_rows", "kv_image_bytes", "kv_image_save", "kv_image_tokens",
-            "kv_image_load"]
+            "kv_image_load", "kv_decode_attn_paged", "kv_window_bytes", "kv_window_init",
+            "kv_window_plan", "kv_window_map"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run quantized_kv_cache_q8_amd.build.build() "
@@ -74,6 +76,13 @@ _sig = {
                            _P]),
     "kv_image_tokens": (_I, [ctypes.POINTER(kv_shape), _P, _SZ]),
     "kv_image_load": (_I, [ctypes.POINTER(kv_shape), ctypes.POINTER(kv_session), _P, _SZ, _P, _P]),
+    "kv_decode_attn_paged": (_I, [ctypes.POINTER(kv_shape), _P, _P, _I, _P, _I, _I, _P,
+                                  ctypes.c_float, _P, _P, _SZ, _P, _P]),
+    "kv_window_bytes": (_SZ, [_I]),
+    "kv_window_init": (_I, [_P, _SZ, _I]),
+    "kv_window_plan": (_I, [_P, _I, _I, _P, _P, _P]),
+    "kv_window_map": (_I, [ctypes.POINTER(kv_shape), _P, ctypes.POINTER(kv_session), _I, _I,
+                           ctypes.POINTER(kv_session), _P, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -137,8 +146,12 @@ class Session:
     (fp16 bits) [kvh][cap][hd/32]."""
 
     def __init__(self, fmt: int, n_kv_heads: int, cap: int, head_dim: int = 128,
-                 device="cuda", fill: int | None = None):
+                 device="cuda", fill: int | None = None, pinned: bool = False):
+        """pinned: the arrays in pinned host memory (a window's host store)."""
         self.fmt, self.kvh, self.cap, self.hd = fmt, n_kv_heads, cap, head_dim
+        self.pinned = pinned
+        if pinned:
+            device = "cpu"
         shp = (n_kv_heads, cap, head_dim)
         if fmt == KV_FMT_F16:
             self.k = torch.empty(shp, dtype=torch.int16, device=device)
@@ -157,6 +170,11 @@ class Session:
             sshp = (n_kv_heads, cap, head_dim // KV_GROUP)
             self.k_scale = torch.empty(sshp, dtype=torch.int16, device=device)
             self.v_scale = torch.empty(sshp, dtype=torch.int16, device=device)
+        if pinned:
+            for name in ("k", "v", "k_scale", "v_scale"):
+                t = getattr(self, name)
+                if t is not None:
+                    setattr(self, name, t.pin_memory())
         for t in self.tensors():
             if fill is None:
                 t.zero_()
@@ -167,7 +185,8 @@ class Session:
         return [t for t in (self.k, self.v, self.k_scale, self.v_scale) if t is not None]
 
     def entry(self) -> kv_session:
-        return kv_session(_ptr(self.k), _ptr(self.v), _ptr(self.k_scale), _ptr(self.v_scale),
+        ptr = (lambda t: None if t is None else _ptr_dev_or_pinned(t, "array")) if self.pinned else _ptr
+        return kv_session(ptr(self.k), ptr(self.v), ptr(self.k_scale), ptr(self.v_scale),
                           self.cap, 0)
 
 
@@ -211,6 +230,61 @@ def kv_decode_attn(shape: kv_shape, tab: torch.Tensor, lens: torch.Tensor, n_ses
                                _ptr(out, torch.float32, "out"), _ptr(ws, None, "ws"),
                                ws.numel() * ws.element_size(), _ptr(status, torch.int32, "status"),
                                _stream(stream)), "kv_decode_attn")
+
+
+def kv_decode_attn_paged(shape: kv_shape, tab: torch.Tensor, pages: torch.Tensor, page_stride: int,
+                         lens: torch.Tensor, n_sess: int, max_len: int, q: torch.Tensor,
+                         sm_scale: float, out: torch.Tensor, ws: torch.Tensor,
+                         status: torch.Tensor | None = None, stream=None) -> None:
+    """kv_decode_attn over paged sessions: pages int32 [n_sess][page_stride] (device)."""
+    _check(_lib.kv_decode_attn_paged(ctypes.byref(shape), _ptr(tab, torch.uint8, "tab"),
+                                     _ptr(pages, torch.int32, "pages"), page_stride,
+                                     _ptr(lens, torch.int32, "lens"), n_sess, max_len,
+                                     _ptr(q, torch.float32, "q"), float(sm_scale),
+                                     _ptr(out, torch.float32, "out"), _ptr(ws, None, "ws"),
+                                     ws.numel() * ws.element_size(),
+                                     _ptr(status, torch.int32, "status"), _stream(stream)),
+           "kv_decode_attn_paged")
+
+
+class Window:
+    """A streamed window's host-side state (kv_window_*): n_slots pool slots."""
+
+    def __init__(self, n_slots: int):
+        nb = int(_lib.kv_window_bytes(n_slots))
+        if nb == 0:
+            raise ValueError("kv_window_bytes: n_slots out of range")
+        self.n_slots = n_slots
+        self.state = ctypes.create_string_buffer(nb)
+        _check(_lib.kv_window_init(self.state, nb, n_slots), "kv_window_init")
+
+    def plan(self, sess_id: int, pages: "np.ndarray"):
+        """Host-only planning: updates pages (int32 numpy array) in place; returns the
+        missed pages."""
+        import numpy as np
+        assert pages.dtype == np.int32 and pages.flags.c_contiguous
+        missed = np.zeros(max(1, pages.size), np.int32)
+        n = ctypes.c_int(0)
+        _check(_lib.kv_window_plan(self.state, sess_id, pages.size, pages.ctypes.data,
+                                   missed.ctypes.data, ctypes.byref(n)), "kv_window_plan")
+        return missed[:n.value].copy()
+
+    def map(self, shape: kv_shape, store: "Session", sess_id: int, n_pages: int, pool: "Session",
+            h_pages: torch.Tensor, d_pages: torch.Tensor, stream=None) -> int:
+        """Make pages [0, n_pages) resident, copying the missed ones from the pinned host
+        store; h_pages: pinned int32 [>= n_pages] (kept per session), d_pages: device
+        int32 row of the page table.  Returns the number of pages copied."""
+        if not store.pinned:
+            raise ValueError("store: must be a pinned Session")
+        if h_pages.dtype != torch.int32 or not h_pages.is_pinned() or h_pages.numel() < n_pages:
+            raise ValueError("h_pages: expected a pinned int32 tensor of at least n_pages entries")
+        missed = torch.zeros(max(1, n_pages), dtype=torch.int32)
+        n = ctypes.c_int(0)
+        _check(_lib.kv_window_map(ctypes.byref(shape), self.state, ctypes.byref(store.entry()),
+                                  sess_id, n_pages, ctypes.byref(pool.entry()), h_pages.data_ptr(),
+                                  missed.data_ptr(), _ptr(d_pages, torch.int32, "d_pages"),
+                                  ctypes.byref(n), _stream(stream)), "kv_window_map")
+        return n.value
 
 
 def kv_compact_f16(shape: kv_shape, sess: kv_session, P: int, k16: torch.Tensor,

@@ -13,7 +13,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(os.path.dirname(PKG), "_build")
 LIB = os.path.join(PKG, "libkvq8.so")
-SOURCES = ["api.hip", "append.hip", "decode.hip", "compact.hip", "prefill.hip", "probe.hip"]
+SOURCES = ["api.hip", "append.hip", "decode.hip", "compact.hip", "prefill.hip", "probe.hip",
+           "window.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -200,6 +200,32 @@ int kv_decode_attn(const kv_shape* h_shape, const kv_session* d_tab, const int32
                                   static_cast<hipStream_t>(stream)));
 }
 
+int kv_decode_attn_paged(const kv_shape* h_shape, const kv_session* d_tab,
+                         const int32_t* d_pages, int page_stride, const int32_t* d_len, int n_sess,
+                         int max_len, const float* d_q, float sm_scale, float* d_out, void* d_ws,
+                         size_t ws_bytes, int32_t* d_status, void* stream) {
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  if (d_tab == nullptr || d_pages == nullptr || d_len == nullptr || d_q == nullptr ||
+      d_out == nullptr)
+    return KV_ERR_ARG;
+  if (n_sess < 1 || n_sess > KV_DEC_MAX_SESS || max_len < 0 || !std::isfinite(sm_scale))
+    return KV_ERR_ARG;
+  // every page of a session of up to max_len cells has a table entry
+  if (page_stride < 1 || (long long)page_stride * KV_PAGE_ROWS < (long long)max_len)
+    return KV_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_tab) & 7) || !aligned4(d_pages) || !aligned4(d_len) ||
+      !aligned16(d_q) || !aligned16(d_out) || !aligned16(d_ws) || !aligned4(d_status))
+    return KV_ERR_ALIGN;
+  if (d_ws == nullptr) return KV_ERR_WORKSPACE;
+  const DecodePlan p =
+      decode_plan(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, n_sess, max_len);
+  if (ws_bytes < p.ws_o_bytes + p.ws_lse_bytes) return KV_ERR_WORKSPACE;
+  return hip_status(launch_decode(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, d_tab,
+                                  d_len, n_sess, max_len, d_q, sm_scale, d_out, d_ws, p, d_status,
+                                  static_cast<hipStream_t>(stream), d_pages, page_stride));
+}
+
 int kv_compact_f16(const kv_shape* h_shape, const kv_session* h_sess, int P, uint16_t* d_k16,
                    uint16_t* d_v16, void* stream) {
   int rc = check_shape(h_shape);
@@ -276,6 +302,17 @@ size_t kv_rows_bytes(const kv_shape* h_shape, int n_rows) {
 
 int kv_copy_rows(const kv_shape* h_shape, const kv_session* h_src, int src_row0,
                  const kv_session* h_dst, int dst_row0, int n_rows, void* stream) {
+  return kvq8::copy_rows(h_shape, h_src, src_row0, h_dst, dst_row0, n_rows, stream,
+                         hipMemcpyDeviceToDevice);
+}
+
+}  // extern "C"
+
+// rows of one session into another, every array of the format; kind says where the
+// two live (device to device, or between pinned host memory and the device)
+int kvq8::copy_rows(const kv_shape* h_shape, const kv_session* h_src, int src_row0,
+                    const kv_session* h_dst, int dst_row0, int n_rows, void* stream,
+                    hipMemcpyKind kind) {
   int rc = check_shape(h_shape);
   if (rc) return rc;
   if ((rc = check_session(h_shape, h_src)) || (rc = check_session(h_shape, h_dst))) return rc;
@@ -294,11 +331,13 @@ int kv_copy_rows(const kv_shape* h_shape, const kv_session* h_src, int src_row0,
     const hipError_t e = hipMemcpy2DAsync(
         pd[a] + (size_t)dst_row0 * rb[a], (size_t)h_dst->cap * rb[a],
         ps[a] + (size_t)src_row0 * rb[a], (size_t)h_src->cap * rb[a], (size_t)n_rows * rb[a],
-        kvh, hipMemcpyDeviceToDevice, st);
+        kvh, kind, st);
     if (e != hipSuccess) return KV_ERR_HIP;
   }
   return KV_OK;
 }
+
+extern "C" {
 
 int kv_gather_rows(const kv_shape* h_shape, const kv_session* h_sess, int row0, int n_rows,
                    void* d_or_h_dst, void* stream) {
@@ -382,6 +421,7 @@ const char* kv_status_str(int status) {
     case KV_ERR_RANGE: return "rows outside the session's capacity";
     case KV_ERR_HIP: return "HIP kernel launch or copy failed";
     case KV_ERR_IMAGE: return "saved image refused (magic, version, format, shape or size)";
+    case KV_ERR_WINDOW: return "window state missing, too small or not initialised";
     default: return "unknown status";
   }
 }

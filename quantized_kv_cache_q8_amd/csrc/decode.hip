@@ -35,6 +35,7 @@
 // of the rounding is fp32 accumulation.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "kvq8_internal.h"
 
@@ -232,8 +233,52 @@ __host__ __device__ constexpr int ch0() {
 }
 template <int FMT, int G>
 __host__ __device__ constexpr int ch1() { return GROUPED ? 2 * ch_steps<G>() - ch0<FMT, G>() : 0; }
+static_assert(2 * KVQ8_DEC_CH <= 256, "a wave has at most 256 steps (the page map's registers)");
 static_assert(KVQ8_DEC_CH % 8 == 0 && ch_steps<8>() % 8 == 0,
               "the group budgets are whole multiples of 8 steps");
+
+// Paged sessions: a session's cells live in pages of KV_PAGE_ROWS (64) inside a pool
+// (the session table's arrays, cap = 64 x slots); a page table maps page p (cells
+// 64p .. 64p + 63) to its slot.  A wave's steps are 8W >= 64 rows apart, so each is in
+// a page of its own: the wave keeps the slot of each of its steps in registers (lane
+// l, register j: step l + 64 j; at most 256 steps per wave, which the plans keep) and
+// a load reads it with one readlane.  A slot outside the pool reads slot 0 (the merge
+// flags the table).
+struct NoPages {
+  __device__ __forceinline__ uint32_t phys(int, uint32_t row) const { return row; }
+  __device__ __forceinline__ uint32_t phys2(int, int, bool, uint32_t row) const { return row; }
+};
+struct PageMap {
+  int slot[4];
+  __device__ __forceinline__ void init(const int32_t* pages, int stride, int b, int gw, int W,
+                                       int n_steps, int n_slots, int lane) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = lane + 64 * j;
+      int sl = 0;
+      if (k < n_steps) {
+        sl = pages[(long long)b * stride + (((gw + k * W) * 8) >> 6)];
+        if ((unsigned)sl >= (unsigned)n_slots) sl = 0;
+      }
+      slot[j] = sl;
+    }
+  }
+  // slot of step k (k the same in every lane)
+  __device__ __forceinline__ int slot_of(int k) const {
+    const int j = k >> 6;
+    const int v = j == 0 ? slot[0] : j == 1 ? slot[1] : j == 2 ? slot[2] : slot[3];
+    return __builtin_amdgcn_readlane(v, k & 63);
+  }
+  // the pool row of logical row `row`, which lies in step k's page
+  __device__ __forceinline__ uint32_t phys(int k, uint32_t row) const {
+    return (uint32_t)slot_of(k) * KV_PAGE_ROWS + (row & (KV_PAGE_ROWS - 1));
+  }
+  // the same for a row of step k1 (second) or k0 (first), chosen per lane
+  __device__ __forceinline__ uint32_t phys2(int k0, int k1, bool second, uint32_t row) const {
+    const uint32_t s0 = (uint32_t)slot_of(k0), s1 = (uint32_t)slot_of(k1);
+    return (second ? s1 : s0) * KV_PAGE_ROWS + (row & (KV_PAGE_ROWS - 1));
+  }
+};
 
 // One batch of U steps for one lane: U x 16 values and, for int8, the U raw fp16
 // scales of the lane's 64-dim group.
@@ -246,12 +291,15 @@ struct Batch {
   // vals, scales: the head's first row of values and of scales
   // V: the V array (only K8V4 lays it out differently from K)
   // kmax: steps past it re-read step kmax (a row of this wave's, still in cache)
-  template <bool V>
+  // pm: the page map of a paged session (rows then lie in step k + u's page)
+  template <bool V, class PM = NoPages>
   __device__ __forceinline__ void load(const char* vals, const char* scales, int gw, int W, int k,
-                                       int len, int r, int c, int kmax = 1 << 30) {
+                                       int len, int r, int c, int kmax = 1 << 30,
+                                       const PM& pm = PM()) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t row = (uint32_t)min((gw + min(k + u, kmax) * W) * 8 + r, len - 1);
+      const int ku = min(k + u, kmax);
+      const uint32_t row = pm.phys(ku, (uint32_t)min((gw + ku * W) * 8 + r, len - 1));
       if constexpr (FMT == KV_FMT_K8V4 && V) {
         ch[u].load_v(vals, row, c);
         sc[u] = ldg16(scales + (row * NQ4 + (c >> 1)) * 2);   // lane c: dims of block c / 2
@@ -342,13 +390,16 @@ struct KBatch {
   static_assert(U % 2 == 0, "blocks of 16 tokens are pairs of steps");
   u32x4 w[U / 2][2];
   uint16_t sc[U / 2][2];
+  template <class PM = NoPages>
   __device__ __forceinline__ void load(const char* kb, const char* ksb, int gw, int W, int k,
-                                       int len, int lane, int kmax = 1 << 30) {
+                                       int len, int lane, int kmax = 1 << 30,
+                                       const PM& pm = PM()) {
     const int n = lane & 15, kq = lane >> 4;
 #pragma unroll
     for (int j = 0; j < U / 2; ++j) {
-      const uint32_t row =
-          (uint32_t)min((gw + min(k + 2 * j + (n >> 3), kmax) * W) * 8 + (n & 7), len - 1);
+      const int k0 = min(k + 2 * j, kmax), k1 = min(k + 2 * j + 1, kmax);
+      const uint32_t row = pm.phys2(k0, k1, (n >> 3) != 0,
+                                    (uint32_t)min((gw + ((n >> 3) ? k1 : k0) * W) * 8 + (n & 7), len - 1));
 #pragma unroll
       for (int grp = 0; grp < NGRP; ++grp) {
         w[j][grp] = ldkv(kb, row * HD + grp * 64 + kq * 16);
@@ -370,12 +421,12 @@ static_assert(split_lds_bytes<1>() <= 160 * 1024 && split_lds_bytes<2>() <= 160 
                   split_lds_bytes<4>() <= 160 * 1024 && split_lds_bytes<8>() <= 160 * 1024,
               "a split workgroup fits in one CU's LDS");
 
-template <int FMT, int G, int U>
+template <int FMT, int G, int U, bool PG>
 __global__ __launch_bounds__(DEC_THREADS)
 __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int kvh,
     const float* __restrict__ q, float qscale, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, int S) {
+    float* __restrict__ ws_lse, int S, const int32_t* __restrict__ pages, int page_stride) {
   constexpr int CH0 = ch0<FMT, G>(), CH1 = ch1<FMT, G>();
   constexpr int UK = k_batch_rows<G>();
   static_assert(CH0 % (2 * U) == 0 && CH1 % (2 * U) == 0, "a chunk holds whole pairs of load batches");
@@ -401,6 +452,10 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
   const int gw = (grp ? Jf : 0) + gw0;           // first step of this wave
   const int W = Sb * GRP_WAVES;                  // waves per group of (session, head)
   const int n_steps = gw0 < Jg ? (Jg - 1 - gw0) / W + 1 : 0;
+  // paged: this wave's steps -> pool slots; rows past the last step re-read it
+  std::conditional_t<PG, PageMap, NoPages> pm{};
+  if constexpr (PG) pm.init(pages, page_stride, b, gw, W, n_steps, ss.cap / KV_PAGE_ROWS, lane);
+  const int kclamp = PG ? max(n_steps - 1, 0) : (1 << 30);
 
   extern __shared__ float smem[];
   float* lg = smem + (grp ? GRP_WAVES * CH0 + wg * CH1 : wg * CH0) * 8 * G;  // logits, then p
@@ -650,24 +705,24 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     };
     auto vpass = [&](int s0, int s1) __attribute__((always_inline)) {
       for (int it0 = s0; it0 < s1; it0 += 2 * U) {
-        B.template load<true>(vb, vsb, gw, W, it0 + U, len, r, c);
+        B.template load<true>(vb, vsb, gw, W, it0 + U, len, r, c, kclamp, pm);
         vstep(A, it0, n_it);
-        if (it0 + 2 * U < s1) A.template load<true>(vb, vsb, gw, W, it0 + 2 * U, len, r, c);
+        if (it0 + 2 * U < s1) A.template load<true>(vb, vsb, gw, W, it0 + 2 * U, len, r, c, kclamp, pm);
         vstep(B, it0 + U, n_it);
       }
     };
     if constexpr (MF) {
       // ---- K pass on the matrix cores ------------------------------------------
       KBatch<UK> KA, KB;
-      KA.load(kb, ksb, gw, W, 0, len, lane);
+      KA.load(kb, ksb, gw, W, 0, len, lane, kclamp, pm);
       for (int it0 = 0; it0 < n_it; it0 += 2 * UK) {
-        KB.load(kb, ksb, gw, W, it0 + UK, len, lane);
+        KB.load(kb, ksb, gw, W, it0 + UK, len, lane, kclamp, pm);
         kstep_m(KA, it0);
-        if (it0 + 2 * UK < n_it) KA.load(kb, ksb, gw, W, it0 + 2 * UK, len, lane);
+        if (it0 + 2 * UK < n_it) KA.load(kb, ksb, gw, W, it0 + 2 * UK, len, lane, kclamp, pm);
         kstep_m(KB, it0 + UK);
       }
       // the first V batch after the loop: its registers are then not live across it
-      A.template load<true>(vb, vsb, gw, W, 0, len, r, c);
+      A.template load<true>(vb, vsb, gw, W, 0, len, r, c, kclamp, pm);
       wave_lds_fence();
       softmax(0, n_it, (n_it + 2 * U - 1) / (2 * U) * (2 * U));
       wave_lds_fence();
@@ -675,14 +730,14 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
       vpass(0, n_it);
     } else {
       // ---- K pass ---------------------------------------------------------------
-      A.template load<false>(kb, ksb, gw, W, 0, len, r, c);
+      A.template load<false>(kb, ksb, gw, W, 0, len, r, c, kclamp, pm);
       for (int it0 = 0; it0 < n_it; it0 += 2 * U) {
-        B.template load<false>(kb, ksb, gw, W, it0 + U, len, r, c);
+        B.template load<false>(kb, ksb, gw, W, it0 + U, len, r, c, kclamp, pm);
         kstep(A, 0, it0, n_it);
         if (it0 + 2 * U < n_it)
-          A.template load<false>(kb, ksb, gw, W, it0 + 2 * U, len, r, c);
+          A.template load<false>(kb, ksb, gw, W, it0 + 2 * U, len, r, c, kclamp, pm);
         else
-          A.template load<true>(vb, vsb, gw, W, 0, len, r, c);
+          A.template load<true>(vb, vsb, gw, W, 0, len, r, c, kclamp, pm);
         kstep(B, 0, it0 + U, n_it);
       }
       wave_lds_fence();
@@ -770,6 +825,7 @@ constexpr int PAIR_MIN_STEPS = 32;
 // steps per pair the plan aims for at most, so that long sessions spread over many
 // workgroups (balance across CUs and sessions)
 constexpr int PAIR_TARGET_STEPS = 256;
+static_assert(PAIR_TARGET_STEPS <= 256, "a pair has at most 256 steps (the page map's registers)");
 
 template <int G>
 __host__ __device__ constexpr size_t pair_lds_bytes() {
@@ -778,11 +834,11 @@ __host__ __device__ constexpr size_t pair_lds_bytes() {
 }
 static_assert(pair_lds_bytes<8>() <= 160 * 1024, "a pair workgroup fits in one CU's LDS");
 
-template <int FMT, int G, int U>
+template <int FMT, int G, int U, bool PG>
 __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 2 : KVQ8_DEC_PAIR_WPE))) void k_decode_pair(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int kvh,
     const float* __restrict__ q, float qscale, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, int S) {
+    float* __restrict__ ws_lse, int S, const int32_t* __restrict__ pages, int page_stride) {
   static_assert(FMT != KV_FMT_F16, "the pair kernel reads int8 K codes");
   constexpr int UK = k_batch_rows<G>();
   static_assert(PAIR_CH % (2 * UK) == 0 && PAIR_CH % (2 * U) == 0,
@@ -807,6 +863,9 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
   const int n_steps = gw < J ? (J - 1 - gw) / W + 1 : 0;
   const int n_first = s_idx * PAIRS < J ? (J - 1 - s_idx * PAIRS) / W + 1 : 0;  // pair 0's
   const int n_chunks = (n_first + PAIR_CH - 1) / PAIR_CH;   // the same for every wave
+  // paged: this pair's steps -> pool slots
+  std::conditional_t<PG, PageMap, NoPages> pm{};
+  if constexpr (PG) pm.init(pages, page_stride, b, gw, W, n_steps, ss.cap / KV_PAGE_ROWS, lane);
 
   extern __shared__ float smem[];
   float* pb = smem + (size_t)pr * 2 * PAIR_CH * 8 * G;      // this pair's two chunk buffers
@@ -919,9 +978,9 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
     auto kiter = [&](int k0, bool pf) __attribute__((always_inline)) {
       const int ch = k0 / PAIR_CH, kr = k0 - ch * PAIR_CH;
       float* lc = pb + (ch & 1) * PAIR_CH * 8 * G;
-      KB.load(kb, ksb, gw, W, k0 + UK, len, lane, kmax);
+      KB.load(kb, ksb, gw, W, k0 + UK, len, lane, kmax, pm);
       kstep(KA, lc, kr);
-      if (pf) KA.load(kb, ksb, gw, W, k0 + 2 * UK, len, lane, kmax);
+      if (pf) KA.load(kb, ksb, gw, W, k0 + 2 * UK, len, lane, kmax, pm);
       kstep(KB, lc, kr + UK);
       if (kr + 2 * UK == PAIR_CH) {
         wave_lds_fence();
@@ -963,7 +1022,7 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
       }
     };
     if (total > 0) {
-      KA.load(kb, ksb, gw, W, 0, len, lane, kmax);
+      KA.load(kb, ksb, gw, W, 0, len, lane, kmax, pm);
       int k0 = 0;
       for (; k0 + 2 * UK < total; k0 += 2 * UK) kiter(k0, true);
       kiter(k0, false);
@@ -1030,12 +1089,12 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
           for (int i = 0; i < 16; ++i) acc[g][i] *= f;
         }
       }
-      B.template load<true>(vb, vsb, gw, W, k0 + U, len, r, c, kmax);
+      B.template load<true>(vb, vsb, gw, W, k0 + U, len, r, c, kmax, pm);
       vstep(A, pc, kr);
-      if (pf) A.template load<true>(vb, vsb, gw, W, k0 + 2 * U, len, r, c, kmax);
+      if (pf) A.template load<true>(vb, vsb, gw, W, k0 + 2 * U, len, r, c, kmax, pm);
       vstep(B, pc, kr + U);
     };
-    if (total > 0) A.template load<true>(vb, vsb, gw, W, 0, len, r, c, kmax);
+    if (total > 0) A.template load<true>(vb, vsb, gw, W, 0, len, r, c, kmax, pm);
     __syncthreads();   // the K wave's first chunk
     if (total > 0) {
       int k0 = 0;
@@ -1095,7 +1154,8 @@ template <int FMT>
 __global__ __launch_bounds__(64 * MERGE_WAVES) void k_decode_merge(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int nqh,
     int n_rows, const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int S,
-    float* __restrict__ out, int32_t* __restrict__ status) {
+    float* __restrict__ out, int32_t* __restrict__ status, const int32_t* __restrict__ pages,
+    int page_stride) {
   const int row = blockIdx.x * MERGE_WAVES + (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= n_rows) return;
@@ -1109,6 +1169,18 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void k_decode_merge(
     dst[lane] = make_float2(0.f, 0.f);
     if (bad && qh == 0 && lane == 0) flag(status, bad);
     return;
+  }
+  // paged: the first head's wave checks the session's page table (the split kernels
+  // read a slot outside the pool as slot 0)
+  if (pages != nullptr && qh == 0) {
+    const int n_slots = ss.cap / KV_PAGE_ROWS;
+    const int n_pages = (len + KV_PAGE_ROWS - 1) / KV_PAGE_ROWS;
+    bool bad_page = false;
+    for (int pg = lane; pg < n_pages; pg += 64) {
+      const int sl = pages[(long long)b * page_stride + pg];
+      bad_page |= sl < 0 || sl >= n_slots;
+    }
+    if (__builtin_amdgcn_ballot_w64(bad_page) != 0 && lane == 0) flag(status, KV_DEV_BAD_PAGE);
   }
   // the splits that worked on this session (the same count the split kernel used)
   const int Sb = active_splits<FMT>(len, S);
@@ -1186,10 +1258,10 @@ int resident_splits() {
   hipError_t e;
   if constexpr (use_pair<FMT>())
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, k_decode_pair<FMT, G, batch_rows<FMT, G>()>, DEC_THREADS, pair_lds_bytes<G>());
+        &per_cu, k_decode_pair<FMT, G, batch_rows<FMT, G>(), false>, DEC_THREADS, pair_lds_bytes<G>());
   else
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, k_decode_split<FMT, G, batch_rows<FMT, G>()>, DEC_THREADS, split_lds_bytes<G>());
+        &per_cu, k_decode_split<FMT, G, batch_rows<FMT, G>(), false>, DEC_THREADS, split_lds_bytes<G>());
   if (e != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
@@ -1217,25 +1289,40 @@ int resident(int fmt, int G) {
   return 0;
 }
 
-template <int FMT, int G>
-hipError_t launch_g(const kv_session* tab, const int32_t* lens, int n_sess, int max_len, int kvh,
-                    const float* q, float sm_scale, float* out, float* ws_o, float* ws_lse,
-                    const DecodePlan& plan, int32_t* status, hipStream_t st) {
+template <int FMT, int G, bool PG>
+hipError_t launch_split(const kv_session* tab, const int32_t* lens, int n_sess, int max_len,
+                        int kvh, const float* q, float sm_scale, float* ws_o, float* ws_lse,
+                        const DecodePlan& plan, const int32_t* pages, int page_stride,
+                        hipStream_t st) {
   constexpr int U = batch_rows<FMT, G>();
   static_assert(U == 1 || U == 2 || U == 4 || U == 8, "U must divide the group budgets / 2");
   dim3 grid(plan.S, kvh, n_sess), block(DEC_THREADS);
   if constexpr (use_pair<FMT>())
-    hipLaunchKernelGGL((k_decode_pair<FMT, G, U>), grid, block, pair_lds_bytes<G>(), st, tab,
-                       lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S);
+    hipLaunchKernelGGL((k_decode_pair<FMT, G, U, PG>), grid, block, pair_lds_bytes<G>(), st, tab,
+                       lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages,
+                       page_stride);
   else
-    hipLaunchKernelGGL((k_decode_split<FMT, G, U>), grid, block, split_lds_bytes<G>(), st, tab,
-                       lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S);
-  hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL((k_decode_split<FMT, G, U, PG>), grid, block, split_lds_bytes<G>(), st,
+                       tab, lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages,
+                       page_stride);
+  return hipGetLastError();
+}
+
+template <int FMT, int G>
+hipError_t launch_g(const kv_session* tab, const int32_t* lens, int n_sess, int max_len, int kvh,
+                    const float* q, float sm_scale, float* out, float* ws_o, float* ws_lse,
+                    const DecodePlan& plan, int32_t* status, const int32_t* pages,
+                    int page_stride, hipStream_t st) {
+  hipError_t e = pages != nullptr
+                     ? launch_split<FMT, G, true>(tab, lens, n_sess, max_len, kvh, q, sm_scale, ws_o,
+                                                  ws_lse, plan, pages, page_stride, st)
+                     : launch_split<FMT, G, false>(tab, lens, n_sess, max_len, kvh, q, sm_scale,
+                                                   ws_o, ws_lse, plan, nullptr, 0, st);
   if (e != hipSuccess) return e;
   const int n_rows = n_sess * kvh * G;
   dim3 mgrid((n_rows + MERGE_WAVES - 1) / MERGE_WAVES), mblock(64 * MERGE_WAVES);
   hipLaunchKernelGGL((k_decode_merge<FMT>), mgrid, mblock, 0, st, tab, lens, max_len, kvh * G,
-                     n_rows, ws_o, ws_lse, plan.S, out, status);
+                     n_rows, ws_o, ws_lse, plan.S, out, status, pages, page_stride);
   return hipGetLastError();
 }
 
@@ -1292,14 +1379,15 @@ DecodePlan decode_plan(int fmt, int kvh, int nqh, int n_sess, int max_len) {
 hipError_t launch_decode(int fmt, int kvh, int nqh, const kv_session* d_tab,
                          const int32_t* d_len, int n_sess, int max_len, const float* d_q,
                          float sm_scale, float* d_out, void* d_ws, const DecodePlan& plan,
-                         int32_t* d_status, hipStream_t st) {
+                         int32_t* d_status, hipStream_t st, const int32_t* d_pages,
+                         int page_stride) {
   float* ws_o = static_cast<float*>(d_ws);
   float* ws_lse = reinterpret_cast<float*>(static_cast<char*>(d_ws) + plan.ws_o_bytes);
   const int G = nqh / kvh;
 #define KVQ8_DEC(F, GG)                                                                          \
   if (fmt == F && G == GG)                                                                       \
     return launch_g<F, GG>(d_tab, d_len, n_sess, max_len, kvh, d_q, sm_scale, d_out, ws_o, ws_lse, \
-                           plan, d_status, st);
+                           plan, d_status, d_pages, page_stride, st);
   KVQ8_DEC(KV_FMT_K8V4, 1)
   KVQ8_DEC(KV_FMT_K8V4, 2)
   KVQ8_DEC(KV_FMT_K8V4, 4)

@@ -151,6 +151,12 @@ hipError_t launch_append(int fmt, int kvh, const kv_session* d_tab, const int32_
                          int n_sess, int n_tok, const float* d_k, const float* d_v,
                          int32_t* d_status, hipStream_t st);
 
+// rows of one session into another (kv_copy_rows, with the copy kind given: the
+// window also moves pages from pinned host memory)
+int copy_rows(const kv_shape* h_shape, const kv_session* h_src, int src_row0,
+              const kv_session* h_dst, int dst_row0, int n_rows, void* stream,
+              hipMemcpyKind kind);
+
 struct DecodePlan {
   int S;      // splits (workgroups) per (session, kv head): grid x
   size_t ws_o_bytes, ws_lse_bytes;
@@ -161,7 +167,8 @@ DecodePlan decode_plan(int fmt, int kvh, int nqh, int n_sess, int max_len);
 hipError_t launch_decode(int fmt, int kvh, int nqh, const kv_session* d_tab,
                          const int32_t* d_len, int n_sess, int max_len, const float* d_q,
                          float sm_scale, float* d_out, void* d_ws, const DecodePlan& plan,
-                         int32_t* d_status, hipStream_t st);
+                         int32_t* d_status, hipStream_t st, const int32_t* d_pages = nullptr,
+                         int page_stride = 0);
 
 hipError_t launch_compact(int fmt, int kvh, const kv_session& sess, int P, uint16_t* d_k16,
                           uint16_t* d_v16, hipStream_t st);

@@ -53,7 +53,7 @@ def test_cache_bytes_matches_oracle():
 
 
 def test_status_strings():
-    for s in range(-8, 1):
+    for s in range(-9, 1):
         assert kq.kv_status_str(s) and kq.kv_status_str(s) != "unknown status"
     assert kq.kv_status_str(-99) == "unknown status"
 

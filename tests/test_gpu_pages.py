@@ -1,0 +1,139 @@
+"""Paged sessions and the streamed window on the GPU: a decode over pages scattered
+through a pool, or streamed into a window from a pinned host store, equals the decode
+over the resident session bit for bit (PR #711 "kv: --kv k8v4 streams with
+--kv-resident", section Tests: streamed and resident attention bitwise equal)."""
+import numpy as np
+import pytest
+import torch
+
+import kvsynth
+import quantized_kv_cache_q8_amd as kq
+from gpu_util import DEV, append_bulk, check_close, oracle_cache, say, shape, sm_scale
+from oracle import kvq8_oracle as o
+
+pytestmark = pytest.mark.gpu
+P = kq.KV_PAGE_ROWS
+
+
+def filled(fmt, kvh, cap, n, seed):
+    xk = kvsynth.kv_tokens(seed, 0, n, kvh, 128, "K", outliers=True)
+    xv = kvsynth.kv_tokens(seed, 0, n, kvh, 128, "V", outliers=True)
+    s = kq.Session(fmt, kvh, cap, fill=0)
+    assert append_bulk(shape(fmt, kvh, kvh), [s], [0], xk[None], xv[None]) == 0
+    return s, xk, xv
+
+
+def copy_pages(src, dst, pages, n_pages):
+    """Rows of page p of src into slot pages[p] of dst (torch copies)."""
+    for a, b in zip(src.tensors(), dst.tensors()):
+        for p in range(n_pages):
+            s = int(pages[p])
+            b[:, s * P:(s + 1) * P].copy_(a[:, p * P:(p + 1) * P])
+
+
+def decode(sh, sessions, lens, q, max_len, pages=None, stride=0, status=None):
+    n = len(sessions)
+    tab = kq.session_table([s.entry() for s in sessions])
+    ln = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out = torch.empty((n, sh.n_q_heads, 128), device=DEV)
+    ws = torch.zeros(kq.kv_decode_workspace_bytes(sh, n, max_len), dtype=torch.uint8, device=DEV)
+    qd = torch.from_numpy(np.ascontiguousarray(q)).to(DEV)
+    if pages is None:
+        kq.kv_decode_attn(sh, tab, ln, n, max_len, qd, sm_scale(), out, ws, status)
+    else:
+        kq.kv_decode_attn_paged(sh, tab, pages, stride, ln, n, max_len, qd, sm_scale(), out, ws, status)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("fmt,G", [(0, 4), (1, 4), (2, 4), (1, 1), (1, 8), (0, 2)])
+def test_paged_decode_equals_resident(fmt, G):
+    kvh, n = 4, 3001
+    say(f"paged fmt={fmt} G={G}")
+    sess, xk, xv = filled(fmt, kvh, 3072, n, 31)
+    sh = shape(fmt, kvh, G * kvh)
+    q = kvsynth.queries(31, 0, 1, G * kvh, 128)
+    y_res = decode(sh, [sess], [n], q, n)
+    n_pages = (n + P - 1) // P
+    n_slots = 80
+    perm = np.random.default_rng(fmt * 10 + G).permutation(n_slots)[:n_pages].astype(np.int32)
+    pool = kq.Session(fmt, kvh, n_slots * P, fill=0x5A)
+    copy_pages(sess, pool, perm, n_pages)
+    pages = torch.from_numpy(perm).to(DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y_pag = decode(sh, [pool], [n], q, n, pages, n_pages, status)
+    assert int(status.item()) == 0
+    assert np.array_equal(y_pag, y_res)
+    # and the oracle's decode over the oracle's view of the pool
+    ref = oracle_cache(fmt, kvh, 3072, 128, xk, xv)
+    view = o.paged_cache(ref, np.arange(n_pages), n)
+    want = o.decode_attn(q[0], view.dequant("k", n), view.dequant("v", n), n, sm_scale())
+    check_close(y_pag[0], want, f"paged fmt={fmt} G={G}")
+
+
+def test_paged_batch_and_bad_page():
+    fmt, kvh, G = kq.KV_FMT_Q8, 8, 4
+    say("paged batch")
+    lens = [700, 2500, 64, 1999]
+    sh = shape(fmt, kvh, G * kvh)
+    sessions = [filled(fmt, kvh, 2560, n, 40 + i)[0] for i, n in enumerate(lens)]
+    q = kvsynth.queries(41, 0, len(lens), G * kvh, 128)
+    max_len = max(lens)
+    y_res = decode(sh, sessions, lens, q, max_len)
+    stride = (max_len + P - 1) // P
+    n_slots = sum((n + P - 1) // P for n in lens) + 7
+    pool = kq.Session(fmt, kvh, n_slots * P, fill=0)
+    perm = np.random.default_rng(5).permutation(n_slots).astype(np.int32)
+    table = np.zeros((len(lens), stride), np.int32)
+    k = 0
+    for b, (s, n) in enumerate(zip(sessions, lens)):
+        npg = (n + P - 1) // P
+        table[b, :npg] = perm[k:k + npg]
+        k += npg
+        copy_pages(s, pool, table[b], npg)
+    pages = torch.from_numpy(table).to(DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y_pag = decode(sh, [pool] * len(lens), lens, q, max_len, pages, stride, status)
+    assert int(status.item()) == 0
+    assert np.array_equal(y_pag, y_res)
+    # a page outside the pool: flagged, read as slot 0 (in bounds), the others intact
+    bad = table.copy()
+    bad[1, 3] = n_slots + 5
+    status.zero_()
+    y_bad = decode(sh, [pool] * len(lens), lens, q, max_len, torch.from_numpy(bad).to(DEV), stride,
+                   status)
+    assert int(status.item()) & kq.KV_DEV_BAD_PAGE
+    assert np.array_equal(y_bad[[0, 2, 3]], y_res[[0, 2, 3]])
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_streamed_window_equals_resident(fmt):
+    kvh, G = 4, 4
+    say(f"window fmt={fmt}")
+    sh = shape(fmt, kvh, G * kvh)
+    lens = {0: 2000, 1: 3001, 2: 1300}
+    res = {s: filled(fmt, kvh, 3072, n, 50 + s)[0] for s, n in lens.items()}
+    # host stores: pinned copies of the sessions
+    store = {}
+    for s, sess in res.items():
+        st = kq.Session(fmt, kvh, 3072, pinned=True)
+        for a, b in zip(sess.tensors(), st.tensors()):
+            b.copy_(a.cpu())
+        store[s] = st
+    n_slots = 64                      # fewer than the 32 + 47 + 21 pages of the three
+    pool = kq.Session(fmt, kvh, n_slots * P, fill=0x33)
+    win = kq.Window(n_slots)
+    model = kq.Window(n_slots)        # the same plan, host only, to predict the copies
+    h_pages = {s: torch.full((48,), -1, dtype=torch.int32).pin_memory() for s in lens}
+    m_pages = {s: np.full(48, -1, np.int32) for s in lens}
+    d_pages = torch.zeros(48, dtype=torch.int32, device=DEV)
+    q = kvsynth.queries(52, 0, 1, G * kvh, 128)
+    for s in (0, 1, 0, 2, 1, 1, 0):
+        n = lens[s]
+        npg = (n + P - 1) // P
+        copied = win.map(sh, store[s], s, npg, pool, h_pages[s], d_pages)
+        want_missed = model.plan(s, m_pages[s][:npg])
+        assert copied == len(want_missed)
+        y_win = decode(sh, [pool], [n], q, n, d_pages[:npg].contiguous(), npg)
+        y_res = decode(sh, [res[s]], [n], q, n)
+        assert np.array_equal(y_win, y_res), s
