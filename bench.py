@@ -489,6 +489,129 @@ def side_configs(kq, torch, steps=10, warmup=3):
             out["row_moves_int8"] = row_moves(kq, torch, sh, copies[0], copies[1], ctx)
         del copies, tabs, ws
         torch.cuda.empty_cache()
+    out.update(paged_and_streamed(kq, torch, steps, warmup))
+    return out
+
+
+def paged_and_streamed(kq, torch, steps, warmup):
+    """Paged sessions and the streamed window, int8.
+
+    paged_int8_ctx262144: the full 262144-cell single-session decode read through a
+    page table: identity pages over the session itself, and a pool whose 4096 pages of
+    64 cells sit at a seeded random permutation of its slots; set against the
+    contiguous decode of the same cache (two caches in turn, each larger than the
+    last-level cache).
+
+    streamed_int8_ctx32768: 4 sessions of 32768 cells in pinned host stores and a
+    1024-slot window (two sessions' worth).  Visiting them in the order 0,1,2,3,...
+    misses every page (each map copies a whole session over the host link); visiting
+    0,1,0,1,... hits every page after the first pass.  A step is kv_window_map + the
+    paged decode, timed by the host clock around the step and a synchronize."""
+    import kvsynth
+    out = {}
+    sm = 1 / math.sqrt(HD)
+    seed = kvsynth.WORKLOADS["full_ctx262144_48l"]["seed"]
+    sh = kq.make_shape(Q8, KVH, NQH, HD)
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    # ---- paged decode at the full context ------------------------------------
+    ctx, P = CTX, kq.KV_PAGE_ROWS
+    npg = ctx // P
+    dk = torch.from_numpy(kvsynth.kv_tokens(seed, 0, ctx, KVH, HD, "K", True)[None]).cuda()
+    dv = torch.from_numpy(kvsynth.kv_tokens(seed, 0, ctx, KVH, HD, "V", True)[None]).cuda()
+    a = kq.Session(Q8, KVH, ctx)
+    kq.kv_append(sh, kq.session_table([a.entry()]), zero, 1, ctx, dk, dv)
+    del dk, dv
+    perm = torch.from_numpy(np.random.default_rng(seed).permutation(npg).astype(np.int32)).cuda()
+    b = kq.Session(Q8, KVH, ctx)
+    for ta, tb in zip(a.tensors(), b.tensors()):   # page p of a -> slot perm[p] of b
+        tb.view(KVH, npg, -1)[:, perm.long()] = ta.view(KVH, npg, -1)
+    ident = torch.arange(npg, dtype=torch.int32, device="cuda")
+    tab_a, tab_b = kq.session_table([a.entry()]), kq.session_table([b.entry()])
+    ld = torch.full((1,), ctx, dtype=torch.int32, device="cuda")
+    q = torch.from_numpy(kvsynth.queries(seed, 0, 1, NQH, HD)).cuda()
+    ws = kq.kv_decode_workspace(sh, 1, ctx)
+    o = [torch.empty((1, NQH, HD), device="cuda") for _ in range(3)]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    calls = [lambda: kq.kv_decode_attn(sh, tab_a, ld, 1, ctx, q, sm, o[0], ws),
+             lambda: kq.kv_decode_attn_paged(sh, tab_b, perm, npg, ld, 1, ctx, q, sm, o[1], ws,
+                                             st),
+             lambda: kq.kv_decode_attn_paged(sh, tab_a, ident, npg, ld, 1, ctx, q, sm, o[2], ws,
+                                             st),
+             lambda: kq.kv_decode_attn_paged(sh, tab_b, perm, npg, ld, 1, ctx, q, sm, o[1], ws,
+                                             st)]
+    _time_calls(torch, calls, warmup)
+    t = _time_calls(torch, calls, steps)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(o[0], o[1]) and torch.equal(o[0], o[2]), "paged decode differs"
+    nb = decode_bytes(Q8, ctx)
+    t_res, t_perm, t_id = t[0], (t[1] + t[3]) / 2, t[2]
+    out["paged_int8_ctx262144"] = {
+        "workload": "int8 cache, 262144 cells, 4096 pages of 64 cells; two caches in turn",
+        "resident_us": t_res * 1e6, "paged_identity_us": t_id * 1e6,
+        "paged_permuted_us": t_perm * 1e6, "decode_bytes": nb,
+        "paged_permuted_GB_s": nb / t_perm / 1e9,
+        "paged_permuted_frac_hbm": nb / t_perm / 1e9 / HBM_PEAK_GBS,
+        "paging_overhead": t_perm / t_res - 1.0,
+        "outputs_bitwise_equal": True}
+    log(f"paged int8 262144: resident {t_res * 1e6:.1f} us, identity pages {t_id * 1e6:.1f} us, "
+        f"permuted pages {t_perm * 1e6:.1f} us ({nb / t_perm / 1e9:.0f} GB/s)")
+    del a, b, tab_a, tab_b, ws, perm, ident
+    torch.cuda.empty_cache()
+
+    # ---- streamed window ------------------------------------------------------
+    n, n_st, n_slots = 32768, 4, 1024
+    npg = n // P
+    stores, host_pages = [], []
+    for s in range(n_st):
+        xk = torch.from_numpy(kvsynth.kv_tokens(seed + 1 + s, 0, n, KVH, HD, "K", True)[None])
+        xv = torch.from_numpy(kvsynth.kv_tokens(seed + 1 + s, 0, n, KVH, HD, "V", True)[None])
+        tmp = kq.Session(Q8, KVH, n)
+        kq.kv_append(sh, kq.session_table([tmp.entry()]), zero, 1, n, xk.cuda(), xv.cuda())
+        hs = kq.Session(Q8, KVH, n, pinned=True)
+        for ta, tb in zip(tmp.tensors(), hs.tensors()):
+            tb.copy_(ta.cpu())
+        stores.append(hs)
+        host_pages.append(torch.full((npg,), -1, dtype=torch.int32).pin_memory())
+    del tmp
+    pool = kq.Session(Q8, KVH, n_slots * P)
+    tab = kq.session_table([pool.entry()])
+    d_pages = torch.zeros(npg, dtype=torch.int32, device="cuda")
+    ld = torch.full((1,), n, dtype=torch.int32, device="cuda")
+    ws = kq.kv_decode_workspace(sh, 1, n)
+    y = torch.empty((1, NQH, HD), device="cuda")
+    row_bytes = kq.kv_rows_bytes(sh, P)
+
+    def run(order):
+        win = kq.Window(n_slots)
+        for hp in host_pages:
+            hp.fill_(-1)
+        ts, copied = [], []
+        for i, s in enumerate(order):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            c = win.map(sh, stores[s], s, npg, pool, host_pages[s], d_pages)
+            kq.kv_decode_attn_paged(sh, tab, d_pages, npg, ld, 1, n, q, sm, y, ws, st)
+            torch.cuda.synchronize()
+            if i >= 2 * n_st:
+                ts.append(time.perf_counter() - t0)
+                copied.append(c)
+        return float(np.mean(ts)), float(np.mean(copied))
+
+    reps = 2 * n_st + max(steps, 8)
+    t_miss, c_miss = run([i % n_st for i in range(reps)])
+    t_hit, c_hit = run([i % 2 for i in range(reps)])
+    assert int(st.item()) == 0
+    miss_bytes = c_miss * row_bytes
+    out["streamed_int8_ctx32768"] = {
+        "workload": "4 int8 sessions of 32768 cells in pinned host stores, a 1024-slot "
+                    "window (2 sessions); a step = kv_window_map + paged decode, host clock",
+        "miss_step_us": t_miss * 1e6, "miss_pages_per_step": c_miss,
+        "miss_host_to_device_GB_s": miss_bytes / t_miss / 1e9,
+        "hit_step_us": t_hit * 1e6, "hit_pages_per_step": c_hit}
+    log(f"streamed int8 32768: all-miss step {t_miss * 1e6:.0f} us ({c_miss:.0f} pages, "
+        f"{miss_bytes / t_miss / 1e9:.1f} GB/s), all-hit step {t_hit * 1e6:.1f} us")
     return out
 
 

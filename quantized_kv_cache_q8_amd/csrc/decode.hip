@@ -245,23 +245,35 @@ static_assert(KVQ8_DEC_CH % 8 == 0 && ch_steps<8>() % 8 == 0,
 // a load reads it with one readlane.  A slot outside the pool reads slot 0 (the merge
 // flags the table).
 struct NoPages {
-  __device__ __forceinline__ uint32_t phys(int, uint32_t row) const { return row; }
-  __device__ __forceinline__ uint32_t phys2(int, int, bool, uint32_t row) const { return row; }
+  static constexpr bool paged = false;
 };
+// Paged sessions: the rows of a step (8 consecutive tokens, 8-aligned) lie in one
+// 64-row page, so a step's rows are one wave-uniform pool row plus the lane's row
+// within the step.
+// NR registers hold the slots of up to 64 NR steps per wave.
+template <int NR>
 struct PageMap {
-  int slot[4];
+  static_assert(NR == 2 || NR == 4, "2 or 4 registers of slots");
+  static constexpr bool paged = true;
+  int slot[NR];   // lane l, register j: the slot of the page of step l + 64 j
+  int last;      // the slot of the page holding row len - 1
+  int len;
   __device__ __forceinline__ void init(const int32_t* pages, int stride, int b, int gw, int W,
-                                       int n_steps, int n_slots, int lane) {
+                                       int n_steps, int n_slots, int len_, int lane) {
+    const int32_t* row = pages + (long long)b * stride;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NR; ++j) {
       const int k = lane + 64 * j;
       int sl = 0;
       if (k < n_steps) {
-        sl = pages[(long long)b * stride + (((gw + k * W) * 8) >> 6)];
+        sl = row[((gw + k * W) * 8) >> 6];
         if ((unsigned)sl >= (unsigned)n_slots) sl = 0;
       }
       slot[j] = sl;
     }
+    len = len_;
+    last = len_ > 0 ? row[(len_ - 1) >> 6] : 0;
+    if ((unsigned)last >= (unsigned)n_slots) last = 0;
   }
   // slot of step k (k the same in every lane)
   __device__ __forceinline__ int slot_of(int k) const {
@@ -269,14 +281,24 @@ struct PageMap {
     const int v = j == 0 ? slot[0] : j == 1 ? slot[1] : j == 2 ? slot[2] : slot[3];
     return __builtin_amdgcn_readlane(v, k & 63);
   }
-  // the pool row of logical row `row`, which lies in step k's page
-  __device__ __forceinline__ uint32_t phys(int k, uint32_t row) const {
-    return (uint32_t)slot_of(k) * KV_PAGE_ROWS + (row & (KV_PAGE_ROWS - 1));
+  // the slots of steps 64 (k / 64) .. 64 (k / 64) + 63, one per lane (k uniform)
+  __device__ __forceinline__ int block(int k) const {
+    const int j = k >> 6;
+    if constexpr (NR == 2) return j == 0 ? slot[0] : slot[1];
+    else return j == 0 ? slot[0] : j == 1 ? slot[1] : j == 2 ? slot[2] : slot[3];
   }
-  // the same for a row of step k1 (second) or k0 (first), chosen per lane
-  __device__ __forceinline__ uint32_t phys2(int k0, int k1, bool second, uint32_t row) const {
-    const uint32_t s0 = (uint32_t)slot_of(k0), s1 = (uint32_t)slot_of(k1);
-    return (second ? s1 : s0) * KV_PAGE_ROWS + (row & (KV_PAGE_ROWS - 1));
+  // step k of wave gw (stride W), v = block(k): pb, the pool row of its first row,
+  // and lim, its last row that holds a token (rows i > lim re-read row lim).  A step
+  // past the session's end reads the session's last step; every step k past the
+  // wave's own is one of them, so k needs no clamp.
+  __device__ __forceinline__ void step(int v, int k, int gw, int W, int& pb, int& lim) const {
+    const int s = (gw + k * W) * 8;
+    const bool past = s >= len;
+    const int s0 = past ? ((len - 1) & ~7) : s;
+    const int rl = __builtin_amdgcn_readlane(v, k & 63);   // always: a select, not a branch
+    const int sl = past ? last : rl;
+    pb = sl * KV_PAGE_ROWS + (s0 & (KV_PAGE_ROWS - 1));
+    lim = len - 1 - s0;
   }
 };
 
@@ -296,16 +318,35 @@ struct Batch {
   __device__ __forceinline__ void load(const char* vals, const char* scales, int gw, int W, int k,
                                        int len, int r, int c, int kmax = 1 << 30,
                                        const PM& pm = PM()) {
+    // paged: k is a multiple of U, which divides 64, so the batch's steps share one
+    // register of the page map
+    static_assert(64 % U == 0, "a batch lies in one 64-step block");
+    int pv = 0;
+    if constexpr (PM::paged) pv = pm.block(k);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int ku = min(k + u, kmax);
-      const uint32_t row = pm.phys(ku, (uint32_t)min((gw + ku * W) * 8 + r, len - 1));
-      if constexpr (FMT == KV_FMT_K8V4 && V) {
-        ch[u].load_v(vals, row, c);
-        sc[u] = ldg16(scales + (row * NQ4 + (c >> 1)) * 2);   // lane c: dims of block c / 2
+      const int ku = PM::paged ? k + u : min(k + u, kmax);
+      uint32_t row;
+      const char* vp = vals;
+      const char* sp = scales;
+      if constexpr (PM::paged) {
+        // the step's rows from a wave-uniform base: the loads take a scalar address
+        int pb, lim;
+        pm.step(pv, ku, gw, W, pb, lim);
+        constexpr size_t VROW = FMT == KV_FMT_F16 ? HD * 2 : (FMT == KV_FMT_K8V4 && V) ? HD / 2 : HD;
+        constexpr size_t SROW = (FMT == KV_FMT_K8V4 && V) ? NQ4 * 2 : NGRP * 2;
+        vp += (size_t)pb * VROW;
+        sp += (size_t)pb * SROW;
+        row = (uint32_t)min(r, lim);
       } else {
-        ch[u].load(vals, row, c);
-        if constexpr (FMT != KV_FMT_F16) sc[u] = ldg16(scales + (row * NGRP + (c >> 2)) * 2);
+        row = (uint32_t)min((gw + ku * W) * 8 + r, len - 1);
+      }
+      if constexpr (FMT == KV_FMT_K8V4 && V) {
+        ch[u].load_v(vp, row, c);
+        sc[u] = ldg16(sp + (row * NQ4 + (c >> 1)) * 2);   // lane c: dims of block c / 2
+      } else {
+        ch[u].load(vp, row, c);
+        if constexpr (FMT != KV_FMT_F16) sc[u] = ldg16(sp + (row * NGRP + (c >> 2)) * 2);
       }
     }
   }
@@ -395,11 +436,22 @@ struct KBatch {
                                        int len, int lane, int kmax = 1 << 30,
                                        const PM& pm = PM()) {
     const int n = lane & 15, kq = lane >> 4;
+    static_assert(64 % U == 0, "a batch lies in one 64-step block");
+    int pv = 0;
+    if constexpr (PM::paged) pv = pm.block(k);   // k: a multiple of U
 #pragma unroll
     for (int j = 0; j < U / 2; ++j) {
       const int k0 = min(k + 2 * j, kmax), k1 = min(k + 2 * j + 1, kmax);
-      const uint32_t row = pm.phys2(k0, k1, (n >> 3) != 0,
-                                    (uint32_t)min((gw + ((n >> 3) ? k1 : k0) * W) * 8 + (n & 7), len - 1));
+      uint32_t row;
+      if constexpr (PM::paged) {
+        int pb0, lim0, pb1, lim1;
+        pm.step(pv, k + 2 * j, gw, W, pb0, lim0);
+        pm.step(pv, k + 2 * j + 1, gw, W, pb1, lim1);
+        const bool second = (n >> 3) != 0;
+        row = (uint32_t)((second ? pb1 : pb0) + min(n & 7, second ? lim1 : lim0));
+      } else {
+        row = (uint32_t)min((gw + ((n >> 3) ? k1 : k0) * W) * 8 + (n & 7), len - 1);
+      }
 #pragma unroll
       for (int grp = 0; grp < NGRP; ++grp) {
         w[j][grp] = ldkv(kb, row * HD + grp * 64 + kq * 16);
@@ -421,7 +473,7 @@ static_assert(split_lds_bytes<1>() <= 160 * 1024 && split_lds_bytes<2>() <= 160 
                   split_lds_bytes<4>() <= 160 * 1024 && split_lds_bytes<8>() <= 160 * 1024,
               "a split workgroup fits in one CU's LDS");
 
-template <int FMT, int G, int U, bool PG>
+template <int FMT, int G, int U, int PG>
 __global__ __launch_bounds__(DEC_THREADS)
 __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int kvh,
@@ -452,10 +504,11 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
   const int gw = (grp ? Jf : 0) + gw0;           // first step of this wave
   const int W = Sb * GRP_WAVES;                  // waves per group of (session, head)
   const int n_steps = gw0 < Jg ? (Jg - 1 - gw0) / W + 1 : 0;
-  // paged: this wave's steps -> pool slots; rows past the last step re-read it
-  std::conditional_t<PG, PageMap, NoPages> pm{};
-  if constexpr (PG) pm.init(pages, page_stride, b, gw, W, n_steps, ss.cap / KV_PAGE_ROWS, lane);
-  const int kclamp = PG ? max(n_steps - 1, 0) : (1 << 30);
+  // paged (PG: the page map's registers, 0 for a contiguous session): this wave's
+  // steps -> pool slots; steps past the session's end read its last step
+  std::conditional_t<PG != 0, PageMap<PG ? PG : 4>, NoPages> pm{};
+  if constexpr (PG != 0) pm.init(pages, page_stride, b, gw, W, n_steps, ss.cap / KV_PAGE_ROWS, len, lane);
+  const int kclamp = 1 << 30;   // rows past len re-read row len - 1
 
   extern __shared__ float smem[];
   float* lg = smem + (grp ? GRP_WAVES * CH0 + wg * CH1 : wg * CH0) * 8 * G;  // logits, then p
@@ -825,7 +878,7 @@ constexpr int PAIR_MIN_STEPS = 32;
 // steps per pair the plan aims for at most, so that long sessions spread over many
 // workgroups (balance across CUs and sessions)
 constexpr int PAIR_TARGET_STEPS = 256;
-static_assert(PAIR_TARGET_STEPS <= 256, "a pair has at most 256 steps (the page map's registers)");
+static_assert(PAIR_TARGET_STEPS <= 256, "a pair has at most 256 steps (4 registers of page map)");
 
 template <int G>
 __host__ __device__ constexpr size_t pair_lds_bytes() {
@@ -834,7 +887,7 @@ __host__ __device__ constexpr size_t pair_lds_bytes() {
 }
 static_assert(pair_lds_bytes<8>() <= 160 * 1024, "a pair workgroup fits in one CU's LDS");
 
-template <int FMT, int G, int U, bool PG>
+template <int FMT, int G, int U, int PG>
 __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 2 : KVQ8_DEC_PAIR_WPE))) void k_decode_pair(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int kvh,
     const float* __restrict__ q, float qscale, float* __restrict__ ws_o,
@@ -863,9 +916,10 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
   const int n_steps = gw < J ? (J - 1 - gw) / W + 1 : 0;
   const int n_first = s_idx * PAIRS < J ? (J - 1 - s_idx * PAIRS) / W + 1 : 0;  // pair 0's
   const int n_chunks = (n_first + PAIR_CH - 1) / PAIR_CH;   // the same for every wave
-  // paged: this pair's steps -> pool slots
-  std::conditional_t<PG, PageMap, NoPages> pm{};
-  if constexpr (PG) pm.init(pages, page_stride, b, gw, W, n_steps, ss.cap / KV_PAGE_ROWS, lane);
+  // paged (PG: the page map's registers, 0 for a contiguous session): this pair's
+  // steps -> pool slots
+  std::conditional_t<PG != 0, PageMap<PG ? PG : 4>, NoPages> pm{};
+  if constexpr (PG != 0) pm.init(pages, page_stride, b, gw, W, n_steps, ss.cap / KV_PAGE_ROWS, len, lane);
 
   extern __shared__ float smem[];
   float* pb = smem + (size_t)pr * 2 * PAIR_CH * 8 * G;      // this pair's two chunk buffers
@@ -1258,10 +1312,10 @@ int resident_splits() {
   hipError_t e;
   if constexpr (use_pair<FMT>())
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, k_decode_pair<FMT, G, batch_rows<FMT, G>(), false>, DEC_THREADS, pair_lds_bytes<G>());
+        &per_cu, k_decode_pair<FMT, G, batch_rows<FMT, G>(), 0>, DEC_THREADS, pair_lds_bytes<G>());
   else
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, k_decode_split<FMT, G, batch_rows<FMT, G>(), false>, DEC_THREADS, split_lds_bytes<G>());
+        &per_cu, k_decode_split<FMT, G, batch_rows<FMT, G>(), 0>, DEC_THREADS, split_lds_bytes<G>());
   if (e != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
@@ -1297,14 +1351,37 @@ hipError_t launch_split(const kv_session* tab, const int32_t* lens, int n_sess, 
   constexpr int U = batch_rows<FMT, G>();
   static_assert(U == 1 || U == 2 || U == 4 || U == 8, "U must divide the group budgets / 2");
   dim3 grid(plan.S, kvh, n_sess), block(DEC_THREADS);
-  if constexpr (use_pair<FMT>())
-    hipLaunchKernelGGL((k_decode_pair<FMT, G, U, PG>), grid, block, pair_lds_bytes<G>(), st, tab,
-                       lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages,
-                       page_stride);
-  else
-    hipLaunchKernelGGL((k_decode_split<FMT, G, U, PG>), grid, block, split_lds_bytes<G>(), st,
-                       tab, lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages,
-                       page_stride);
+  if constexpr (use_pair<FMT>()) {
+    if constexpr (!PG) {
+      hipLaunchKernelGGL((k_decode_pair<FMT, G, U, 0>), grid, block, pair_lds_bytes<G>(), st, tab,
+                         lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages,
+                         page_stride);
+    } else {
+      // the page map in 2 registers when no pair has more than 128 steps, else in 4
+      // with V batches of at most 2 steps, so the V wave stays within its registers.
+      // A session of J_b steps runs on Sb = active_splits splits: Sb = S gives a pair
+      // at most ceil(J / (PAIRS S)) steps (J: the steps of max_len); a smaller Sb is
+      // at least Jf / (PAIRS MIN_STEPS), Jf >= J_b lead16 / 16, so a pair has at most
+      // 16 MIN_STEPS / lead16 steps.
+      static_assert(KVQ8_DEC_MIN_STEPS * 16 <= 128 * lead16<FMT>(),
+                    "a session short for the grid fits the 2-register page map");
+      const long long J = ((long long)max_len + 7) / 8;
+      const long long per_pair = (J + (long long)PAIRS * plan.S - 1) / ((long long)PAIRS * plan.S);
+      constexpr int U4 = U > 2 ? 2 : U;
+      if (per_pair <= 128)
+        hipLaunchKernelGGL((k_decode_pair<FMT, G, U, 2>), grid, block, pair_lds_bytes<G>(), st,
+                           tab, lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S,
+                           pages, page_stride);
+      else
+        hipLaunchKernelGGL((k_decode_pair<FMT, G, U4, 4>), grid, block, pair_lds_bytes<G>(), st,
+                           tab, lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S,
+                           pages, page_stride);
+    }
+  } else {
+    hipLaunchKernelGGL((k_decode_split<FMT, G, U, PG ? 4 : 0>), grid, block, split_lds_bytes<G>(),
+                       st, tab, lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S,
+                       pages, page_stride);
+  }
   return hipGetLastError();
 }
 

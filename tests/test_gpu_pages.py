@@ -71,6 +71,41 @@ def test_paged_decode_equals_resident(fmt, G):
     check_close(y_pag[0], want, f"paged fmt={fmt} G={G}")
 
 
+@pytest.mark.parametrize("fmt", [kq.KV_FMT_Q8, kq.KV_FMT_K8V4])
+def test_paged_long_batch_equals_resident(fmt):
+    """8 sessions of up to 65536 cells over 8 kv heads: the grid then gives a pair
+    more than 128 steps, which takes the wider page map."""
+    kvh, G, n = 8, 4, 65536
+    say(f"paged long batch fmt={fmt}")
+    lens = [65536, 41000, 65533, 12345, 65536, 300, 50001, 64]
+    sh = shape(fmt, kvh, G * kvh)
+    master = filled(fmt, kvh, n, n, 61)[0]
+    q = kvsynth.queries(62, 0, len(lens), G * kvh, 128)
+    # the split count from the workspace size: per split, nqh rows of HD + 1 floats
+    splits = kq.kv_decode_workspace_bytes(sh, len(lens), n) // (len(lens) * G * kvh * 129 * 4)
+    J = n // 8
+    assert -(-J // (4 * splits)) > 128, splits
+    y_res = decode(sh, [master] * len(lens), lens, q, n)
+    stride = n // P
+    n_pg = [(m + P - 1) // P for m in lens]
+    n_slots = sum(n_pg) + 5
+    perm = np.random.default_rng(63).permutation(n_slots).astype(np.int32)
+    table = np.zeros((len(lens), stride), np.int32)
+    pool = kq.Session(fmt, kvh, n_slots * P, fill=0)
+    k = 0
+    for b, npg in enumerate(n_pg):
+        table[b, :npg] = perm[k:k + npg]
+        k += npg
+        idx = torch.from_numpy(table[b, :npg].astype(np.int64)).to(DEV)
+        for a, d in zip(master.tensors(), pool.tensors()):
+            d.view(kvh, n_slots, -1)[:, idx] = a.view(kvh, n // P, -1)[:, :npg]
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y_pag = decode(sh, [pool] * len(lens), lens, q, n, torch.from_numpy(table).to(DEV), stride,
+                   status)
+    assert int(status.item()) == 0
+    assert np.array_equal(y_pag, y_res)
+
+
 def test_paged_batch_and_bad_page():
     fmt, kvh, G = kq.KV_FMT_Q8, 8, 4
     say("paged batch")
