@@ -57,7 +57,9 @@ def test_paged_decode_equals_resident(fmt, G):
     n_pages = (n + P - 1) // P
     n_slots = 80
     perm = np.random.default_rng(fmt * 10 + G).permutation(n_slots)[:n_pages].astype(np.int32)
-    pool = kq.Session(fmt, kvh, n_slots * P, fill=0x5A)
+    # 0xFF bytes: NaN fp16 values and scales wherever the pool was not written, so a
+    # read of a row past the session's end (0 weight or not) would show in the output
+    pool = kq.Session(fmt, kvh, n_slots * P, fill=0xFF)
     copy_pages(sess, pool, perm, n_pages)
     pages = torch.from_numpy(perm).to(DEV)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -91,7 +93,7 @@ def test_paged_long_batch_equals_resident(fmt):
     n_slots = sum(n_pg) + 5
     perm = np.random.default_rng(63).permutation(n_slots).astype(np.int32)
     table = np.zeros((len(lens), stride), np.int32)
-    pool = kq.Session(fmt, kvh, n_slots * P, fill=0)
+    pool = kq.Session(fmt, kvh, n_slots * P, fill=0xFF)   # NaN where not written
     k = 0
     for b, npg in enumerate(n_pg):
         table[b, :npg] = perm[k:k + npg]
@@ -117,7 +119,7 @@ def test_paged_batch_and_bad_page():
     y_res = decode(sh, sessions, lens, q, max_len)
     stride = (max_len + P - 1) // P
     n_slots = sum((n + P - 1) // P for n in lens) + 7
-    pool = kq.Session(fmt, kvh, n_slots * P, fill=0)
+    pool = kq.Session(fmt, kvh, n_slots * P, fill=0xFF)   # NaN where not written
     perm = np.random.default_rng(5).permutation(n_slots).astype(np.int32)
     table = np.zeros((len(lens), stride), np.int32)
     k = 0
@@ -156,7 +158,7 @@ def test_streamed_window_equals_resident(fmt):
             b.copy_(a.cpu())
         store[s] = st
     n_slots = 64                      # fewer than the 32 + 47 + 21 pages of the three
-    pool = kq.Session(fmt, kvh, n_slots * P, fill=0x33)
+    pool = kq.Session(fmt, kvh, n_slots * P, fill=0xFF)   # NaN where not written
     win = kq.Window(n_slots)
     model = kq.Window(n_slots)        # the same plan, host only, to predict the copies
     h_pages = {s: torch.full((48,), -1, dtype=torch.int32).pin_memory() for s in lens}
