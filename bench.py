@@ -36,8 +36,6 @@ sys.path.insert(0, ROOT)
 METRIC = "decode-attn KV read GB/s (% HBM peak) at 262144 ctx, fp16 & int8; append cells/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix, vendor figure
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed FMA), vendor figure
-DECODE_FLOP_PER_TOKEN_HEAD = 2048  # per (context token, kv head): 4 heads x 128 dims x 2 x 2
 KVH, NQH, HD, CTX, LAYERS = 8, 32, 128, 262144, 48
 F16, Q8, K8V4 = 0, 1, 2
 BYTES_PER_CELL_HEAD = {F16: 2 * HD * 2, Q8: 2 * (HD + 2 * (HD // 64)),      # K+V per (cell, kv head)
@@ -309,9 +307,11 @@ def traffic_summary(fetch_dir, write_dir, command):
         "fetch_factor": f_fac, "write_factor": w_fac}}
     ids = sorted(fetch)
     for fmt, key in ((F16, "decode_f16"), (Q8, "decode_int8")):
-        # one kv_decode_attn call = one split kernel (k_decode_split for FP16, k_decode_pair
-        # for int8) then one k_decode_merge<fmt>
-        tags = (f"k_decode_split<{fmt},", f"k_decode_pair<{fmt},")
+        # one kv_decode_attn call = one split kernel (k_decode_split for FP16,
+        # k_decode_pair_mv for int8 at 1, 2 or 4 query heads per kv head, else
+        # k_decode_pair) then one k_decode_merge<fmt>
+        tags = (f"k_decode_split<{fmt},", f"k_decode_pair<{fmt},") + \
+            (("k_decode_pair_mv<",) if fmt == Q8 else ())
         splits = [i for i in ids if any(t in fetch[i][0] for t in tags)]
         per = []
         for i in splits:
@@ -809,23 +809,14 @@ def main():
         roof[fmt] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS,
                      "traffic": load_traffic(key, source_hash("decode.hip")),
-                     "kernel": ("k_decode_split" if fmt == F16 else "k_decode_pair") +
+                     "kernel": ("k_decode_split" if fmt == F16 else "k_decode_pair_mv") +
                                " + k_decode_merge (one kv_decode_attn call)",
                      "avg_us": avg * 1e6, "algorithmic_bytes_per_launch": per_launch,
                      "tokens_per_s_48_layers": 1.0 / (avg * LAYERS)}
         if fmt == Q8:
-            # the int8 decode's V pass runs on the vector ALU (its K logits on the matrix
-            # cores): the V arithmetic set against the vector ALU peak
-            flop = DECODE_FLOP_PER_TOKEN_HEAD // 2 * KVH * float(
-                np.mean([length + s + 1 for s in range(n_steps)]))
-            tf = flop / avg / 1e12
-            roof[fmt]["alu_view"] = {
-                "bound": "alu", "achieved": tf, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": tf / FP32_VECTOR_PEAK_TFLOPS, "algorithmic_flop_per_launch": flop,
-                "peak_without_packed_fma": FP32_VECTOR_PEAK_TFLOPS / 2,
-                "note": "the V pass: 1024 flop per (token, kv head) = 4 query heads x 128 dims "
-                        "x 2; packed fp32 FMA, half of the peak, is not used; the K logits run "
-                        "as int8 matrix products"}
+            roof[fmt]["note"] = ("both products on the matrix cores (K logits as int8, the V "
+                                 "sums as bf16 with fp32 accumulation); the kernel is bound by "
+                                 "the HBM stream")
         log(f"fmt={fmt}: {avg * 1e6:.1f} us/layer, {ach:.0f} GB/s ({ach / HBM_PEAK_GBS:.1%})")
     dominant = F16 if roof[F16]["avg_us"] >= roof[Q8]["avg_us"] else Q8
     del model

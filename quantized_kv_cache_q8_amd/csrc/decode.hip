@@ -258,6 +258,7 @@ struct PageMap {
   int slot[NR];   // lane l, register j: the slot of the page of step l + 64 j
   int last;      // the slot of the page holding row len - 1
   int len;
+  int nst;       // the wave's steps (n_steps)
   __device__ __forceinline__ void init(const int32_t* pages, int stride, int b, int gw, int W,
                                        int n_steps, int n_slots, int len_, int lane) {
     const int32_t* row = pages + (long long)b * stride;
@@ -272,6 +273,7 @@ struct PageMap {
       slot[j] = sl;
     }
     len = len_;
+    nst = n_steps;
     last = len_ > 0 ? row[(len_ - 1) >> 6] : 0;
     if ((unsigned)last >= (unsigned)n_slots) last = 0;
   }
@@ -289,16 +291,27 @@ struct PageMap {
   }
   // step k of wave gw (stride W), v = block(k): pb, the pool row of its first row,
   // and lim, its last row that holds a token (rows i > lim re-read row lim).  A step
-  // past the session's end reads the session's last step; every step k past the
-  // wave's own is one of them, so k needs no clamp.
+  // past the wave's own (its tokens are masked; in a grouped kernel it may still lie
+  // inside the session, on a page this wave has not mapped) or past the session's
+  // end reads the session's last step, so k needs no clamp.
   __device__ __forceinline__ void step(int v, int k, int gw, int W, int& pb, int& lim) const {
     const int s = (gw + k * W) * 8;
-    const bool past = s >= len;
+    const bool past = s >= len || k >= nst;
     const int s0 = past ? ((len - 1) & ~7) : s;
     const int rl = __builtin_amdgcn_readlane(v, k & 63);   // always: a select, not a branch
     const int sl = past ? last : rl;
     pb = sl * KV_PAGE_ROWS + (s0 & (KV_PAGE_ROWS - 1));
     lim = len - 1 - s0;
+  }
+  // the pool row of row i of step k, k per lane within one 64-step block (v = block of
+  // that block)
+  __device__ __forceinline__ uint32_t lane_row(int v, int k, int gw, int W, int i) const {
+    const int s = (gw + k * W) * 8;
+    const bool past = s >= len || k >= nst;
+    const int s0 = past ? ((len - 1) & ~7) : s;
+    const int sk = __shfl(v, k & 63, 64);
+    const int sl = past ? last : sk;
+    return (uint32_t)(sl * KV_PAGE_ROWS + (s0 & (KV_PAGE_ROWS - 1)) + min(i, len - 1 - s0));
   }
 };
 
@@ -1197,6 +1210,421 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
   }
 }
 
+// k_decode_pair_mv: the q8 format (1, 2 or 4 query heads per kv head) with both
+//   products on the matrix cores, in the pairs of k_decode_pair.
+//   K wave: the logits as in k_decode_pair; then, per 64-token block (8 steps), the
+//     weights w = p * (V scale of the token's 64-dim group), each split into two bf16
+//     values, hi = w truncated to bf16 and lo = (w - hi) rounded to bf16
+//     (|w - hi - lo| <= 2^-16 |w|), written to LDS in the layout of an MFMA A operand:
+//     16 rows (64-dim group, head, hi / lo) by the block's 64 tokens.
+//   V wave: stages the block's V rows in an LDS tile as loaded and reads them back
+//     transposed (ds_read_b64_tr_b8: 16 lanes receive one dim each, 8 tokens per
+//     read); the int8 codes become bf16 exactly (an integer of at most 7 bits is the
+//     upper half of its fp32 value), and one v_mfma_f32_16x16x32_bf16 per 16 dims and
+//     32 tokens accumulates the rows' products in fp32.  The block's 64 tokens are the
+//     k-slots of both operands in the same order.  Lane (q, i) of a 16-dim tile holds
+//     rows 4q .. 4q + 3; the tiles of group 0 use rows 0 .. 7, those of group 1 rows
+//     8 .. 15, so each tile's other half is discarded.
+//   Against the vector V pass this moves the 64 FMAs a lane spends per step and 4
+//   heads onto the matrix cores; the V wave keeps 12 conversions per 8 codes.
+#ifndef KVQ8_DEC_MV
+#define KVQ8_DEC_MV 1   // 0: the int8 decode keeps the vector V pass
+#endif
+#ifndef KVQ8_DEC_MV_CH
+#define KVQ8_DEC_MV_CH 16
+#endif
+constexpr int MV_CH = KVQ8_DEC_MV_CH;  // steps per chunk
+constexpr int MV_BLK = 8;              // steps per 64-token block
+constexpr int MV_PITCH = 144;          // bytes per V tile row (16-byte aligned rows)
+constexpr int MV_AROW = 32;            // weight-table bytes per token (16 bf16 rows)
+static_assert(MV_CH % (2 * MV_BLK) == 0, "a chunk holds whole pairs of blocks");
+
+template <int G>
+__host__ __device__ constexpr size_t mv_pair_bytes() {
+  // logits of one chunk, the weight tables of two chunks, the rescale factors of two
+  // chunks, the V tile
+  return (size_t)MV_CH * 8 * G * 4 + 2 * (size_t)MV_CH * 8 * MV_AROW + 2 * 4 * 4 +
+         64 * MV_PITCH;
+}
+template <int G>
+__host__ __device__ constexpr size_t mv_lds_bytes() {
+  return PAIRS * mv_pair_bytes<G>() + DEC_WAVES * 64 * 4;
+}
+static_assert(mv_pair_bytes<4>() % 16 == 0 && mv_pair_bytes<2>() % 16 == 0 &&
+                  mv_pair_bytes<1>() % 16 == 0, "pair regions keep 16-byte alignment");
+static_assert(PAIRS * mv_pair_bytes<1>() >= sizeof(float) * (PAIRS * 4 * HD + 2 * PAIRS * 4),
+              "the final partials fit in the pair regions");
+
+// max(a, b) in one instruction (the median of a, b and +inf; no NaN quieting)
+__device__ __forceinline__ float max2(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, INFINITY);
+}
+// Max over the wave, returned wave-uniform, with cross-lane moves only: the four
+// in-row stages, then each row's lane 15 into the next row, lane 31 into rows 2 and 3;
+// lane 63 then holds the whole wave's max.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = max2(v, dpp<DPP_QUAD_XOR1>(v));
+  v = max2(v, dpp<DPP_QUAD_XOR2>(v));
+  v = max2(v, dpp<DPP_ROW_HALF_MIRROR>(v));
+  v = max2(v, dpp<DPP_ROW_MIRROR>(v));
+  const int iv = __builtin_bit_cast(int, v);
+  v = max2(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iv, iv, 0x142, 0xA, 0xF, false)));
+  const int iw = __builtin_bit_cast(int, v);
+  v = max2(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iw, iw, 0x143, 0xC, 0xF, false)));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+#define KVQ8_LDS __attribute__((address_space(3)))
+// transposing 8-byte LDS read: within each 16 lanes, lane i receives byte i % 8 of
+// the 8 bytes addressed by lanes 2 j + i / 8, j = 0 .. 7
+__device__ __forceinline__ i32x2 lds_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((KVQ8_LDS i32x2*)(KVQ8_LDS uint8_t*)p);
+}
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 8 int8 codes (the bytes of c, in order) as 8 bf16, exactly: the upper half of each
+// code's fp32 value
+__device__ __forceinline__ bf16x8 codes_bf16(i32x2 c) {
+  uint32_t o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const uint32_t src = (uint32_t)(d < 2 ? c.x : c.y);
+    const uint32_t f0 = __builtin_bit_cast(uint32_t, i8_to_f32(src, 2 * (d & 1)));
+    const uint32_t f1 = __builtin_bit_cast(uint32_t, i8_to_f32(src, 2 * (d & 1) + 1));
+    o[d] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+  }
+  return __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
+}
+template <int G, int PG>
+__global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_PAIR_WPE)))
+void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restrict__ lens,
+                      int max_len, int kvh, const float* __restrict__ q, float qscale,
+                      float* __restrict__ ws_o, float* __restrict__ ws_lse, int S,
+                      const int32_t* __restrict__ pages, int page_stride) {
+  constexpr int FMT = KV_FMT_Q8;
+  static_assert(G <= 4, "one block of 4 heads");
+  constexpr int UK = k_batch_rows<G>();
+  static_assert(MV_CH % (2 * UK) == 0, "a chunk holds whole pairs of K batches");
+  constexpr int NCB = MV_CH / MV_BLK;            // blocks per chunk
+  const int s_idx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nqh = kvh * G;
+  const kv_session ss = tab[b];
+  const int len = lens[b];
+  // workgroup-uniform exits only (the loops below have barriers)
+  if (session_bad(ss, FMT) || len < 0 || len > ss.cap || len > max_len) return;  // merge flags
+  const int J = (len + 7) >> 3;
+  const int Sb = active_splits<FMT>(len, S);
+  if (s_idx >= Sb) return;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int r = lane >> 3, c = lane & 7;
+  const bool kw = wave >= PAIRS;
+  const int pr = wave & (PAIRS - 1);
+  const int gw = s_idx * PAIRS + pr;
+  const int W = Sb * PAIRS;
+  const int n_steps = gw < J ? (J - 1 - gw) / W + 1 : 0;
+  const int n_first = s_idx * PAIRS < J ? (J - 1 - s_idx * PAIRS) / W + 1 : 0;
+  const int n_chunks = (n_first + MV_CH - 1) / MV_CH;
+  const int kmax = max(n_steps - 1, 0);
+  const int total = n_chunks * MV_CH;
+  // paged (PG: the page map's registers, 0 for a contiguous session): this pair's
+  // steps -> pool slots; steps past the session's end read its last step
+  std::conditional_t<PG != 0, PageMap<PG ? PG : 4>, NoPages> pm{};
+  if constexpr (PG != 0) pm.init(pages, page_stride, b, gw, W, n_steps, ss.cap / KV_PAGE_ROWS, len, lane);
+
+  extern __shared__ float smem[];
+  uint8_t* reg = reinterpret_cast<uint8_t*>(smem) + (size_t)pr * mv_pair_bytes<G>();
+  float* lc = reinterpret_cast<float*>(reg);                               // [CH*8][G]
+  uint8_t* at = reg + (size_t)MV_CH * 8 * G * 4;                           // [2][CH*8][AROW]
+  float* fb = reinterpret_cast<float*>(at + 2 * MV_CH * 8 * MV_AROW);       // [2][4]
+  uint8_t* tile = reinterpret_cast<uint8_t*>(fb + 8);                      // [64][PITCH]
+  float* junk = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem) +
+                                         PAIRS * mv_pair_bytes<G>()) + wave * 64;
+  // after the loops every pair region is free: the partials reuse them
+  float* o_l = smem;                         // [pairs][G][HD]
+  float* m_l = o_l + PAIRS * G * HD;         // [pairs][G]
+  float* l_l = m_l + PAIRS * G;              // [pairs][G]
+
+  const size_t hrow = (size_t)h * (size_t)ss.cap;
+  const char* kb = static_cast<const char*>(ss.k) + hrow * HD;
+  const char* vb = static_cast<const char*>(ss.v) + hrow * HD;
+  const char* ksb = reinterpret_cast<const char*>(ss.k_scale) + hrow * NGRP * 2;
+  const char* vsb = reinterpret_cast<const char*>(ss.v_scale) + hrow * NGRP * 2;
+
+  if (kw) {
+    // ================= K wave ===================================================
+    float m[G], l[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+    }
+    i32x4 aq[NGRP];
+    float qs[NGRP][QLEV];
+    {
+      const int mrow = lane & 15, kq = lane >> 4;
+      const int ga = mrow >> 2, lev = mrow & 3;
+#pragma unroll
+      for (int grp = 0; grp < NGRP; ++grp) {
+        const float* qp =
+            q + ((long long)b * nqh + h * G + min(ga, G - 1)) * HD + grp * 64 + kq * 16;
+        float x[16];
+        float mx = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u32x4 v = ldg128(qp + 4 * k);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[4 * k + e] = as_f32(v[e]) * qscale;
+            mx = fmaxf(mx, fabsf(x[4 * k + e]));
+          }
+        }
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        float sl[QLEV];
+        sl[0] = mx > 0.f ? mx / 127.f : 1.f;
+#pragma unroll
+        for (int lv = 1; lv < QLEV; ++lv) sl[lv] = sl[lv - 1] * QBASE_INV;
+        const bool live = ga < G && lev < QLEV;
+        uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float rr = x[i];
+          int a = 0;
+#pragma unroll
+          for (int lv = 0; lv < QLEV; ++lv) {
+            const int al = q_level(rr, sl[lv]);
+            a = lv == lev ? al : a;
+          }
+          wd[i >> 2] |= (uint32_t)((live ? a : 0) & 0xFF) << (8 * (i & 3));
+        }
+        aq[grp] = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+#pragma unroll
+        for (int lv = 0; lv < QLEV; ++lv) qs[grp][lv] = __shfl(sl[lv], 4 * kq, 64);
+      }
+    }
+    auto kstep = [&](const KBatch<UK>& cur, int kr) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j = 0; j < UK / 2; ++j) {
+        float v = 0.f;
+#pragma unroll
+        for (int grp = 0; grp < NGRP; ++grp) {
+          const u32x4& bw = cur.w[j][grp];
+          const i32x4 bk = i32x4{(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3]};
+          const i32x4 d =
+              __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[grp], bk, i32x4{0, 0, 0, 0}, 0, 0, 0);
+          const float lv = fmaf((float)d[2], qs[grp][2],
+                                fmaf((float)d[1], qs[grp][1], (float)d[0] * qs[grp][0]));
+          v = fmaf(lv, h2f(cur.sc[j][grp]), v);
+        }
+        const int g = lane >> 4;
+        float* dst = g < G ? lc + ((kr + 2 * j) * 8 + (lane & 15)) * G + g : junk + lane;
+        *dst = v;
+      }
+    };
+    KBatch<UK> KA, KB;
+    uint32_t svn[NCB];   // the chunk's V scales, loaded as it starts
+    if (total > 0) KA.load(kb, ksb, gw, W, 0, len, lane, kmax, pm);
+    for (int k0 = 0; k0 < total; k0 += 2 * UK) {
+      const int ch = k0 / MV_CH, kr = k0 - ch * MV_CH;
+      if (kr == 0) {
+#pragma unroll
+        for (int bl = 0; bl < NCB; ++bl) {
+          const int st = ch * MV_CH + bl * 8 + (lane >> 3);
+          uint32_t row;
+          if constexpr (PG != 0)
+            row = pm.lane_row(pm.block(ch * MV_CH + bl * 8), st, gw, W, lane & 7);
+          else
+            row = (uint32_t)min((gw + min(st, kmax) * W) * 8 + (lane & 7), len - 1);
+          svn[bl] = *(const KVQ8_GLOBAL uint32_t*)(vsb + row * NGRP * 2);
+        }
+      }
+      KB.load(kb, ksb, gw, W, k0 + UK, len, lane, kmax, pm);
+      kstep(KA, kr);
+      KA.load(kb, ksb, gw, W, k0 + 2 * UK, len, lane, kmax, pm);
+      kstep(KB, kr + UK);
+      if (kr + 2 * UK == MV_CH) {
+        wave_lds_fence();
+        // the chunk's softmax, then per block the weight table
+        const int c0 = ch * MV_CH;
+        const int nl = max(0, min(n_steps, c0 + MV_CH) - c0) * 8;
+        float mc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) mc[g] = -INFINITY;
+#pragma unroll
+        for (int bl = 0; bl < NCB; ++bl) {
+          const int tl = bl * 64 + lane;
+          const int t = (gw + (c0 + (tl >> 3)) * W) * 8 + (tl & 7);
+          if (tl < nl && t < len) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) mc[g] = max2(mc[g], lc[tl * G + g]);
+          }
+        }
+        float* fc = fb + (ch & 1) * 4;
+        float cm[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) cm[g] = wave_max_dpp(mc[g]);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float mn = max2(m[g], cm[g]);
+          const float f = mn == -INFINITY ? 1.f : exp2f(m[g] - mn);
+          m[g] = mn;
+          l[g] *= f;
+          if (lane == g) fc[g] = f;
+        }
+        uint8_t* atc = at + (ch & 1) * MV_CH * 8 * MV_AROW;
+#pragma unroll
+        for (int bl = 0; bl < NCB; ++bl) {
+          const int tl = bl * 64 + lane;
+          const int st = c0 + (tl >> 3);
+          const int t = (gw + st * W) * 8 + (tl & 7);
+          const bool ok = tl < nl && t < len;
+          const uint32_t svw = svn[bl];
+          const float sv[NGRP] = {h2f((uint16_t)(svw & 0xFFFFu)), h2f((uint16_t)(svw >> 16))};
+          // the weights w = p * s_v and their bf16 split: hi = w truncated to bf16, lo =
+          // the rest rounded to bf16 (|w - hi - lo| <= 2^-16 |w|)
+          float w[4][NGRP];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            float p = 0.f;
+            if (g < G) {
+              p = ok ? exp2f(lc[tl * G + g] - m[g]) : 0.f;
+              l[g] += p;
+            }
+#pragma unroll
+            for (int grp = 0; grp < NGRP; ++grp) w[g][grp] = p * sv[grp];
+          }
+          // A operand layout: row m = 8 grp + 2 head + part, token k = lane = 8 g8 + j
+          // at byte (g8 16 + (m ^ g8)) 16 + 2 j of the block's 2 KB
+          uint8_t* atb = atc + (size_t)bl * 64 * MV_AROW;
+          const int g8 = lane >> 3, jt = lane & 7;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+#pragma unroll
+            for (int grp = 0; grp < NGRP; ++grp) {
+              const uint32_t wb = __builtin_bit_cast(uint32_t, w[g][grp]);
+              const uint32_t hib = wb & 0xFFFF0000u;
+              const float lo = w[g][grp] - __builtin_bit_cast(float, hib);
+              const uint16_t lob = __builtin_bit_cast(uint16_t, (__bf16)lo);
+              const int m0 = 8 * grp + 2 * g;
+              *reinterpret_cast<uint16_t*>(atb + (g8 * 16 + (m0 ^ g8)) * 16 + 2 * jt) =
+                  (uint16_t)(hib >> 16);
+              *reinterpret_cast<uint16_t*>(atb + (g8 * 16 + ((m0 + 1) ^ g8)) * 16 + 2 * jt) = lob;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    __syncthreads();   // the V wave's last chunk
+#pragma unroll
+    for (int g = 0; g < G; ++g) l[g] = wave_sum(l[g]);
+    if (lane == 0) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        m_l[pr * G + g] = m[g];
+        l_l[pr * G + g] = l[g];
+      }
+    }
+  } else {
+    // ================= V wave ===================================================
+    const int qv = lane >> 4, iv = lane & 15;
+    // D tile jd (dims 16 jd ..): lane (qv, iv) holds rows 4 qv .. 4 qv + 3 of dim
+    // 16 jd + iv, rows m = 8 grp + 2 head + part; heads ha, ha + 1 of this lane
+    const int ha = 2 * (qv & 1);
+    f32x4 acc[8];
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) acc[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto vload = [&](u32x4 (&vw)[MV_BLK], int blk) __attribute__((always_inline)) {
+      int pv = 0;
+      if constexpr (PG != 0) pv = pm.block(blk * MV_BLK);   // the block's 8 steps share it
+#pragma unroll
+      for (int u = 0; u < MV_BLK; ++u) {
+        if constexpr (PG != 0) {
+          int pb, lim;
+          pm.step(pv, blk * MV_BLK + u, gw, W, pb, lim);
+          vw[u] = ldkv(vb + (size_t)pb * HD, (uint32_t)min(r, lim) * HD + c * 16);
+        } else {
+          const uint32_t row =
+              (uint32_t)min((gw + min(blk * MV_BLK + u, kmax) * W) * 8 + r, len - 1);
+          vw[u] = ldkv(vb, row * HD + c * 16);
+        }
+      }
+    };
+    auto vblock = [&](const u32x4 (&vw)[MV_BLK], int blk) __attribute__((always_inline)) {
+      const int ch = blk / NCB, bl = blk - ch * NCB;
+      if (bl == 0) {
+        if (ch > 0) __syncthreads();   // the K wave's chunk ch
+        const float fa = fb[(ch & 1) * 4 + min(ha, G - 1)];
+        const float fc = fb[(ch & 1) * 4 + min(ha + 1, G - 1)];
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) {
+          acc[jd][0] *= fa;
+          acc[jd][1] *= fa;
+          acc[jd][2] *= fc;
+          acc[jd][3] *= fc;
+        }
+      }
+      // the block's rows, token u * 8 + r, as loaded
+#pragma unroll
+      for (int u = 0; u < MV_BLK; ++u)
+        *reinterpret_cast<u32x4*>(tile + (u * 8 + r) * MV_PITCH + c * 16) = vw[u];
+      wave_lds_fence();
+      const uint8_t* atb = at + (ch & 1) * MV_CH * 8 * MV_AROW + bl * 64 * MV_AROW;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int g8 = 4 * hh + qv;   // tokens 8 g8 .. 8 g8 + 7 of the block
+        const bf16x8 aw = *reinterpret_cast<const bf16x8*>(atb + (g8 * 16 + (iv ^ g8)) * 16);
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) {
+          // B: the codes of tokens 8 g8 + 0 .. 7, dim 16 jd + iv, as bf16 (exact)
+          const i32x2 cb = lds_tr8(tile + (8 * g8 + (iv >> 1)) * MV_PITCH + 16 * jd + 8 * (iv & 1));
+          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, codes_bf16(cb), acc[jd], 0, 0, 0);
+        }
+      }
+      wave_lds_fence();
+    };
+    const int nblk = total / MV_BLK;
+    u32x4 VA[MV_BLK], VB[MV_BLK];
+    if (nblk > 0) vload(VA, 0);
+    __syncthreads();   // the K wave's first chunk
+    for (int blk = 0; blk < nblk; blk += 2) {
+      vload(VB, blk + 1);
+      vblock(VA, blk);
+      vload(VA, blk + 2);
+      vblock(VB, blk + 1);
+    }
+    if (nblk > 0) __syncthreads();   // frees the K wave's last buffers
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) {
+      if ((qv >> 1) == (jd >> 2)) {   // this lane's rows are of the tile's group
+        if (ha < G) o_l[(pr * G + ha) * HD + jd * 16 + iv] = acc[jd][0] + acc[jd][1];
+        if (ha + 1 < G) o_l[(pr * G + ha + 1) * HD + jd * 16 + iv] = acc[jd][2] + acc[jd][3];
+      }
+    }
+  }
+  // ---- combine the pair partials of the workgroup ----------------------------
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * HD; idx += DEC_THREADS) {
+    const int g = idx / HD, d = idx % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < PAIRS; ++w) M = fmaxf(M, m_l[w * G + g]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < PAIRS; ++w) {
+      const float mw = m_l[w * G + g];
+      if (mw == -INFINITY) continue;
+      const float f = exp2f(mw - M);
+      L += l_l[w * G + g] * f;
+      O += o_l[(w * G + g) * HD + d] * f;
+    }
+    const long long qrow = ((long long)b * nqh + h * G + g) * S + s_idx;
+    ws_o[qrow * HD + d] = O / L;
+    if (d == 0) ws_lse[qrow] = M + log2f(L);
+  }
+}
+
 // One wave per (session, query head), MERGE_WAVES heads per workgroup.  Splits are
 // taken 64 at a time: lane k loads split j0 + k's lse (one vector load), the wave
 // reduces the chunk's max and weight sum, and the o rows of the chunk (one float2
@@ -1297,6 +1725,9 @@ constexpr int batch_rows() {
 
 template <int FMT>
 constexpr bool use_pair() { return KVQ8_DEC_PAIR && FMT != KV_FMT_F16; }
+// the q8 format with 1, 2 or 4 query heads per kv head: V products on the matrix cores
+template <int FMT, int G>
+constexpr bool use_mv() { return KVQ8_DEC_MV && use_pair<FMT>() && FMT == KV_FMT_Q8 && G <= 4; }
 
 
 // Split workgroups of one kernel instance that fit on the current device at once
@@ -1310,7 +1741,10 @@ int resident_splits() {
   if (v > 0) return v;
   int per_cu = 0, cus = 0;
   hipError_t e;
-  if constexpr (use_pair<FMT>())
+  if constexpr (use_mv<FMT, G>())
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_pair_mv<G, 0>, DEC_THREADS,
+                                                     mv_lds_bytes<G>());
+  else if constexpr (use_pair<FMT>())
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
         &per_cu, k_decode_pair<FMT, G, batch_rows<FMT, G>(), 0>, DEC_THREADS, pair_lds_bytes<G>());
   else
@@ -1351,7 +1785,23 @@ hipError_t launch_split(const kv_session* tab, const int32_t* lens, int n_sess, 
   constexpr int U = batch_rows<FMT, G>();
   static_assert(U == 1 || U == 2 || U == 4 || U == 8, "U must divide the group budgets / 2");
   dim3 grid(plan.S, kvh, n_sess), block(DEC_THREADS);
-  if constexpr (use_pair<FMT>()) {
+  if constexpr (use_mv<FMT, G>()) {
+    // the page map's registers as for k_decode_pair below
+    const long long J = ((long long)max_len + 7) / 8;
+    const long long per_pair = (J + (long long)PAIRS * plan.S - 1) / ((long long)PAIRS * plan.S);
+    if constexpr (!PG)
+      hipLaunchKernelGGL((k_decode_pair_mv<G, 0>), grid, block, mv_lds_bytes<G>(), st, tab, lens,
+                         max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages,
+                         page_stride);
+    else if (per_pair <= 128)
+      hipLaunchKernelGGL((k_decode_pair_mv<G, 2>), grid, block, mv_lds_bytes<G>(), st, tab, lens,
+                         max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages,
+                         page_stride);
+    else
+      hipLaunchKernelGGL((k_decode_pair_mv<G, 4>), grid, block, mv_lds_bytes<G>(), st, tab, lens,
+                         max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages,
+                         page_stride);
+  } else if constexpr (use_pair<FMT>()) {
     if constexpr (!PG) {
       hipLaunchKernelGGL((k_decode_pair<FMT, G, U, 0>), grid, block, pair_lds_bytes<G>(), st, tab,
                          lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages,
