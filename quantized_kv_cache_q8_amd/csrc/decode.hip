@@ -247,11 +247,20 @@ static_assert(KVQ8_DEC_CH % 8 == 0 && ch_steps<8>() % 8 == 0,
 struct NoPages {
   static constexpr bool paged = false;
 };
+// The global step (8 tokens) of step k of wave gw, W waves sharing a head's steps:
+// SP = 1 deals single steps round robin; SP = 2 deals pairs of adjacent steps, so a
+// wave's steps 2j and 2j + 1 are 16 consecutive tokens (2 KB of int8 codes per read).
+template <int SP>
+__device__ __forceinline__ int step_g(int gw, int k, int W) {
+  static_assert(SP == 1 || SP == 2, "steps dealt singly or in pairs");
+  if constexpr (SP == 1) return gw + k * W;
+  else return 2 * (gw + (k >> 1) * W) + (k & 1);
+}
 // Paged sessions: the rows of a step (8 consecutive tokens, 8-aligned) lie in one
 // 64-row page, so a step's rows are one wave-uniform pool row plus the lane's row
 // within the step.
-// NR registers hold the slots of up to 64 NR steps per wave.
-template <int NR>
+// NR registers hold the slots of up to 64 NR steps per wave; SP as for step_g.
+template <int NR, int SP = 1>
 struct PageMap {
   static_assert(NR == 2 || NR == 4, "2 or 4 registers of slots");
   static constexpr bool paged = true;
@@ -267,7 +276,7 @@ struct PageMap {
       const int k = lane + 64 * j;
       int sl = 0;
       if (k < n_steps) {
-        sl = row[((gw + k * W) * 8) >> 6];
+        sl = row[(step_g<SP>(gw, k, W) * 8) >> 6];
         if ((unsigned)sl >= (unsigned)n_slots) sl = 0;
       }
       slot[j] = sl;
@@ -295,7 +304,7 @@ struct PageMap {
   // inside the session, on a page this wave has not mapped) or past the session's
   // end reads the session's last step, so k needs no clamp.
   __device__ __forceinline__ void step(int v, int k, int gw, int W, int& pb, int& lim) const {
-    const int s = (gw + k * W) * 8;
+    const int s = step_g<SP>(gw, k, W) * 8;
     const bool past = s >= len || k >= nst;
     const int s0 = past ? ((len - 1) & ~7) : s;
     const int rl = __builtin_amdgcn_readlane(v, k & 63);   // always: a select, not a branch
@@ -306,7 +315,7 @@ struct PageMap {
   // the pool row of row i of step k, k per lane within one 64-step block (v = block of
   // that block)
   __device__ __forceinline__ uint32_t lane_row(int v, int k, int gw, int W, int i) const {
-    const int s = (gw + k * W) * 8;
+    const int s = step_g<SP>(gw, k, W) * 8;
     const bool past = s >= len || k >= nst;
     const int s0 = past ? ((len - 1) & ~7) : s;
     const int sk = __shfl(v, k & 63, 64);
@@ -439,7 +448,7 @@ __device__ __forceinline__ int q_level(float& r, float s) {
 // 64 * group + 16 * (l / 16) .. + 15 and that token's group scale.  Token n of block
 // j is row n % 8 of step k + 2j + n / 8, so its logit goes where the 8-lane layout
 // of the other passes expects it.
-template <int U>
+template <int U, int SP = 1>
 struct KBatch {
   static_assert(U % 2 == 0, "blocks of 16 tokens are pairs of steps");
   u32x4 w[U / 2][2];
@@ -463,7 +472,7 @@ struct KBatch {
         const bool second = (n >> 3) != 0;
         row = (uint32_t)((second ? pb1 : pb0) + min(n & 7, second ? lim1 : lim0));
       } else {
-        row = (uint32_t)min((gw + ((n >> 3) ? k1 : k0) * W) * 8 + (n & 7), len - 1);
+        row = (uint32_t)min(step_g<SP>(gw, (n >> 3) ? k1 : k0, W) * 8 + (n & 7), len - 1);
       }
 #pragma unroll
       for (int grp = 0; grp < NGRP; ++grp) {
@@ -890,7 +899,10 @@ constexpr int PAIR_CH = KVQ8_DEC_PAIR_CH;
 constexpr int PAIR_MIN_STEPS = 32;
 // steps per pair the plan aims for at most, so that long sessions spread over many
 // workgroups (balance across CUs and sessions)
-constexpr int PAIR_TARGET_STEPS = 256;
+#ifndef KVQ8_DEC_PAIR_TARGET
+#define KVQ8_DEC_PAIR_TARGET 256
+#endif
+constexpr int PAIR_TARGET_STEPS = KVQ8_DEC_PAIR_TARGET;
 static_assert(PAIR_TARGET_STEPS <= 256, "a pair has at most 256 steps (4 registers of page map)");
 
 template <int G>
@@ -1322,14 +1334,19 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
   const int pr = wave & (PAIRS - 1);
   const int gw = s_idx * PAIRS + pr;
   const int W = Sb * PAIRS;
-  const int n_steps = gw < J ? (J - 1 - gw) / W + 1 : 0;
-  const int n_first = s_idx * PAIRS < J ? (J - 1 - s_idx * PAIRS) / W + 1 : 0;
+  // steps dealt in pairs (step_g<2>): the J steps form U2 units of 16 tokens, unit u
+  // to wave u mod W; the wave holding the last unit of an odd J has one step less
+  const int U2 = (J + 1) >> 1;
+  const int nu = gw < U2 ? (U2 - 1 - gw) / W + 1 : 0;
+  const int n_steps = nu ? 2 * nu - (2 * (gw + (nu - 1) * W) + 1 >= J ? 1 : 0) : 0;
+  // chunks: pair 0 holds the most units (a bound on every pair's steps)
+  const int n_first = s_idx * PAIRS < U2 ? 2 * ((U2 - 1 - s_idx * PAIRS) / W + 1) : 0;
   const int n_chunks = (n_first + MV_CH - 1) / MV_CH;
   const int kmax = max(n_steps - 1, 0);
   const int total = n_chunks * MV_CH;
   // paged (PG: the page map's registers, 0 for a contiguous session): this pair's
   // steps -> pool slots; steps past the session's end read its last step
-  std::conditional_t<PG != 0, PageMap<PG ? PG : 4>, NoPages> pm{};
+  std::conditional_t<PG != 0, PageMap<PG ? PG : 4, 2>, NoPages> pm{};
   if constexpr (PG != 0) pm.init(pages, page_stride, b, gw, W, n_steps, ss.cap / KV_PAGE_ROWS, len, lane);
 
   extern __shared__ float smem[];
@@ -1403,7 +1420,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         for (int lv = 0; lv < QLEV; ++lv) qs[grp][lv] = __shfl(sl[lv], 4 * kq, 64);
       }
     }
-    auto kstep = [&](const KBatch<UK>& cur, int kr) __attribute__((always_inline)) {
+    auto kstep = [&](const KBatch<UK, 2>& cur, int kr) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < UK / 2; ++j) {
         float v = 0.f;
@@ -1422,7 +1439,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         *dst = v;
       }
     };
-    KBatch<UK> KA, KB;
+    KBatch<UK, 2> KA, KB;
     uint32_t svn[NCB];   // the chunk's V scales, loaded as it starts
     if (total > 0) KA.load(kb, ksb, gw, W, 0, len, lane, kmax, pm);
     for (int k0 = 0; k0 < total; k0 += 2 * UK) {
@@ -1435,7 +1452,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
           if constexpr (PG != 0)
             row = pm.lane_row(pm.block(ch * MV_CH + bl * 8), st, gw, W, lane & 7);
           else
-            row = (uint32_t)min((gw + min(st, kmax) * W) * 8 + (lane & 7), len - 1);
+            row = (uint32_t)min(step_g<2>(gw, min(st, kmax), W) * 8 + (lane & 7), len - 1);
           svn[bl] = *(const KVQ8_GLOBAL uint32_t*)(vsb + row * NGRP * 2);
         }
       }
@@ -1454,7 +1471,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
 #pragma unroll
         for (int bl = 0; bl < NCB; ++bl) {
           const int tl = bl * 64 + lane;
-          const int t = (gw + (c0 + (tl >> 3)) * W) * 8 + (tl & 7);
+          const int t = step_g<2>(gw, c0 + (tl >> 3), W) * 8 + (tl & 7);
           if (tl < nl && t < len) {
 #pragma unroll
             for (int g = 0; g < G; ++g) mc[g] = max2(mc[g], lc[tl * G + g]);
@@ -1477,7 +1494,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         for (int bl = 0; bl < NCB; ++bl) {
           const int tl = bl * 64 + lane;
           const int st = c0 + (tl >> 3);
-          const int t = (gw + st * W) * 8 + (tl & 7);
+          const int t = step_g<2>(gw, st, W) * 8 + (tl & 7);
           const bool ok = tl < nl && t < len;
           const uint32_t svw = svn[bl];
           const float sv[NGRP] = {h2f((uint16_t)(svw & 0xFFFFu)), h2f((uint16_t)(svw >> 16))};
@@ -1546,7 +1563,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
           vw[u] = ldkv(vb + (size_t)pb * HD, (uint32_t)min(r, lim) * HD + c * 16);
         } else {
           const uint32_t row =
-              (uint32_t)min((gw + min(blk * MV_BLK + u, kmax) * W) * 8 + r, len - 1);
+              (uint32_t)min(step_g<2>(gw, min(blk * MV_BLK + u, kmax), W) * 8 + r, len - 1);
           vw[u] = ldkv(vb, row * HD + c * 16);
         }
       }
