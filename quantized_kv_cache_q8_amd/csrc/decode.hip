@@ -248,14 +248,19 @@ struct NoPages {
   static constexpr bool paged = false;
 };
 // The global step (8 tokens) of step k of wave gw, W waves sharing a head's steps:
-// SP = 1 deals single steps round robin; SP = 2 deals pairs of adjacent steps, so a
-// wave's steps 2j and 2j + 1 are 16 consecutive tokens (2 KB of int8 codes per read).
+// SP = 1 deals single steps round robin; SP = 2 or 4 deals units of SP adjacent steps,
+// so a wave's steps SP j .. SP j + SP - 1 are 8 SP consecutive tokens (SP KB of int8
+// codes per read).
 template <int SP>
 __device__ __forceinline__ int step_g(int gw, int k, int W) {
-  static_assert(SP == 1 || SP == 2, "steps dealt singly or in pairs");
+  static_assert(SP == 1 || SP == 2 || SP == 4, "steps dealt singly, in pairs or fours");
   if constexpr (SP == 1) return gw + k * W;
-  else return 2 * (gw + (k >> 1) * W) + (k & 1);
+  else return SP * (gw + (k / SP) * W) + (k % SP);
 }
+#ifndef KVQ8_DEC_MV_SP
+#define KVQ8_DEC_MV_SP 4
+#endif
+constexpr int MV_SP = KVQ8_DEC_MV_SP;   // steps per unit dealt to a wave (k_decode_pair_mv)
 // Paged sessions: the rows of a step (8 consecutive tokens, 8-aligned) lie in one
 // 64-row page, so a step's rows are one wave-uniform pool row plus the lane's row
 // within the step.
@@ -1334,19 +1339,19 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
   const int pr = wave & (PAIRS - 1);
   const int gw = s_idx * PAIRS + pr;
   const int W = Sb * PAIRS;
-  // steps dealt in pairs (step_g<2>): the J steps form U2 units of 16 tokens, unit u
-  // to wave u mod W; the wave holding the last unit of an odd J has one step less
-  const int U2 = (J + 1) >> 1;
-  const int nu = gw < U2 ? (U2 - 1 - gw) / W + 1 : 0;
-  const int n_steps = nu ? 2 * nu - (2 * (gw + (nu - 1) * W) + 1 >= J ? 1 : 0) : 0;
+  // steps dealt in units of MV_SP (step_g<MV_SP>): the J steps form NU units, unit u to
+  // wave u mod W; the wave holding the last unit has J - MV_SP (NU - 1) steps of it
+  const int NU = (J + MV_SP - 1) / MV_SP;
+  const int nu = gw < NU ? (NU - 1 - gw) / W + 1 : 0;
+  const int n_steps = nu ? min(MV_SP * nu, J - MV_SP * (gw + (nu - 1) * W) + MV_SP * (nu - 1)) : 0;
   // chunks: pair 0 holds the most units (a bound on every pair's steps)
-  const int n_first = s_idx * PAIRS < U2 ? 2 * ((U2 - 1 - s_idx * PAIRS) / W + 1) : 0;
+  const int n_first = s_idx * PAIRS < NU ? MV_SP * ((NU - 1 - s_idx * PAIRS) / W + 1) : 0;
   const int n_chunks = (n_first + MV_CH - 1) / MV_CH;
   const int kmax = max(n_steps - 1, 0);
   const int total = n_chunks * MV_CH;
   // paged (PG: the page map's registers, 0 for a contiguous session): this pair's
   // steps -> pool slots; steps past the session's end read its last step
-  std::conditional_t<PG != 0, PageMap<PG ? PG : 4, 2>, NoPages> pm{};
+  std::conditional_t<PG != 0, PageMap<PG ? PG : 4, MV_SP>, NoPages> pm{};
   if constexpr (PG != 0) pm.init(pages, page_stride, b, gw, W, n_steps, ss.cap / KV_PAGE_ROWS, len, lane);
 
   extern __shared__ float smem[];
@@ -1420,7 +1425,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         for (int lv = 0; lv < QLEV; ++lv) qs[grp][lv] = __shfl(sl[lv], 4 * kq, 64);
       }
     }
-    auto kstep = [&](const KBatch<UK, 2>& cur, int kr) __attribute__((always_inline)) {
+    auto kstep = [&](const KBatch<UK, MV_SP>& cur, int kr) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < UK / 2; ++j) {
         float v = 0.f;
@@ -1439,7 +1444,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         *dst = v;
       }
     };
-    KBatch<UK, 2> KA, KB;
+    KBatch<UK, MV_SP> KA, KB;
     uint32_t svn[NCB];   // the chunk's V scales, loaded as it starts
     if (total > 0) KA.load(kb, ksb, gw, W, 0, len, lane, kmax, pm);
     for (int k0 = 0; k0 < total; k0 += 2 * UK) {
@@ -1452,7 +1457,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
           if constexpr (PG != 0)
             row = pm.lane_row(pm.block(ch * MV_CH + bl * 8), st, gw, W, lane & 7);
           else
-            row = (uint32_t)min(step_g<2>(gw, min(st, kmax), W) * 8 + (lane & 7), len - 1);
+            row = (uint32_t)min(step_g<MV_SP>(gw, min(st, kmax), W) * 8 + (lane & 7), len - 1);
           svn[bl] = *(const KVQ8_GLOBAL uint32_t*)(vsb + row * NGRP * 2);
         }
       }
@@ -1471,7 +1476,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
 #pragma unroll
         for (int bl = 0; bl < NCB; ++bl) {
           const int tl = bl * 64 + lane;
-          const int t = step_g<2>(gw, c0 + (tl >> 3), W) * 8 + (tl & 7);
+          const int t = step_g<MV_SP>(gw, c0 + (tl >> 3), W) * 8 + (tl & 7);
           if (tl < nl && t < len) {
 #pragma unroll
             for (int g = 0; g < G; ++g) mc[g] = max2(mc[g], lc[tl * G + g]);
@@ -1494,7 +1499,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         for (int bl = 0; bl < NCB; ++bl) {
           const int tl = bl * 64 + lane;
           const int st = c0 + (tl >> 3);
-          const int t = step_g<2>(gw, st, W) * 8 + (tl & 7);
+          const int t = step_g<MV_SP>(gw, st, W) * 8 + (tl & 7);
           const bool ok = tl < nl && t < len;
           const uint32_t svw = svn[bl];
           const float sv[NGRP] = {h2f((uint16_t)(svw & 0xFFFFu)), h2f((uint16_t)(svw >> 16))};
@@ -1563,7 +1568,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
           vw[u] = ldkv(vb + (size_t)pb * HD, (uint32_t)min(r, lim) * HD + c * 16);
         } else {
           const uint32_t row =
-              (uint32_t)min(step_g<2>(gw, min(blk * MV_BLK + u, kmax), W) * 8 + r, len - 1);
+              (uint32_t)min(step_g<MV_SP>(gw, min(blk * MV_BLK + u, kmax), W) * 8 + r, len - 1);
           vw[u] = ldkv(vb, row * HD + c * 16);
         }
       }
