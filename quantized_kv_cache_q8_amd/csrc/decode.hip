@@ -260,7 +260,9 @@ __device__ __forceinline__ int step_g(int gw, int k, int W) {
 #ifndef KVQ8_DEC_MV_SP
 #define KVQ8_DEC_MV_SP 4
 #endif
-constexpr int MV_SP = KVQ8_DEC_MV_SP;   // steps per unit dealt to a wave (k_decode_pair_mv)
+// steps per unit dealt to a wave of k_decode_pair_mv for one session (a batch of
+// ragged sessions takes single steps: its short sessions split more evenly)
+constexpr int MV_SP = KVQ8_DEC_MV_SP;
 // Paged sessions: the rows of a step (8 consecutive tokens, 8-aligned) lie in one
 // 64-row page, so a step's rows are one wave-uniform pool row plus the lane's row
 // within the step.
@@ -1312,7 +1314,7 @@ __device__ __forceinline__ bf16x8 codes_bf16(i32x2 c) {
   }
   return __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
 }
-template <int G, int PG>
+template <int G, int PG, int SP>
 __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_PAIR_WPE)))
 void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restrict__ lens,
                       int max_len, int kvh, const float* __restrict__ q, float qscale,
@@ -1339,19 +1341,19 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
   const int pr = wave & (PAIRS - 1);
   const int gw = s_idx * PAIRS + pr;
   const int W = Sb * PAIRS;
-  // steps dealt in units of MV_SP (step_g<MV_SP>): the J steps form NU units, unit u to
-  // wave u mod W; the wave holding the last unit has J - MV_SP (NU - 1) steps of it
-  const int NU = (J + MV_SP - 1) / MV_SP;
+  // steps dealt in units of SP (step_g<SP>): the J steps form NU units, unit u to
+  // wave u mod W; the wave holding the last unit has J - SP (NU - 1) steps of it
+  const int NU = (J + SP - 1) / SP;
   const int nu = gw < NU ? (NU - 1 - gw) / W + 1 : 0;
-  const int n_steps = nu ? min(MV_SP * nu, J - MV_SP * (gw + (nu - 1) * W) + MV_SP * (nu - 1)) : 0;
+  const int n_steps = nu ? min(SP * nu, J - SP * (gw + (nu - 1) * W) + SP * (nu - 1)) : 0;
   // chunks: pair 0 holds the most units (a bound on every pair's steps)
-  const int n_first = s_idx * PAIRS < NU ? MV_SP * ((NU - 1 - s_idx * PAIRS) / W + 1) : 0;
+  const int n_first = s_idx * PAIRS < NU ? SP * ((NU - 1 - s_idx * PAIRS) / W + 1) : 0;
   const int n_chunks = (n_first + MV_CH - 1) / MV_CH;
   const int kmax = max(n_steps - 1, 0);
   const int total = n_chunks * MV_CH;
   // paged (PG: the page map's registers, 0 for a contiguous session): this pair's
   // steps -> pool slots; steps past the session's end read its last step
-  std::conditional_t<PG != 0, PageMap<PG ? PG : 4, MV_SP>, NoPages> pm{};
+  std::conditional_t<PG != 0, PageMap<PG ? PG : 4, SP>, NoPages> pm{};
   if constexpr (PG != 0) pm.init(pages, page_stride, b, gw, W, n_steps, ss.cap / KV_PAGE_ROWS, len, lane);
 
   extern __shared__ float smem[];
@@ -1425,7 +1427,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         for (int lv = 0; lv < QLEV; ++lv) qs[grp][lv] = __shfl(sl[lv], 4 * kq, 64);
       }
     }
-    auto kstep = [&](const KBatch<UK, MV_SP>& cur, int kr) __attribute__((always_inline)) {
+    auto kstep = [&](const KBatch<UK, SP>& cur, int kr) __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < UK / 2; ++j) {
         float v = 0.f;
@@ -1444,7 +1446,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         *dst = v;
       }
     };
-    KBatch<UK, MV_SP> KA, KB;
+    KBatch<UK, SP> KA, KB;
     uint32_t svn[NCB];   // the chunk's V scales, loaded as it starts
     if (total > 0) KA.load(kb, ksb, gw, W, 0, len, lane, kmax, pm);
     for (int k0 = 0; k0 < total; k0 += 2 * UK) {
@@ -1457,7 +1459,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
           if constexpr (PG != 0)
             row = pm.lane_row(pm.block(ch * MV_CH + bl * 8), st, gw, W, lane & 7);
           else
-            row = (uint32_t)min(step_g<MV_SP>(gw, min(st, kmax), W) * 8 + (lane & 7), len - 1);
+            row = (uint32_t)min(step_g<SP>(gw, min(st, kmax), W) * 8 + (lane & 7), len - 1);
           svn[bl] = *(const KVQ8_GLOBAL uint32_t*)(vsb + row * NGRP * 2);
         }
       }
@@ -1476,7 +1478,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
 #pragma unroll
         for (int bl = 0; bl < NCB; ++bl) {
           const int tl = bl * 64 + lane;
-          const int t = step_g<MV_SP>(gw, c0 + (tl >> 3), W) * 8 + (tl & 7);
+          const int t = step_g<SP>(gw, c0 + (tl >> 3), W) * 8 + (tl & 7);
           if (tl < nl && t < len) {
 #pragma unroll
             for (int g = 0; g < G; ++g) mc[g] = max2(mc[g], lc[tl * G + g]);
@@ -1499,7 +1501,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         for (int bl = 0; bl < NCB; ++bl) {
           const int tl = bl * 64 + lane;
           const int st = c0 + (tl >> 3);
-          const int t = step_g<MV_SP>(gw, st, W) * 8 + (tl & 7);
+          const int t = step_g<SP>(gw, st, W) * 8 + (tl & 7);
           const bool ok = tl < nl && t < len;
           const uint32_t svw = svn[bl];
           const float sv[NGRP] = {h2f((uint16_t)(svw & 0xFFFFu)), h2f((uint16_t)(svw >> 16))};
@@ -1568,7 +1570,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
           vw[u] = ldkv(vb + (size_t)pb * HD, (uint32_t)min(r, lim) * HD + c * 16);
         } else {
           const uint32_t row =
-              (uint32_t)min(step_g<MV_SP>(gw, min(blk * MV_BLK + u, kmax), W) * 8 + r, len - 1);
+              (uint32_t)min(step_g<SP>(gw, min(blk * MV_BLK + u, kmax), W) * 8 + r, len - 1);
           vw[u] = ldkv(vb, row * HD + c * 16);
         }
       }
@@ -1764,7 +1766,7 @@ int resident_splits() {
   int per_cu = 0, cus = 0;
   hipError_t e;
   if constexpr (use_mv<FMT, G>())
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_pair_mv<G, 0>, DEC_THREADS,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_pair_mv<G, 0, MV_SP>, DEC_THREADS,
                                                      mv_lds_bytes<G>());
   else if constexpr (use_pair<FMT>())
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
@@ -1811,18 +1813,21 @@ hipError_t launch_split(const kv_session* tab, const int32_t* lens, int n_sess, 
     // the page map's registers as for k_decode_pair below
     const long long J = ((long long)max_len + 7) / 8;
     const long long per_pair = (J + (long long)PAIRS * plan.S - 1) / ((long long)PAIRS * plan.S);
-    if constexpr (!PG)
-      hipLaunchKernelGGL((k_decode_pair_mv<G, 0>), grid, block, mv_lds_bytes<G>(), st, tab, lens,
-                         max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages,
-                         page_stride);
-    else if (per_pair <= 128)
-      hipLaunchKernelGGL((k_decode_pair_mv<G, 2>), grid, block, mv_lds_bytes<G>(), st, tab, lens,
-                         max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages,
-                         page_stride);
-    else
-      hipLaunchKernelGGL((k_decode_pair_mv<G, 4>), grid, block, mv_lds_bytes<G>(), st, tab, lens,
-                         max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages,
-                         page_stride);
+    const bool one = n_sess == 1;
+#define KVQ8_MV_LAUNCH(P, SPV)                                                                 \
+  hipLaunchKernelGGL((k_decode_pair_mv<G, P, SPV>), grid, block, mv_lds_bytes<G>(), st, tab, lens, \
+                     max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages, page_stride)
+    if constexpr (!PG) {
+      if (one) KVQ8_MV_LAUNCH(0, MV_SP);
+      else KVQ8_MV_LAUNCH(0, 1);
+    } else if (per_pair <= 128) {
+      if (one) KVQ8_MV_LAUNCH(2, MV_SP);
+      else KVQ8_MV_LAUNCH(2, 1);
+    } else {
+      if (one) KVQ8_MV_LAUNCH(4, MV_SP);
+      else KVQ8_MV_LAUNCH(4, 1);
+    }
+#undef KVQ8_MV_LAUNCH
   } else if constexpr (use_pair<FMT>()) {
     if constexpr (!PG) {
       hipLaunchKernelGGL((k_decode_pair<FMT, G, U, 0>), grid, block, pair_lds_bytes<G>(), st, tab,
