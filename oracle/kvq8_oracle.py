@@ -16,7 +16,7 @@ Sources (web pages; cited by title and section):
        Scope, Phased plan, Not in scope.
   [P3] PR #711 "kv: --kv k8v4 streams with --kv-resident": sections What, How.
 
-Readings where the pages are silent (all listed in the design doc):
+Readings where the pages are silent:
   * K8V4 ([P3, What]: "INT8 K + rotated Q4_0 V"): K is the q8 K; V is rotated by
     the orthonormal Walsh-Hadamard matrix H/sqrt(HD) (H the Sylvester Hadamard
     matrix), computed as the unnormalised transform w = H x in fp32 butterflies
