@@ -17,7 +17,7 @@ Sources (web pages; cited by title and section):
   [P3] PR #711 "kv: --kv k8v4 streams with --kv-resident": sections What, How.
 
 Readings where the pages are silent:
-  * K8V4 ([P3, What]: "INT8 K + rotated Q4_0 V"): K is the q8 K; V is rotated by
+  * K8V4 ([P3, What]: int8 K with a rotated 4-bit V): K is the q8 K; V is rotated by
     the orthonormal Walsh-Hadamard matrix H/sqrt(HD) (H the Sylvester Hadamard
     matrix), computed as the unnormalised transform w = H x in fp32 butterflies
     (stages h = 1, 2, 4, ..., HD/2), then quantised per 32-value block with the

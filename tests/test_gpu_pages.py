@@ -1,7 +1,8 @@
 """Paged sessions and the streamed window on the GPU: a decode over pages scattered
 through a pool, or streamed into a window from a pinned host store, equals the decode
 over the resident session bit for bit (PR #711 "kv: --kv k8v4 streams with
---kv-resident", section Tests: streamed and resident attention bitwise equal)."""
+--kv-resident", section Tests: the streamed decode must match the resident one bit
+for bit)."""
 import numpy as np
 import pytest
 import torch
