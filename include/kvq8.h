@@ -4,8 +4,11 @@
  * C ABI.  Every pointer named d_* is a DEVICE pointer, every h_* a HOST pointer.
  * Every call that takes a `stream` (a hipStream_t passed as void*, NULL for the
  * null stream) only enqueues work on it and returns; nothing allocates, frees or
- * synchronises, and no call keeps state between calls (reentrant, thread-safe).
- * The caller owns every buffer: caches, session tables, lengths, workspaces.
+ * synchronises.  The caller owns every buffer: caches, session tables, lengths,
+ * workspaces.  Calls are reentrant and thread-safe.  What the library keeps between
+ * calls: per device, the number of decode workgroups that device holds at once
+ * (queried on the first decode planning with that device current, then read only),
+ * which sets the split count and so the workspace size.
  *
  * Error behaviour: every argument a host can check is checked before anything is
  * enqueued; on error the call returns a negative KV_ERR_* code and enqueues
@@ -126,8 +129,18 @@ size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_le
  * of session b, kv head h = q / G:
  *   out[b][q] = sum_t softmax_t(sm_scale * q . K[h][t]) V[h][t],  t < d_len[b],
  * with K, V the dequantised cache values (code * scale, exact in fp32, or the
- * fp16 values), fp32 arithmetic.  Partials of each split of the context are
- * merged by log-sum-exp.  d_len[b] == 0 gives a zero row.
+ * fp16 values).  Partials of each split of the context are merged by log-sum-exp.
+ * d_len[b] == 0 gives a zero row.  Arithmetic:
+ *   F16: fp16 values widened to fp32; dot products, softmax and sums in fp32.
+ *   int8 K (Q8, K8V4): the scaled query is split per 64-dim group into three int8
+ *     levels, q = s (a + b/254 + c/254^2) with s = max|q| / 127 over the group
+ *     (residual at most s / (2 * 254^2)); each level's dot product with the codes
+ *     is an exact integer (matrix cores), combined with the K scales in fp32.
+ *   V of Q8 with G <= 4: each softmax weight times its V scale is carried as two
+ *     bf16 values, hi + lo, with |w - hi - lo| <= 2^-16 |w|; codes times hi and lo
+ *     are summed in fp32 on the matrix cores.  An output element then lies within
+ *     2^-16 A of the exact weighted sum, A = sum_t w_t |V_td| / sum_t w_t, plus fp32
+ *     rounding.  V of Q8 with G = 8 and of K8V4: fp32 vector sums.
  *   d_q   : fp32 [n_sess][n_q_heads][head_dim];  d_out : fp32 [n_sess][n_q_heads][head_dim]
  *   n_sess : 1 .. 65535.
  *   max_len : host upper bound of every d_len[b] (sizes the grid); a session over it
@@ -138,8 +151,9 @@ int kv_decode_attn(const kv_shape* h_shape, const kv_session* d_tab, const int32
                    int n_sess, int max_len, const float* d_q, float sm_scale, float* d_out,
                    void* d_ws, size_t ws_bytes, int32_t* d_status, void* stream);
 
-/* Compaction [P1, Extra Notes]: the FP16 [kvh][P][HD] copy of cache rows [0, P) that
- * the prompt chunk's Q K^T and P V products read.  F16: a copy (stride cap -> P).
+/* Compaction [P1, What changed; Extra Notes]: cache rows [0, P) rewritten as the FP16
+ * [kvh][P][HD] array on which prompt-chunk attention runs both of its matrix
+ * products.  F16: a copy (stride cap -> P).
  * Q8: fp16_rne(float(code) * float(scale)) -- one rounding of an exact product.
  *   h_sess : one session (host struct holding device pointers), P <= h_sess->cap
  *   d_k16, d_v16 : fp16 bits [n_kv_heads][P][head_dim] (device), 16-byte aligned. */
@@ -163,10 +177,10 @@ int kv_prefill_attn(const kv_shape* h_shape, const kv_session* h_sess, int pos0,
                     const float* d_q, float sm_scale, float* d_out, void* d_ws, size_t ws_bytes,
                     void* stream);
 
-/* Moving a session's rows, sized by the format ([P1, What changed]: the
- * session-to-slot copy is sized in the format's elements, with a second copy for the
- * scales under q8; [P2, Phased plan]: gather to the host and scatter back, the scales
- * beside the KV body).  A packed block of n_rows rows holds, for each array of the
+/* Moving a session's rows, sized by the format ([P1, What changed]: copying a session
+ * into a slot counts the format's own element size, and int8 adds a copy of the scale
+ * arrays; [P2, Phased plan]: gather to the host and scatter back, the scales beside
+ * the KV body).  A packed block of n_rows rows holds, for each array of the
  * format in the order K values, K scales, V values, V scales (absent arrays take no
  * bytes), [n_kv_heads][n_rows][row bytes of that array]: F16 256 / - / 256 / -,
  * Q8 128 / 4 / 128 / 4, K8V4 128 / 4 / 64 / 8 bytes per row of one head.
@@ -226,8 +240,15 @@ int kv_window_plan(void* h_state, int sess_id, int n_pages, int32_t* h_pages, in
  * arrays are pinned host memory, cap >= 64 n_pages) into its pool slot of h_pool (device,
  * cap >= 64 x slots), consecutive pages in consecutive slots as one copy per array, and
  * h_pages (pinned) to d_pages (device int32 [n_pages]).  Asynchronous on the stream:
- * h_pages and h_store must stay valid until the stream reaches the call; a decode of the
- * session enqueued after it on the stream reads the pages. */
+ * h_store must stay valid, and h_pages must be neither freed nor passed to another call
+ * (the next kv_window_map of the session rewrites it), until the stream reaches this
+ * call -- e.g. record an event after it and wait on that event before the session's next
+ * map.  A decode of the session enqueued after it on the stream reads the pages.
+ * Every argument (shape, both sessions' format, alignment and capacity, the window
+ * state) is checked before the window's state changes.  If a copy cannot be enqueued
+ * the call returns KV_ERR_HIP, the pages not yet copied are unmapped (their slots
+ * free, their h_pages entries -1, so the next plan lists them as missed); copies of
+ * earlier runs of this call may already be enqueued. */
 int kv_window_map(const kv_shape* h_shape, void* h_state, const kv_session* h_store, int sess_id,
                   int n_pages, const kv_session* h_pool, int32_t* h_pages, int32_t* h_missed,
                   int32_t* d_pages, int* h_misses, void* stream);

@@ -256,6 +256,9 @@ class Window:
             raise ValueError("kv_window_bytes: n_slots out of range")
         self.n_slots = n_slots
         self.state = ctypes.create_string_buffer(nb)
+        # per page-table buffer (by address): the event recorded after the map that
+        # last enqueued a copy from it; the next map of that table waits for it
+        self._table_events = {}
         _check(_lib.kv_window_init(self.state, nb, n_slots), "kv_window_init")
 
     def plan(self, sess_id: int, pages: "np.ndarray"):
@@ -280,10 +283,18 @@ class Window:
             raise ValueError("h_pages: expected a pinned int32 tensor of at least n_pages entries")
         missed = torch.zeros(max(1, n_pages), dtype=torch.int32)
         n = ctypes.c_int(0)
+        # the previous map's copy from this table must have run before the table is
+        # rewritten (the copy reads h_pages when the stream reaches it)
+        ev = self._table_events.pop(h_pages.data_ptr(), None)
+        if ev is not None:
+            ev.synchronize()
         _check(_lib.kv_window_map(ctypes.byref(shape), self.state, ctypes.byref(store.entry()),
                                   sess_id, n_pages, ctypes.byref(pool.entry()), h_pages.data_ptr(),
                                   missed.data_ptr(), _ptr(d_pages, torch.int32, "d_pages"),
                                   ctypes.byref(n), _stream(stream)), "kv_window_map")
+        ev = torch.cuda.Event()
+        ev.record(torch.cuda.current_stream() if stream is None else stream)
+        self._table_events[h_pages.data_ptr()] = ev
         return n.value
 
 

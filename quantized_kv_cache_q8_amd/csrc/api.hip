@@ -8,11 +8,11 @@
 using namespace kvq8;
 
 namespace {
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+}  // namespace
 
-int check_shape(const kv_shape* s) {
+int kvq8::check_shape(const kv_shape* s) {
   if (s == nullptr) return KV_ERR_ARG;
   if (s->fmt != KV_FMT_F16 && s->fmt != KV_FMT_Q8 && s->fmt != KV_FMT_K8V4) return KV_ERR_FMT;
   if (s->n_kv_heads < 1 || s->n_kv_heads > KV_MAX_KV_HEADS || s->n_q_heads < 1 ||
@@ -25,7 +25,7 @@ int check_shape(const kv_shape* s) {
 }
 
 // host copy of one session entry (prefill / compaction take one on the host)
-int check_session(const kv_shape* s, const kv_session* e) {
+int kvq8::check_session(const kv_shape* s, const kv_session* e) {
   if (e == nullptr || e->k == nullptr || e->v == nullptr) return KV_ERR_ARG;
   if (s->fmt != KV_FMT_F16) {
     if (e->k_scale == nullptr || e->v_scale == nullptr) return KV_ERR_FMT;
@@ -38,6 +38,8 @@ int check_session(const kv_shape* s, const kv_session* e) {
   if (e->cap > KV_MAX_CAP) return KV_ERR_RANGE;
   return KV_OK;
 }
+
+namespace {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? KV_OK : KV_ERR_HIP; }
 

@@ -151,6 +151,10 @@ hipError_t launch_append(int fmt, int kvh, const kv_session* d_tab, const int32_
                          int n_sess, int n_tok, const float* d_k, const float* d_v,
                          int32_t* d_status, hipStream_t st);
 
+// host-side checks shared by the entry points (KV_OK or a negative KV_ERR_*)
+int check_shape(const kv_shape* s);
+int check_session(const kv_shape* s, const kv_session* e);
+
 // rows of one session into another (kv_copy_rows, with the copy kind given: the
 // window also moves pages from pinned host memory)
 int copy_rows(const kv_shape* h_shape, const kv_session* h_src, int src_row0,

@@ -1,6 +1,7 @@
 // Causal attention of a prompt chunk over the FP16 [kvh][P][HD] copy of the cache,
 // on the matrix cores (PR #3084 "FP16 K/V cache by default, int8 with --kv-q8",
-// section Extra Notes: the prompt chunk's Q K^T and P V products read fp16 halves).
+// section Extra Notes: prompt attention runs both of its matrix products, scores and
+// weighted values, on an fp16 compaction of the cache).
 //
 // Workgroup = (kv head h, block of BQ = 256/G queries); its 256 rows are the
 // (query, head) pairs of the G query heads sharing kv head h, so one K/V tile in

@@ -107,14 +107,16 @@ int kv_window_plan(void* h_state, int sess_id, int n_pages, int32_t* h_pages,
 int kv_window_map(const kv_shape* h_shape, void* h_state, const kv_session* h_store, int sess_id,
                   int n_pages, const kv_session* h_pool, int32_t* h_pages, int32_t* h_missed,
                   int32_t* d_pages, int* h_misses, void* stream) {
-  if (h_shape == nullptr || h_store == nullptr || h_pool == nullptr) return KV_ERR_ARG;
+  // every argument is checked before the plan changes the window's state
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  if ((rc = check_session(h_shape, h_store)) || (rc = check_session(h_shape, h_pool))) return rc;
   if (h_state == nullptr || header(h_state)->magic != kWindowMagic) return KV_ERR_WINDOW;
   const int n_slots = header(h_state)->n_slots;
   if ((long long)h_pool->cap < (long long)n_slots * KV_PAGE_ROWS) return KV_ERR_RANGE;
   if ((long long)h_store->cap < (long long)n_pages * KV_PAGE_ROWS) return KV_ERR_RANGE;
   if (n_pages > 0 && d_pages == nullptr) return KV_ERR_ARG;
-  int rc = kv_rows_bytes(h_shape, 1) == 0 ? KV_ERR_ARG : KV_OK;
-  if (rc) return rc;
+  if (reinterpret_cast<uintptr_t>(d_pages) & 3) return KV_ERR_ALIGN;
   rc = kv_window_plan(h_state, sess_id, n_pages, h_pages, h_missed, h_misses);
   if (rc) return rc;
   // copy the missed pages, runs of consecutive pages in consecutive slots at once
@@ -127,7 +129,18 @@ int kv_window_map(const kv_shape* h_shape, void* h_state, const kv_session* h_st
     rc = copy_rows(h_shape, h_store, h_missed[i] * KV_PAGE_ROWS, h_pool,
                    h_pages[h_missed[i]] * KV_PAGE_ROWS, (j - i) * KV_PAGE_ROWS, stream,
                    hipMemcpyHostToDevice);
-    if (rc) return rc;
+    if (rc) {
+      // the pages from this run on were planned but never copied: their slots are
+      // marked free and the pages unmapped, so a later plan lists them as missed
+      // (the runs before this one were enqueued and keep their slots)
+      WinSlot* sl = slots(h_state);
+      for (int k = i; k < m; ++k) {
+        const int32_t s = h_pages[h_missed[k]];
+        sl[s] = WinSlot{-1, -1, -1, 0};
+        h_pages[h_missed[k]] = -1;
+      }
+      return rc;
+    }
     i = j;
   }
   if (n_pages > 0 &&

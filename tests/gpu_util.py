@@ -108,3 +108,25 @@ def check_close(got, ref, what, atol=ATOL, rtol=RTOL):
 
 def sm_scale(hd=128):
     return float(np.float32(1.0 / math.sqrt(hd)))
+
+
+# Fidelity gate of the decode, tighter than the tolerance: every output element
+# within FID_C * A_d + FID_ABS of the fp64 reference, where A_d = sum_t w_t |V_td| /
+# sum_t w_t is the attention of the same weights over |V| (computed by the oracle).
+# The int8 decode carries each weight p * s_v as two bf16 values with
+# |w - hi - lo| <= 2^-16 |w|, which moves an output by at most 2^-16 A_d; the
+# three-level int8 split of the query leaves a residual of about 2^-24 of each
+# group's largest query value, and the rest is fp32 rounding of products and sums.
+# FID_C = 2^-13 leaves 8x the weight-split term for those; a two-level query split
+# or a single bf16 weight (2^-8 A_d) lands far outside.
+FID_C = 2.0 ** -13
+FID_ABS = 1e-6
+
+
+def check_fidelity(got, ref, absref, what):
+    err = np.abs(got - ref)
+    bound = FID_C * absref + FID_ABS
+    ratio = err / (2.0 ** -16 * absref + FID_ABS)
+    say(f"  {what} fidelity: max_abs={err.max():.3e} worst err/(2^-16 A + 1e-6)={ratio.max():.3f} "
+        f"worst err/bound={np.max(err / bound):.3f}")
+    assert (err <= bound).all(), f"{what}: {(err > bound).sum()} of {err.size} outside the fidelity gate"

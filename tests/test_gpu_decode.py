@@ -8,18 +8,20 @@ import torch
 import kvsynth
 import oracle
 import quantized_kv_cache_q8_amd as kq
-from gpu_util import (DEV, append_bulk, check_close, decode_gpu, oracle_cache, say, shape,
-                      sm_scale, to_dev)
+from gpu_util import (DEV, append_bulk, assert_cache_equal, check_close, check_fidelity,
+                      decode_gpu, oracle_cache, say, shape, sm_scale, to_dev)
 
 pytestmark = pytest.mark.gpu
 F16, Q8, K4 = kq.KV_FMT_F16, kq.KV_FMT_Q8, kq.KV_FMT_K8V4
 
 
-def oracle_decode(cache: oracle.Cache, q, length, sm):
-    """fp64 decode one kv head at a time (bounded memory at long contexts)."""
+def oracle_decode(cache: oracle.Cache, q, length, sm, with_abs=False):
+    """fp64 decode one kv head at a time (bounded memory at long contexts).
+    with_abs: also the attention of the same weights over |V| (the fidelity gate's A)."""
     nqh = q.shape[0]
     G = nqh // cache.kvh
     out = np.zeros((nqh, cache.hd))
+    absv = np.zeros((nqh, cache.hd))
     for h in range(cache.kvh):
         sub = oracle.Cache(cache.fmt, 1, cache.cap, cache.hd)
         sub.k, sub.v = cache.k[h:h + 1], cache.v[h:h + 1]
@@ -28,7 +30,10 @@ def oracle_decode(cache: oracle.Cache, q, length, sm):
         K = sub.dequant("k", length)
         V = sub.dequant("v", length)
         out[h * G:(h + 1) * G] = oracle.decode_attn(q[h * G:(h + 1) * G], K, V, length, sm)
-    return out
+        if with_abs:
+            absv[h * G:(h + 1) * G] = oracle.decode_attn(q[h * G:(h + 1) * G], K, np.abs(V),
+                                                         length, sm)
+    return (out, absv) if with_abs else out
 
 
 def filled(fmt, kvh, cap, n, seed, outliers, layer=0):
@@ -73,7 +78,10 @@ def test_every_head_ratio(fmt, G):
     for length in (1, 9, 777, 3001):
         say(f"decode fmt={fmt} G={G} len={length}")
         got = decode_gpu(sh, [s], [length], q[None], sm_scale())[0]
-        check_close(got, oracle_decode(ref, q, length, sm_scale()), f"G={G} len={length}")
+        want, absv = oracle_decode(ref, q, length, sm_scale(), with_abs=True)
+        check_close(got, want, f"G={G} len={length}")
+        if fmt != K4:
+            check_fidelity(got, want, absv, f"G={G} len={length}")
 
 
 def test_empty_session_gives_zeros_and_determinism():
@@ -108,7 +116,10 @@ def test_f16_ctx32768_steps():
         assert ref.append(length, xk, xv)
         q = kvsynth.queries(seed, 0, 1, nqh, 128, sub=step, half_grid=True)[0]
         got = decode_gpu(sh, [s], [length + 1], q[None], sm_scale())[0]
-        check_close(got, oracle_decode(ref, q, length + 1, sm_scale()), f"f16 step {step}")
+        want, absv = oracle_decode(ref, q, length + 1, sm_scale(), with_abs=True)
+        check_close(got, want, f"f16 step {step}")
+        check_fidelity(got, want, absv, f"f16 step {step}")
+    assert_cache_equal(s, ref)
 
 
 def test_q8_ctx131072_steps():
@@ -118,6 +129,8 @@ def test_q8_ctx131072_steps():
     cap = kvsynth.round_up(ctx + steps, 64)
     say("q8 ctx131072: fill")
     s, ref = filled(Q8, kvh, cap, ctx, seed, outliers=True)
+    say("q8 ctx131072: codes and scales of the seeded fill, bit for bit")
+    assert_cache_equal(s, ref)
     sh = shape(Q8, kvh, nqh)
     tab = kq.session_table([s.entry()])
     for step in range(steps):
@@ -129,7 +142,11 @@ def test_q8_ctx131072_steps():
         assert ref.append(length, xk, xv)
         q = kvsynth.queries(seed, 0, 1, nqh, 128, sub=step)[0]
         got = decode_gpu(sh, [s], [length + 1], q[None], sm_scale())[0]
-        check_close(got, oracle_decode(ref, q, length + 1, sm_scale()), f"q8 step {step}")
+        want, absv = oracle_decode(ref, q, length + 1, sm_scale(), with_abs=True)
+        check_close(got, want, f"q8 step {step}")
+        check_fidelity(got, want, absv, f"q8 step {step}")
+    say("q8 ctx131072: the appended rows too")
+    assert_cache_equal(s, ref)
 
 
 @pytest.mark.slow
@@ -141,10 +158,14 @@ def test_full_context_262144_layer(fmt):
     kvh, nqh, ctx, seed = w["kvh"], w["nqh"], w["ctx"], w["seed"]
     say(f"full ctx fmt={fmt}: fill")
     s, ref = filled(fmt, kvh, ctx, ctx, seed, outliers=True)
+    say(f"full ctx fmt={fmt}: cache of the seeded fill, bit for bit")
+    assert_cache_equal(s, ref)
     q = kvsynth.queries(seed, 0, 1, nqh, 128)[0]
     say("full ctx: decode")
     got = decode_gpu(shape(fmt, kvh, nqh), [s], [ctx], q[None], sm_scale())[0]
-    check_close(got, oracle_decode(ref, q, ctx, sm_scale()), f"full ctx fmt={fmt}")
+    want, absv = oracle_decode(ref, q, ctx, sm_scale(), with_abs=True)
+    check_close(got, want, f"full ctx fmt={fmt}")
+    check_fidelity(got, want, absv, f"full ctx fmt={fmt}")
 
 
 def test_batched_variable_lengths_small():
@@ -236,3 +257,42 @@ def test_device_side_range_checks():
     torch.cuda.synchronize()
     assert status.item() == kq.KV_DEV_RANGE | kq.KV_DEV_BAD_SESSION
     assert not out.any()
+
+
+@pytest.mark.parametrize("fmt", [F16, Q8, K4])
+def test_batch_composition_bitwise(fmt):
+    """A session's decode does not depend on its place in a batch or on what the other
+    sessions hold: permuting the batch, or replacing every other session's cache and
+    query, gives it bitwise the same output (the split count and step unit depend only
+    on the call's session count and max_len, and each session's arithmetic only on
+    its own length).  A one-session call plans its own split count and step unit, so a
+    session decoded alone and in a batch take different summation orders; both are
+    checked against the oracle, with the fidelity gate for F16 and Q8."""
+    kvh, G = 2, 4
+    nqh = kvh * G
+    sh = shape(fmt, kvh, nqh)
+    lens = [3000, 1, 2999, 64, 1500, 3000]
+    a = [filled(fmt, kvh, 3008, n, 700 + i, outliers=True) for i, n in enumerate(lens)]
+    b = [filled(fmt, kvh, 3008, n, 800 + i, outliers=True) for i, n in enumerate(lens)]
+    q = kvsynth.queries(90, 0, len(lens), nqh, 128)
+    q2 = kvsynth.queries(91, 0, len(lens), nqh, 128)
+    base = decode_gpu(sh, [s for s, _ in a], lens, q, sm_scale())
+    perm = [4, 2, 0, 5, 3, 1]
+    got = decode_gpu(sh, [a[i][0] for i in perm], [lens[i] for i in perm], q[perm], sm_scale())
+    for k, i in enumerate(perm):
+        assert np.array_equal(got[k], base[i]), f"permuted batch, session {i}"
+    # session 0 and 4 kept, the others replaced by other caches and queries
+    keep = (0, 4)
+    mixed = [a[i][0] if i in keep else b[i][0] for i in range(len(lens))]
+    qm = np.stack([q[i] if i in keep else q2[i] for i in range(len(lens))])
+    got = decode_gpu(sh, mixed, lens, qm, sm_scale())
+    for i in keep:
+        assert np.array_equal(got[i], base[i]), f"neighbours changed, session {i}"
+    for i in range(len(lens)):
+        single = decode_gpu(sh, [a[i][0]], [lens[i]], q[i][None], sm_scale())[0]
+        want, absv = oracle_decode(a[i][1], q[i], lens[i], sm_scale(), with_abs=True)
+        check_close(base[i], want, f"batched session {i}")
+        check_close(single, want, f"single session {i}")
+        if fmt != K4:
+            check_fidelity(base[i], want, absv, f"batched session {i}")
+            check_fidelity(single, want, absv, f"single session {i}")

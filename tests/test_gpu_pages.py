@@ -109,6 +109,37 @@ def test_paged_long_batch_equals_resident(fmt):
     assert np.array_equal(y_pag, y_res)
 
 
+@pytest.mark.slow
+def test_paged_single_session_wide_map():
+    """One session whose pairs hold more than 128 steps each: the one-session int8
+    launch with the 4-register page map and units of four steps, paged against resident,
+    bit for bit."""
+    fmt, kvh, G, n = kq.KV_FMT_Q8, 32, 4, 131072
+    say("paged single session, wide page map")
+    sh = shape(fmt, kvh, G * kvh)
+    # 8192 seeded cells, tiled over the session on the device (the comparison is of
+    # two decodes of the same cache)
+    master = filled(fmt, kvh, n, 8192, 71)[0]
+    for t in master.tensors():
+        t.view(kvh, n // 8192, 8192, -1)[:, 1:] = t.view(kvh, n // 8192, 8192, -1)[:, :1]
+    q = kvsynth.queries(72, 0, 1, G * kvh, 128)
+    splits = kq.kv_decode_workspace_bytes(sh, 1, n) // (G * kvh * 129 * 4)
+    assert -(-(n // 8) // (4 * splits)) > 128, splits
+    y_res = decode(sh, [master], [n], q, n)
+    n_pg = n // P
+    n_slots = n_pg + 3
+    perm = np.random.default_rng(73).permutation(n_slots)[:n_pg].astype(np.int32)
+    pool = kq.Session(fmt, kvh, n_slots * P, fill=0xFF)   # NaN where not written
+    idx = torch.from_numpy(perm.astype(np.int64)).to(DEV)
+    for a, d in zip(master.tensors(), pool.tensors()):
+        d.view(kvh, n_slots, -1)[:, idx] = a.view(kvh, n_pg, -1)
+    del master
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    y_pag = decode(sh, [pool], [n], q, n, torch.from_numpy(perm).to(DEV), n_pg, status)
+    assert int(status.item()) == 0
+    assert np.array_equal(y_pag, y_res)
+
+
 def test_paged_batch_and_bad_page():
     fmt, kvh, G = kq.KV_FMT_Q8, 8, 4
     say("paged batch")
@@ -175,3 +206,48 @@ def test_streamed_window_equals_resident(fmt):
         y_win = decode(sh, [pool], [n], q, n, d_pages[:npg].contiguous(), npg)
         y_res = decode(sh, [res[s]], [n], q, n)
         assert np.array_equal(y_win, y_res), s
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_streamed_window_interleaved_without_sync(fmt):
+    """Map/decode pairs of three sessions enqueued back to back on one stream, with no
+    synchronisation between them: each session's page table is rewritten by its next
+    map while earlier copies from it may still be queued (the binding waits for the
+    copy that read the table before the table is rewritten).  Every output equals the
+    resident decode bit for bit."""
+    kvh, G = 4, 4
+    say(f"window no-sync fmt={fmt}")
+    sh = shape(fmt, kvh, G * kvh)
+    lens = {0: 2000, 1: 3001, 2: 1300}
+    res = {s: filled(fmt, kvh, 3072, n, 150 + s)[0] for s, n in lens.items()}
+    store = {}
+    for s, sess in res.items():
+        st = kq.Session(fmt, kvh, 3072, pinned=True)
+        for a, b in zip(sess.tensors(), st.tensors()):
+            b.copy_(a.cpu())
+        store[s] = st
+    n_slots = 64
+    pool = kq.Session(fmt, kvh, n_slots * P, fill=0xFF)
+    win = kq.Window(n_slots)
+    h_pages = {s: torch.full((48,), -1, dtype=torch.int32).pin_memory() for s in lens}
+    d_pages = {s: torch.zeros(48, dtype=torch.int32, device=DEV) for s in lens}
+    q = kvsynth.queries(152, 0, 1, G * kvh, 128)
+    qd = torch.from_numpy(np.ascontiguousarray(q)).to(DEV)
+    order = (0, 1, 0, 2, 1, 1, 0, 2, 2, 0, 1)
+    max_len = max(lens.values())
+    ws = torch.zeros(kq.kv_decode_workspace_bytes(sh, 1, max_len), dtype=torch.uint8, device=DEV)
+    tab = kq.session_table([pool.entry()])
+    outs = []
+    for s in order:
+        n = lens[s]
+        npg = (n + P - 1) // P
+        win.map(sh, store[s], s, npg, pool, h_pages[s], d_pages[s])
+        out = torch.empty((1, G * kvh, 128), device=DEV)
+        ln = torch.tensor([n], dtype=torch.int32, device=DEV)
+        kq.kv_decode_attn_paged(sh, tab, d_pages[s], 48, ln, 1, max_len, qd, sm_scale(), out, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    for s, out in zip(order, outs):
+        n = lens[s]
+        y_res = decode(sh, [res[s]], [n], q, max_len)
+        assert np.array_equal(out.cpu().numpy(), y_res), s

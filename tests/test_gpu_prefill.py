@@ -82,7 +82,8 @@ def test_prefill_single_token_equals_decode_definition():
 @pytest.mark.slow
 def test_prefill_chunk4096_at131072_sampled_rows():
     """The 4096-token prompt chunk at position 131072 of an int8 cache (8 kv heads,
-    32 query heads); 48 sampled rows (all heads) against the oracle."""
+    32 query heads); 72 sampled rows (all heads) against the oracle, rows 0 and
+    n_tok - 1 among them."""
     w = kvsynth.WORKLOADS["prefill4096_at131072"]
     kvh, nqh, pos0, n_tok, seed = w["kvh"], w["nqh"], w["pos0"], w["n_tok"], w["seed"]
     P = pos0 + n_tok
@@ -92,7 +93,8 @@ def test_prefill_chunk4096_at131072_sampled_rows():
     say("prefill 4096@131072: run")
     got = run_prefill(Q8, s, kvh, nqh, pos0, n_tok, q, sm_scale())
     rows = np.unique(np.concatenate([[0, 1, 63, 64, 255, 256, 2047, 4094, 4095],
-                                     np.random.default_rng(seed).choice(n_tok, 39, replace=False)]))
+                                     np.random.default_rng(seed).choice(n_tok, 63, replace=False)]))
+    assert rows.size >= 64 and rows[0] == 0 and rows[-1] == n_tok - 1
     k16, v16 = oracle.compact_f16(ref, P)
     say("prefill 4096@131072: oracle")
     want = oracle.prefill_attn(q, k16, v16, pos0, sm_scale(), rows=rows)
