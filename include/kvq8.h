@@ -8,7 +8,8 @@
  * workspaces.  Calls are reentrant and thread-safe.  What the library keeps between
  * calls: per device, the number of decode workgroups that device holds at once
  * (queried on the first decode planning with that device current, then read only),
- * which sets the split count and so the workspace size.
+ * which sets the split count and so the workspace size; and, per device, the fixed
+ * scratch array of kv_decode_attn_static.
  *
  * Error behaviour: every argument a host can check is checked before anything is
  * enqueued; on error the call returns a negative KV_ERR_* code and enqueues
@@ -150,6 +151,22 @@ size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_le
 int kv_decode_attn(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d_len,
                    int n_sess, int max_len, const float* d_q, float sm_scale, float* d_out,
                    void* d_ws, size_t ws_bytes, int32_t* d_status, void* stream);
+
+/* kv_decode_attn without a caller workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the split partials go to a fixed scratch array of
+ * KV_DECODE_STATIC_WS_BYTES that the library holds on each device it runs on, from
+ * its first use until the process ends.  No call allocates or frees anything.
+ * Same arguments, plan, kernels and results (bitwise) as kv_decode_attn, without
+ * d_ws / ws_bytes; KV_ERR_WORKSPACE when the call's partials
+ * (kv_decode_workspace_bytes) exceed the scratch, KV_ERR_HIP if its address cannot
+ * be had.  Every call on one device shares that device's scratch: calls that may
+ * overlap on a device (on different streams, or from several threads without
+ * ordering) race and must not be made; calls in order on one stream are safe. */
+#define KV_DECODE_STATIC_WS_BYTES (16u << 20)
+int kv_decode_attn_static(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d_len,
+                          int n_sess, int max_len, const float* d_q, float sm_scale, float* d_out,
+                          int32_t* d_status, void* stream);
 
 /* Compaction [P1, What changed; Extra Notes]: cache rows [0, P) rewritten as the FP16
  * [kvh][P][HD] array on which prompt-chunk attention runs both of its matrix

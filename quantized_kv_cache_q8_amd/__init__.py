@@ -25,13 +25,14 @@ KV_OK, KV_ERR_ARG, KV_ERR_FMT, KV_ERR_ALIGN, KV_ERR_UNSUPPORTED = 0, -1, -2, -3,
 KV_ERR_WORKSPACE, KV_ERR_RANGE, KV_ERR_HIP, KV_ERR_IMAGE, KV_ERR_WINDOW = -5, -6, -7, -8, -9
 KV_DEV_RANGE, KV_DEV_BAD_SESSION, KV_DEV_BAD_PAGE = 1, 2, 4
 KV_PAGE_ROWS = 64
+KV_DECODE_STATIC_WS_BYTES = 16 << 20
 
 EXPORTED = ["kv_cache_bytes", "kv_append", "kv_decode_workspace_bytes", "kv_decode_attn",
             "kv_compact_f16", "kv_prefill_workspace_bytes", "kv_prefill_attn", "kv_status_str",
             "kv_probe_stream_read", "kv_rows_bytes", "kv_copy_rows", "kv_gather_rows",
             "kv_scatter_rows", "kv_image_bytes", "kv_image_save", "kv_image_tokens",
             "kv_image_load", "kv_decode_attn_paged", "kv_window_bytes", "kv_window_init",
-            "kv_window_plan", "kv_window_map"]
+            "kv_window_plan", "kv_window_map", "kv_decode_attn_static"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run quantized_kv_cache_q8_amd.build.build() "
@@ -78,6 +79,8 @@ _sig = {
     "kv_image_load": (_I, [ctypes.POINTER(kv_shape), ctypes.POINTER(kv_session), _P, _SZ, _P, _P]),
     "kv_decode_attn_paged": (_I, [ctypes.POINTER(kv_shape), _P, _P, _I, _P, _I, _I, _P,
                                   ctypes.c_float, _P, _P, _SZ, _P, _P]),
+    "kv_decode_attn_static": (_I, [ctypes.POINTER(kv_shape), _P, _P, _I, _I, _P, ctypes.c_float,
+                                   _P, _P, _P]),
     "kv_window_bytes": (_SZ, [_I]),
     "kv_window_init": (_I, [_P, _SZ, _I]),
     "kv_window_plan": (_I, [_P, _I, _I, _P, _P, _P]),
@@ -230,6 +233,18 @@ def kv_decode_attn(shape: kv_shape, tab: torch.Tensor, lens: torch.Tensor, n_ses
                                _ptr(out, torch.float32, "out"), _ptr(ws, None, "ws"),
                                ws.numel() * ws.element_size(), _ptr(status, torch.int32, "status"),
                                _stream(stream)), "kv_decode_attn")
+
+
+def kv_decode_attn_static(shape: kv_shape, tab: torch.Tensor, lens: torch.Tensor, n_sess: int,
+                          max_len: int, q: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                          status: torch.Tensor | None = None, stream=None) -> None:
+    """kv_decode_attn with the library's fixed per-device scratch (no workspace)."""
+    _check(_lib.kv_decode_attn_static(ctypes.byref(shape), _ptr(tab, torch.uint8, "tab"),
+                                      _ptr(lens, torch.int32, "lens"), n_sess, max_len,
+                                      _ptr(q, torch.float32, "q"), float(sm_scale),
+                                      _ptr(out, torch.float32, "out"),
+                                      _ptr(status, torch.int32, "status"), _stream(stream)),
+           "kv_decode_attn_static")
 
 
 def kv_decode_attn_paged(shape: kv_shape, tab: torch.Tensor, pages: torch.Tensor, page_stride: int,

@@ -202,6 +202,27 @@ int kv_decode_attn(const kv_shape* h_shape, const kv_session* d_tab, const int32
                                   static_cast<hipStream_t>(stream)));
 }
 
+int kv_decode_attn_static(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d_len,
+                          int n_sess, int max_len, const float* d_q, float sm_scale, float* d_out,
+                          int32_t* d_status, void* stream) {
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  if (d_tab == nullptr || d_len == nullptr || d_q == nullptr || d_out == nullptr) return KV_ERR_ARG;
+  if (n_sess < 1 || n_sess > KV_DEC_MAX_SESS || max_len < 0 || !std::isfinite(sm_scale))
+    return KV_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_tab) & 7) || !aligned4(d_len) || !aligned16(d_q) ||
+      !aligned16(d_out) || !aligned4(d_status))
+    return KV_ERR_ALIGN;
+  const DecodePlan p =
+      decode_plan(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, n_sess, max_len);
+  if (p.ws_o_bytes + p.ws_lse_bytes > (size_t)KV_DECODE_STATIC_WS_BYTES) return KV_ERR_WORKSPACE;
+  void* ws = static_workspace();
+  if (ws == nullptr) return KV_ERR_HIP;
+  return hip_status(launch_decode(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, d_tab,
+                                  d_len, n_sess, max_len, d_q, sm_scale, d_out, ws, p, d_status,
+                                  static_cast<hipStream_t>(stream)));
+}
+
 int kv_decode_attn_paged(const kv_shape* h_shape, const kv_session* d_tab,
                          const int32_t* d_pages, int page_stride, const int32_t* d_len, int n_sess,
                          int max_len, const float* d_q, float sm_scale, float* d_out, void* d_ws,

@@ -1930,6 +1930,24 @@ DecodePlan decode_plan(int fmt, int kvh, int nqh, int n_sess, int max_len) {
   return p;
 }
 
+// The fixed scratch of kv_decode_attn_static: room for the split partials of one
+// call (KV_DECODE_STATIC_WS_BYTES).  Each device holds its own copy at its own
+// address; host code reaches it only through the address hipGetSymbolAddress gives,
+// fetched once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[KV_DECODE_STATIC_WS_BYTES];
+
+void* static_workspace() {
+  static std::atomic<void*> addr[KVQ8_MAX_DEVICES];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= KVQ8_MAX_DEVICES) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p != nullptr) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+  addr[dev].store(q, std::memory_order_release);   // the same value from any racing thread
+  return q;
+}
+
 hipError_t launch_decode(int fmt, int kvh, int nqh, const kv_session* d_tab,
                          const int32_t* d_len, int n_sess, int max_len, const float* d_q,
                          float sm_scale, float* d_out, void* d_ws, const DecodePlan& plan,

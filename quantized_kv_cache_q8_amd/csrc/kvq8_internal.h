@@ -174,6 +174,10 @@ hipError_t launch_decode(int fmt, int kvh, int nqh, const kv_session* d_tab,
                          int32_t* d_status, hipStream_t st, const int32_t* d_pages = nullptr,
                          int page_stride = 0);
 
+// kv_decode_attn_static's scratch on the current device (KV_DECODE_STATIC_WS_BYTES
+// bytes; its address fetched once per device), or NULL if it cannot be had
+void* static_workspace();
+
 hipError_t launch_compact(int fmt, int kvh, const kv_session& sess, int P, uint16_t* d_k16,
                           uint16_t* d_v16, hipStream_t st);
 

@@ -44,6 +44,7 @@ hipError_t launch_decode(int, int, int, const kv_session*, const int32_t*, int, 
   ++g_launches;
   return hipSuccess;
 }
+void* static_workspace() { return reinterpret_cast<void*>(0x7E0000000000ull); }
 hipError_t launch_compact(int, int, const kv_session&, int, uint16_t*, uint16_t*, hipStream_t) {
   ++g_launches;
   return hipSuccess;
@@ -137,6 +138,15 @@ static void argument_errors() {
                        P<float>(0x200), P<void>(0x300), 1 << 30, st, nullptr) == KV_ERR_ARG);
   CHECK(kv_decode_attn(&ok, P<kv_session>(0), P<int32_t>(64), 1, 100, P<float>(0x104), 0.1f,
                        P<float>(0x200), P<void>(0x300), 1 << 30, st, nullptr) == KV_ERR_ALIGN);
+  CHECK(kv_decode_attn_static(&ok, P<kv_session>(0), P<int32_t>(64), 65536, 100, P<float>(0x100),
+                              0.1f, P<float>(0x200), st, nullptr) == KV_ERR_ARG);
+  CHECK(kv_decode_attn_static(&ok, P<kv_session>(0), P<int32_t>(64), 1, 100, P<float>(0x100),
+                              0.1f, P<float>(0x204), st, nullptr) == KV_ERR_ALIGN);
+  // the stub plan's partials for 1000 sessions exceed the fixed scratch
+  CHECK(kv_decode_attn_static(&ok, P<kv_session>(0), P<int32_t>(64), 1000, 100, P<float>(0x100),
+                              0.1f, P<float>(0x200), st, nullptr) == KV_ERR_WORKSPACE);
+  CHECK(kv_decode_attn_static(&ok, P<kv_session>(0), P<int32_t>(64), 1, 100, nullptr, 0.1f,
+                              P<float>(0x200), st, nullptr) == KV_ERR_ARG);
   CHECK(kv_decode_attn_paged(&ok, P<kv_session>(0), P<int32_t>(0x500), 1, P<int32_t>(64), 1, 100,
                              P<float>(0x100), 0.1f, P<float>(0x200), P<void>(0x300), 1 << 30, st,
                              nullptr) == KV_ERR_ARG);   // page_stride * 64 < max_len
