@@ -775,10 +775,21 @@ def main():
               for li in range(LAYERS)]
     ws = {fmt: kq.kv_decode_workspace(model[fmt]["shape"], 1, CTX) for fmt in model}
 
-    log(f"warmup {n_warm} steps")
+    log(f"warmup {n_warm} eager steps")
     length = run_steps(kq, torch, model, n_warm, len0, q, xk_new, xv_new, ws)
     torch.cuda.synchronize()
-    log(f"timing {n_steps} steps")
+    bytes_total = sum(decode_bytes(fmt, length + s + 1) * LAYERS for fmt in (F16, Q8)
+                      for s in range(n_steps))
+    # one step captured as a HIP graph and replayed from len0 again (the appends rewrite
+    # the same cells): n_warm untimed replays, then the n_steps timed ones -- the value
+    log(f"graph: warmup {n_warm}, timing {n_steps} replays")
+    g_s = graph_steps(kq, torch, model, n_warm, n_steps, len0, q, xk_new, xv_new, ws)
+    step_s = g_s / n_steps
+    value = bytes_total / g_s / 1e9
+    log(f"graph steps: {step_s * 1e3:.2f} ms per step, {value:.0f} GB/s")
+    # the same n_steps again, launched eagerly with HIP events around every decode call
+    # (the per-call rooflines), at the clocks the graph steps ran at
+    log(f"eager: timing {n_steps} steps, events around each decode")
     events = {F16: [], Q8: []}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -787,17 +798,8 @@ def main():
     t1 = time.perf_counter()
     assert end_len == CTX
     eager_step_s = (t1 - t0) / n_steps
-    bytes_total = sum(decode_bytes(fmt, length + s + 1) * LAYERS for fmt in (F16, Q8)
-                      for s in range(n_steps))
     eager_value = bytes_total / (t1 - t0) / 1e9
     log(f"eager steps: {eager_step_s * 1e3:.2f} ms per step, {eager_value:.0f} GB/s")
-    # the same steps again (lengths reset: the appends rewrite the same cells), one step
-    # captured as a HIP graph and replayed: the timed value
-    log(f"graph: warmup {n_warm}, timing {n_steps} replays")
-    g_s = graph_steps(kq, torch, model, n_warm, n_steps, len0, q, xk_new, xv_new, ws)
-    step_s = g_s / n_steps
-    value = bytes_total / g_s / 1e9
-    log(f"graph steps: {step_s * 1e3:.2f} ms per step, {value:.0f} GB/s")
 
     roof = {}
     for fmt in (F16, Q8):

@@ -253,7 +253,7 @@ struct NoPages {
 // codes per read).
 template <int SP>
 __device__ __forceinline__ int step_g(int gw, int k, int W) {
-  static_assert(SP == 1 || SP == 2 || SP == 4, "steps dealt singly, in pairs or fours");
+  static_assert(SP == 1 || SP == 2 || SP == 4 || SP == 8, "steps dealt in units of 1, 2, 4 or 8");
   if constexpr (SP == 1) return gw + k * W;
   else return SP * (gw + (k / SP) * W) + (k % SP);
 }
@@ -455,11 +455,12 @@ __device__ __forceinline__ int q_level(float& r, float s) {
 // 64 * group + 16 * (l / 16) .. + 15 and that token's group scale.  Token n of block
 // j is row n % 8 of step k + 2j + n / 8, so its logit goes where the 8-lane layout
 // of the other passes expects it.
-template <int U, int SP = 1>
+// SC: also load each token's K scales (false: the caller fetches them per chunk)
+template <int U, int SP = 1, bool SC = true>
 struct KBatch {
   static_assert(U % 2 == 0, "blocks of 16 tokens are pairs of steps");
   u32x4 w[U / 2][2];
-  uint16_t sc[U / 2][2];
+  uint16_t sc[SC ? U / 2 : 1][2];
   template <class PM = NoPages>
   __device__ __forceinline__ void load(const char* kb, const char* ksb, int gw, int W, int k,
                                        int len, int lane, int kmax = 1 << 30,
@@ -484,7 +485,7 @@ struct KBatch {
 #pragma unroll
       for (int grp = 0; grp < NGRP; ++grp) {
         w[j][grp] = ldkv(kb, row * HD + grp * 64 + kq * 16);
-        sc[j][grp] = ldg16(ksb + (row * NGRP + grp) * 2);
+        if constexpr (SC) sc[j][grp] = ldg16(ksb + (row * NGRP + grp) * 2);
       }
     }
   }
@@ -1427,9 +1428,16 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         for (int lv = 0; lv < QLEV; ++lv) qs[grp][lv] = __shfl(sl[lv], 4 * kq, 64);
       }
     }
-    auto kstep = [&](const KBatch<UK, SP>& cur, int kr) __attribute__((always_inline)) {
+    // the K scales of the batch's tokens come from the chunk's scale words: token
+    // n = lane % 16 of block j is lane 16 j + n of the chunk's 64-token block kr / 8
+    // (ksw: the scale word of the block holding the batch, kr its first step)
+    static_assert(2 * UK == MV_CH && UK * 8 == 64, "a chunk is two K batches, one per block");
+    auto kstep = [&](const KBatch<UK, SP, false>& cur, int kr, uint32_t ksw)
+        __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < UK / 2; ++j) {
+        const uint32_t kw2 = (uint32_t)__shfl((int)ksw, 16 * j + (lane & 15), 64);
+        const float ks[NGRP] = {h2f((uint16_t)(kw2 & 0xFFFFu)), h2f((uint16_t)(kw2 >> 16))};
         float v = 0.f;
 #pragma unroll
         for (int grp = 0; grp < NGRP; ++grp) {
@@ -1439,35 +1447,47 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
               __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[grp], bk, i32x4{0, 0, 0, 0}, 0, 0, 0);
           const float lv = fmaf((float)d[2], qs[grp][2],
                                 fmaf((float)d[1], qs[grp][1], (float)d[0] * qs[grp][0]));
-          v = fmaf(lv, h2f(cur.sc[j][grp]), v);
+          v = fmaf(lv, ks[grp], v);
         }
         const int g = lane >> 4;
         float* dst = g < G ? lc + ((kr + 2 * j) * 8 + (lane & 15)) * G + g : junk + lane;
         *dst = v;
       }
     };
-    KBatch<UK, SP> KA, KB;
+    // The scale words of a chunk: lane l of block bl holds both 64-dim group scales
+    // (4 bytes) of token 64 bl + l of the chunk, one 32-bit load per lane and block.
+    auto chunk_scales = [&](const char* sb, int ch, uint32_t (&dst)[NCB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int bl = 0; bl < NCB; ++bl) {
+        const int st = ch * MV_CH + bl * 8 + (lane >> 3);
+        uint32_t row;
+        if constexpr (PG != 0)
+          row = pm.lane_row(pm.block(ch * MV_CH + bl * 8), st, gw, W, lane & 7);
+        else
+          row = (uint32_t)min(step_g<SP>(gw, min(st, kmax), W) * 8 + (lane & 7), len - 1);
+        dst[bl] = *(const KVQ8_GLOBAL uint32_t*)(sb + row * NGRP * 2);
+      }
+    };
+    KBatch<UK, SP, false> KA, KB;
     uint32_t svn[NCB];   // the chunk's V scales, loaded as it starts
-    if (total > 0) KA.load(kb, ksb, gw, W, 0, len, lane, kmax, pm);
+    uint32_t ksn[NCB], ksx[NCB] = {};   // the K scales of this chunk and of the next
+    if (total > 0) {
+      chunk_scales(ksb, 0, ksn);
+      KA.load(kb, ksb, gw, W, 0, len, lane, kmax, pm);
+    }
     for (int k0 = 0; k0 < total; k0 += 2 * UK) {
       const int ch = k0 / MV_CH, kr = k0 - ch * MV_CH;
       if (kr == 0) {
-#pragma unroll
-        for (int bl = 0; bl < NCB; ++bl) {
-          const int st = ch * MV_CH + bl * 8 + (lane >> 3);
-          uint32_t row;
-          if constexpr (PG != 0)
-            row = pm.lane_row(pm.block(ch * MV_CH + bl * 8), st, gw, W, lane & 7);
-          else
-            row = (uint32_t)min(step_g<SP>(gw, min(st, kmax), W) * 8 + (lane & 7), len - 1);
-          svn[bl] = *(const KVQ8_GLOBAL uint32_t*)(vsb + row * NGRP * 2);
-        }
+        chunk_scales(vsb, ch, svn);
+        if (k0 + MV_CH < total) chunk_scales(ksb, ch + 1, ksx);
       }
       KB.load(kb, ksb, gw, W, k0 + UK, len, lane, kmax, pm);
-      kstep(KA, kr);
+      kstep(KA, kr, ksn[0]);
       KA.load(kb, ksb, gw, W, k0 + 2 * UK, len, lane, kmax, pm);
-      kstep(KB, kr + UK);
+      kstep(KB, kr + UK, ksn[1]);
       if (kr + 2 * UK == MV_CH) {
+#pragma unroll
+        for (int bl = 0; bl < NCB; ++bl) ksn[bl] = ksx[bl];
         wave_lds_fence();
         // the chunk's softmax, then per block the weight table
         const int c0 = ch * MV_CH;
@@ -1649,40 +1669,63 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
   }
 }
 
-// One wave per (session, query head), MERGE_WAVES heads per workgroup.  Splits are
-// taken 64 at a time: lane k loads split j0 + k's lse (one vector load), the wave
-// reduces the chunk's max and weight sum, and the o rows of the chunk (one float2
-// per lane each) are loaded together up front, so a chunk costs about one memory
-// round trip.  Chunks fold in with a running max: out = sum_j 2^(lse_j - L) o_j,
-// L = log2 sum_j 2^lse_j.
-constexpr int MERGE_WAVES = 4;
+// One workgroup of 256 threads per (session, query head).  Thread t holds dims
+// 4 (t % 32) .. + 3 of the splits j = t / 32 + 8 k (k = 0 .. 7) of a chunk of 64
+// splits; every wave also holds the chunk's 64 lse values, one per lane, and forms
+// the chunk's max and weights itself.  The first chunk's partials and lse are loaded
+// at entry, before the session entry and length arrive (the workspace holds S splits
+// of every row, so the loads are in bounds whatever the session), so one call costs
+// about one memory round trip.  Splits past the session's count (active_splits) are
+// excluded by selects, never by multiplying stale values by a zero weight.  The 8 split
+// groups are summed through LDS: out = sum_j 2^(lse_j - L) o_j, L = log2 sum_j 2^lse_j.
+// Paged: the workgroups of a session's query heads each check a slice of its page
+// table.
+constexpr int MERGE_THREADS = 256;
+constexpr int MERGE_SG = MERGE_THREADS / 32;   // split groups of a chunk
+constexpr int MERGE_CHUNK = 64;                // splits per chunk (one per lane)
+constexpr int MERGE_PER = MERGE_CHUNK / MERGE_SG;   // splits per thread and chunk
 template <int FMT>
-__global__ __launch_bounds__(64 * MERGE_WAVES) void k_decode_merge(
+__global__ __launch_bounds__(MERGE_THREADS) void k_decode_merge(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int nqh,
-    int n_rows, const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int S,
+    const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int S,
     float* __restrict__ out, int32_t* __restrict__ status, const int32_t* __restrict__ pages,
     int page_stride) {
-  const int row = blockIdx.x * MERGE_WAVES + (int)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= n_rows) return;
+  __shared__ float4 red[MERGE_SG][32];
+  const int row = blockIdx.x;
   const int b = row / nqh, qh = row - b * nqh;
+  const int t = threadIdx.x, lane = t & 63;
+  const int dq = t & 31, sg = t >> 5;
+  const float* lse = ws_lse + (long long)row * S;
+  const float4* o = reinterpret_cast<const float4*>(ws_o + (long long)row * S * HD);
+  float4 v[MERGE_PER];
+  float f;
+  auto load_chunk = [&](int j0) __attribute__((always_inline)) {
+    const int last = min(S - 1, j0 + MERGE_CHUNK - 1);
+#pragma unroll
+    for (int k = 0; k < MERGE_PER; ++k)
+      v[k] = o[(long long)min(j0 + sg + MERGE_SG * k, last) * (HD / 4) + dq];
+    f = lse[min(j0 + lane, last)];
+  };
+  load_chunk(0);
   const kv_session ss = tab[b];
   const int len = lens[b];
   int bad = session_bad(ss, FMT);
   if (!bad && (len < 0 || len > ss.cap || len > max_len)) bad = KV_DEV_RANGE;
-  float2* dst = reinterpret_cast<float2*>(out + (long long)row * HD);
-  if (bad || len == 0) {
-    dst[lane] = make_float2(0.f, 0.f);
-    if (bad && qh == 0 && lane == 0) flag(status, bad);
+  float4* dst = reinterpret_cast<float4*>(out + (long long)row * HD);
+  if (bad || len == 0) {   // workgroup-uniform
+    if (t < 32) dst[t] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (bad && qh == 0 && t == 0) flag(status, bad);
     return;
   }
-  // paged: the first head's wave checks the session's page table (the split kernels
-  // read a slot outside the pool as slot 0)
-  if (pages != nullptr && qh == 0) {
+  if (pages != nullptr) {
+    // this head's slice of the session's page table (the split kernels read a slot
+    // outside the pool as slot 0)
     const int n_slots = ss.cap / KV_PAGE_ROWS;
     const int n_pages = (len + KV_PAGE_ROWS - 1) / KV_PAGE_ROWS;
+    const int per = (n_pages + nqh - 1) / nqh;
+    const int p1 = min(n_pages, (qh + 1) * per);
     bool bad_page = false;
-    for (int pg = lane; pg < n_pages; pg += 64) {
+    for (int pg = qh * per + t; pg < p1; pg += MERGE_THREADS) {
       const int sl = pages[(long long)b * page_stride + pg];
       bad_page |= sl < 0 || sl >= n_slots;
     }
@@ -1690,54 +1733,72 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void k_decode_merge(
   }
   // the splits that worked on this session (the same count the split kernel used)
   const int Sb = active_splits<FMT>(len, S);
-  const float* lse = ws_lse + (long long)row * S;
-  const float2* o = reinterpret_cast<const float2*>(ws_o + (long long)row * S * HD);
   float M = -INFINITY, L = 0.f;
-  float2 acc = make_float2(0.f, 0.f);
-  for (int j0 = 0; j0 < Sb; j0 += 64) {
-    const int n = min(64, Sb - j0);  // splits in this chunk (wave-uniform)
-    float2 v[64];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (16 * q < n) {
-#pragma unroll
-        for (int k = 16 * q; k < 16 * q + 16; ++k)
-          v[k] = o[(long long)(j0 + min(k, n - 1)) * (HD / 2) + lane];  // in bounds
-      }
-    const float f = lse[j0 + min(lane, n - 1)];
-    const float Mn = fmaxf(M, wave_max(f));  // finite: the chunk holds split j0
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < Sb; j0 += MERGE_CHUNK) {
+    if (j0 > 0) load_chunk(j0);
+    const int n = min(MERGE_CHUNK, Sb - j0);   // workgroup-uniform
+    const float fl = lane < n ? f : -INFINITY;
+    const float Mn = fmaxf(M, wave_max(fl));   // finite: the chunk holds split j0
     const float w = lane < n ? exp2f(f - Mn) : 0.f;
-    const float alpha = exp2f(M - Mn);       // 0 on the first chunk (M = -inf)
+    const float alpha = exp2f(M - Mn);          // 0 on the first chunk (M = -inf)
     L = fmaf(L, alpha, wave_sum(w));
     acc.x *= alpha;
     acc.y *= alpha;
+    acc.z *= alpha;
+    acc.w *= alpha;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (16 * q < n) {
-#pragma unroll
-        for (int k = 16 * q; k < 16 * q + 16; ++k) {
-          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), k));
-          acc.x = fmaf(wk, v[k].x, acc.x);
-          acc.y = fmaf(wk, v[k].y, acc.y);
-        }
+    for (int k = 0; k < MERGE_PER; ++k) {
+      const int js = sg + MERGE_SG * k;
+      const float wk = __shfl(w, js, 64);
+      if (js < n) {
+        acc.x = fmaf(wk, v[k].x, acc.x);
+        acc.y = fmaf(wk, v[k].y, acc.y);
+        acc.z = fmaf(wk, v[k].z, acc.z);
+        acc.w = fmaf(wk, v[k].w, acc.w);
       }
+    }
     M = Mn;
   }
-  float2 res = make_float2(acc.x / L, acc.y / L);
+  red[sg][dq] = acc;
+  __syncthreads();
   if constexpr (FMT == KV_FMT_K8V4) {
     // the merged row is in the rotated basis: V = H (code d) / 128, so out = H res / 128.
-    // Lane holds dims 2 lane, 2 lane + 1: stage 1 in the lane, stages 2 .. 64 pair
+    // Lane t of wave 0 holds dims 2t, 2t + 1: stage 1 in the lane, stages 2 .. 64 pair
     // lanes 1 .. 32 apart (the lower lane keeps a + b, the upper a - b)
-    float u0 = res.x + res.y, u1 = res.x - res.y;
+    if (t < 64) {
+      const float* rf = reinterpret_cast<const float*>(red);
+      float r0 = 0.f, r1 = 0.f;
 #pragma unroll
-    for (int mk = 1; mk < 64; mk *= 2) {
-      const float p0 = __shfl_xor(u0, mk, 64), p1 = __shfl_xor(u1, mk, 64);
-      u0 = (lane & mk) ? p0 - u0 : u0 + p0;
-      u1 = (lane & mk) ? p1 - u1 : u1 + p1;
+      for (int g = 0; g < MERGE_SG; ++g) {
+        r0 += rf[g * HD + 2 * t];
+        r1 += rf[g * HD + 2 * t + 1];
+      }
+      r0 = r0 / L;
+      r1 = r1 / L;
+      float u0 = r0 + r1, u1 = r0 - r1;
+#pragma unroll
+      for (int mk = 1; mk < 64; mk *= 2) {
+        const float p0 = __shfl_xor(u0, mk, 64), p1 = __shfl_xor(u1, mk, 64);
+        u0 = (t & mk) ? p0 - u0 : u0 + p0;
+        u1 = (t & mk) ? p1 - u1 : u1 + p1;
+      }
+      reinterpret_cast<float2*>(dst)[t] = make_float2(u0 * 0.0078125f, u1 * 0.0078125f);
     }
-    res = make_float2(u0 * 0.0078125f, u1 * 0.0078125f);
+  } else {
+    if (t < 32) {
+      float4 r = red[0][t];
+#pragma unroll
+      for (int g = 1; g < MERGE_SG; ++g) {
+        const float4 e = red[g][t];
+        r.x += e.x;
+        r.y += e.y;
+        r.z += e.z;
+        r.w += e.w;
+      }
+      dst[t] = make_float4(r.x / L, r.y / L, r.z / L, r.w / L);
+    }
   }
-  dst[lane] = res;
 }
 
 // steps per load batch: int8 takes 4 (its loads are half the size), except with 8
@@ -1874,9 +1935,8 @@ hipError_t launch_g(const kv_session* tab, const int32_t* lens, int n_sess, int 
                                                    ws_o, ws_lse, plan, nullptr, 0, st);
   if (e != hipSuccess) return e;
   const int n_rows = n_sess * kvh * G;
-  dim3 mgrid((n_rows + MERGE_WAVES - 1) / MERGE_WAVES), mblock(64 * MERGE_WAVES);
-  hipLaunchKernelGGL((k_decode_merge<FMT>), mgrid, mblock, 0, st, tab, lens, max_len, kvh * G,
-                     n_rows, ws_o, ws_lse, plan.S, out, status, pages, page_stride);
+  hipLaunchKernelGGL((k_decode_merge<FMT>), dim3(n_rows), dim3(MERGE_THREADS), 0, st, tab, lens,
+                     max_len, kvh * G, ws_o, ws_lse, plan.S, out, status, pages, page_stride);
   return hipGetLastError();
 }
 
