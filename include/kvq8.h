@@ -119,6 +119,19 @@ int kv_append(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d
               int n_sess, int n_tok, const float* d_k_new, const float* d_v_new,
               int32_t* d_status, void* stream);
 
+/* kv_append into paged sessions ([P3, How]: the decode and prompt appends write the
+ * streamed state's pool): cell c of session b (c in [d_len[b], d_len[b] + n_tok)) goes
+ * to row c % 64 of the pool slot d_pages[b * page_stride + c / 64] of d_tab[b] (usually
+ * one pool for every session), with the same arithmetic as kv_append.  A session then
+ * holds up to 64 page_stride cells: d_len[b] + n_tok above that flags KV_DEV_RANGE and
+ * skips the session; a table entry outside [0, cap / 64) flags KV_DEV_BAD_PAGE and
+ * skips that row.  d_pages: int32, device, 4-byte aligned; page_stride 1 .. 2^18.
+ * Mapping the pages first (kv_window_map) and copying the new rows back to the host
+ * store (kv_window_writeback) are the caller's. */
+int kv_append_paged(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d_pages,
+                    int page_stride, const int32_t* d_len, int n_sess, int n_tok,
+                    const float* d_k_new, const float* d_v_new, int32_t* d_status, void* stream);
+
 /* Workspace for kv_decode_attn: split-K partials.  Depends on its arguments and on
  * the current HIP device (the split count follows that device's occupancy); query
  * it with the device current that kv_decode_attn will run on.  0 on invalid
@@ -269,6 +282,18 @@ int kv_window_plan(void* h_state, int sess_id, int n_pages, int32_t* h_pages, in
 int kv_window_map(const kv_shape* h_shape, void* h_state, const kv_session* h_store, int sess_id,
                   int n_pages, const kv_session* h_pool, int32_t* h_pages, int32_t* h_missed,
                   int32_t* d_pages, int* h_misses, void* stream);
+
+/* Copy rows [row0, row0 + n_rows) of session sess_id from their pool slots back to its
+ * host store ([P3, How]: appends write the host copy as well as the pool), one copy per
+ * array for each run of consecutive pages in consecutive slots.  h_pages: the session's
+ * page table from its last kv_window_map; every page the rows touch must be resident for
+ * the session in the slot the table names, else KV_ERR_WINDOW (nothing enqueued).
+ * h_store: pinned host arrays, cap >= row0 + n_rows (else KV_ERR_RANGE).  Asynchronous on
+ * the stream: the rows reach the store once the stream passes the call; a later map on
+ * the same stream that copies them back to the pool reads the new values. */
+int kv_window_writeback(const kv_shape* h_shape, void* h_state, const kv_session* h_store,
+                        int sess_id, int row0, int n_rows, const kv_session* h_pool,
+                        const int32_t* h_pages, void* stream);
 
 /* Saved session image ([P2, Scope]: a header, the token ids, the KV body, then the
  * scales body; [P2, Phased plan]: version 3 carries the scales, and a version-2 image

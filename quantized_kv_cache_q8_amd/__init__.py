@@ -32,7 +32,8 @@ EXPORTED = ["kv_cache_bytes", "kv_append", "kv_decode_workspace_bytes", "kv_deco
             "kv_probe_stream_read", "kv_rows_bytes", "kv_copy_rows", "kv_gather_rows",
             "kv_scatter_rows", "kv_image_bytes", "kv_image_save", "kv_image_tokens",
             "kv_image_load", "kv_decode_attn_paged", "kv_window_bytes", "kv_window_init",
-            "kv_window_plan", "kv_window_map", "kv_decode_attn_static"]
+            "kv_window_plan", "kv_window_map", "kv_decode_attn_static", "kv_append_paged",
+            "kv_window_writeback"]
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run quantized_kv_cache_q8_amd.build.build() "
@@ -81,6 +82,9 @@ _sig = {
                                   ctypes.c_float, _P, _P, _SZ, _P, _P]),
     "kv_decode_attn_static": (_I, [ctypes.POINTER(kv_shape), _P, _P, _I, _I, _P, ctypes.c_float,
                                    _P, _P, _P]),
+    "kv_append_paged": (_I, [ctypes.POINTER(kv_shape), _P, _P, _I, _P, _I, _I, _P, _P, _P, _P]),
+    "kv_window_writeback": (_I, [ctypes.POINTER(kv_shape), _P, ctypes.POINTER(kv_session), _I, _I,
+                                 _I, ctypes.POINTER(kv_session), _P, _P]),
     "kv_window_bytes": (_SZ, [_I]),
     "kv_window_init": (_I, [_P, _SZ, _I]),
     "kv_window_plan": (_I, [_P, _I, _I, _P, _P, _P]),
@@ -213,6 +217,19 @@ def kv_append(shape: kv_shape, tab: torch.Tensor, lens: torch.Tensor, n_sess: in
                           _ptr(status, torch.int32, "status"), _stream(stream)), "kv_append")
 
 
+def kv_append_paged(shape: kv_shape, tab: torch.Tensor, pages: torch.Tensor, page_stride: int,
+                    lens: torch.Tensor, n_sess: int, n_tok: int, k_new: torch.Tensor,
+                    v_new: torch.Tensor, status: torch.Tensor | None = None, stream=None) -> None:
+    """kv_append into paged sessions: pages int32 [n_sess][page_stride] (device)."""
+    _check(_lib.kv_append_paged(ctypes.byref(shape), _ptr(tab, torch.uint8, "tab"),
+                                _ptr(pages, torch.int32, "pages"), page_stride,
+                                _ptr(lens, torch.int32, "lens"), n_sess, n_tok,
+                                _ptr(k_new, torch.float32, "k_new"),
+                                _ptr(v_new, torch.float32, "v_new"),
+                                _ptr(status, torch.int32, "status"), _stream(stream)),
+           "kv_append_paged")
+
+
 def kv_decode_workspace_bytes(shape: kv_shape, n_sess: int, max_len: int) -> int:
     return int(_lib.kv_decode_workspace_bytes(ctypes.byref(shape), n_sess, max_len))
 
@@ -311,6 +328,22 @@ class Window:
         ev.record(torch.cuda.current_stream() if stream is None else stream)
         self._table_events[h_pages.data_ptr()] = ev
         return n.value
+
+
+def _window_writeback(self, shape: kv_shape, store: "Session", sess_id: int, row0: int,
+                      n_rows: int, pool: "Session", h_pages: torch.Tensor, stream=None) -> None:
+    """Rows [row0, row0 + n_rows) of the session from their pool slots back to its pinned
+    host store (kv_window_writeback); h_pages: the table of the session's last map."""
+    if not store.pinned:
+        raise ValueError("store: must be a pinned Session")
+    if h_pages.dtype != torch.int32 or h_pages.device.type != "cpu" or not h_pages.is_contiguous():
+        raise ValueError("h_pages: expected a contiguous int32 host tensor")
+    _check(_lib.kv_window_writeback(ctypes.byref(shape), self.state, ctypes.byref(store.entry()),
+                                    sess_id, row0, n_rows, ctypes.byref(pool.entry()),
+                                    h_pages.data_ptr(), _stream(stream)), "kv_window_writeback")
+
+
+Window.writeback = _window_writeback
 
 
 def kv_compact_f16(shape: kv_shape, sess: kv_session, P: int, k16: torch.Tensor,

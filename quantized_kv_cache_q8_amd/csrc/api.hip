@@ -175,6 +175,26 @@ int kv_append(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d
                                   d_k_new, d_v_new, d_status, static_cast<hipStream_t>(stream)));
 }
 
+int kv_append_paged(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d_pages,
+                    int page_stride, const int32_t* d_len, int n_sess, int n_tok,
+                    const float* d_k_new, const float* d_v_new, int32_t* d_status, void* stream) {
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  if (d_tab == nullptr || d_pages == nullptr || d_len == nullptr || d_k_new == nullptr ||
+      d_v_new == nullptr)
+    return KV_ERR_ARG;
+  if (n_sess < 1 || n_sess > 65535 || n_tok < 0 || page_stride < 1 ||
+      page_stride > KV_MAX_CAP / KV_PAGE_ROWS)
+    return KV_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_tab) & 7) || !aligned4(d_pages) || !aligned4(d_len) ||
+      !aligned16(d_k_new) || !aligned16(d_v_new) || !aligned4(d_status))
+    return KV_ERR_ALIGN;
+  if (n_tok == 0) return KV_OK;
+  return hip_status(launch_append(h_shape->fmt, h_shape->n_kv_heads, d_tab, d_len, n_sess, n_tok,
+                                  d_k_new, d_v_new, d_status, static_cast<hipStream_t>(stream),
+                                  d_pages, page_stride));
+}
+
 size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_len) {
   if (check_shape(h_shape) || n_sess < 1 || n_sess > KV_DEC_MAX_SESS || max_len < 0) return 0;
   const DecodePlan p =

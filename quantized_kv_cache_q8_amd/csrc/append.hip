@@ -36,10 +36,26 @@ constexpr int ROW_PAIRS = 2;                                      // row pairs p
 constexpr int TOK_PER_BLOCK = (APPEND_THREADS / 64) * ROW_PAIRS * 2;  // 16
 static_assert(TOK_PER_BLOCK == (APPEND_THREADS / 64) * 4, "the K8V4 V path: 4 rows per wave");
 
+// Destination row of cell c of session b in head h's rows of its arrays: row c of a
+// contiguous session, or, for a paged session, row c % 64 of the pool slot its page
+// table names for page c / 64 (-1: the entry lies outside the pool; the row is
+// skipped and the session flagged).
+struct RowMap {
+  const int32_t* pages;   // NULL: contiguous
+  int stride;
+  __device__ __forceinline__ long long row(const kv_session& s, int b, int h, int c) const {
+    if (pages == nullptr) return (long long)h * s.cap + c;
+    const int sl = pages[(long long)b * stride + (c >> 6)];
+    if (sl < 0 || sl >= s.cap / KV_PAGE_ROWS) return -1;
+    return (long long)h * s.cap + (long long)sl * KV_PAGE_ROWS + (c & (KV_PAGE_ROWS - 1));
+  }
+};
+
 // K8V4 V rows [len + t] of head h: 16 lanes per row, 4 rows per wave (TOK_PER_BLOCK
 // rows per block, the same tokens the other paths cover)
 __device__ __forceinline__ void append_v_rot4(const kv_session& s, int len, int n_tok, int kvh,
-                                              int h, int b, const float* __restrict__ xv) {
+                                              int h, int b, const float* __restrict__ xv,
+                                              const RowMap& rm, int32_t* status) {
   const int lane = threadIdx.x & 63;
   const int l = lane & 15;   // dims 8l .. 8l + 7 of the row
   const int t = blockIdx.x * TOK_PER_BLOCK + (threadIdx.x >> 6) * 4 + (lane >> 4);
@@ -91,7 +107,12 @@ __device__ __forceinline__ void append_v_rot4(const kv_session& s, int len, int 
     word |= nib << (4 * j);   // dim 8l + j: byte j / 2, low nibble for even j
   }
   if (t < n_tok) {
-    const size_t row = (size_t)h * s.cap + len + t;
+    const long long r = rm.row(s, b, h, len + t);
+    if (r < 0) {
+      if (l == 0) flag(status, KV_DEV_BAD_PAGE);
+      return;
+    }
+    const size_t row = (size_t)r;
     uint8_t* dst = static_cast<uint8_t*>(s.v) + row * (HD / 2) + 4 * l;
     __builtin_nontemporal_store(word, (KVQ8_GLOBAL uint32_t*)dst);
     if ((l & 3) == 0) stg16(s.v_scale + row * NQ4 + (l >> 2), dbits);
@@ -101,24 +122,28 @@ __device__ __forceinline__ void append_v_rot4(const kv_session& s, int len, int 
 // Grid: x = blocks of TOK_PER_BLOCK tokens, y = (K or V, kv head), z = session.  Every
 // index comes from the block coordinates; a block writes the rows [len + t] of one
 // head of one of the two arrays.
+// A paged session (rm.pages set) holds cells [0, 64 stride): its rows lie in the
+// pool slots of its page table.
 template <int FMT>
 __global__ __launch_bounds__(APPEND_THREADS) void k_append(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int n_tok, int kvh,
-    const float* __restrict__ xk, const float* __restrict__ xv, int32_t* __restrict__ status) {
+    const float* __restrict__ xk, const float* __restrict__ xv, int32_t* __restrict__ status,
+    RowMap rm) {
   const int b = blockIdx.z;
   const int which = blockIdx.y >= (unsigned)kvh;   // 0 = K, 1 = V
   const int h = blockIdx.y - which * kvh;
   const kv_session s = tab[b];
   const int len = lens[b];
   int bad = session_bad(s, FMT);
-  if (!bad && (len < 0 || (long long)len + n_tok > s.cap)) bad = KV_DEV_RANGE;
+  const long long room = rm.pages == nullptr ? (long long)s.cap : (long long)rm.stride * KV_PAGE_ROWS;
+  if (!bad && (len < 0 || (long long)len + n_tok > room)) bad = KV_DEV_RANGE;
   if (bad) {   // the whole session is skipped; one thread of the session reports it
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) flag(status, bad);
     return;
   }
   if constexpr (FMT == KV_FMT_K8V4) {
     if (which) {
-      append_v_rot4(s, len, n_tok, kvh, h, b, xv);
+      append_v_rot4(s, len, n_tok, kvh, h, b, xv, rm, status);
       return;
     }
   }
@@ -128,7 +153,6 @@ __global__ __launch_bounds__(APPEND_THREADS) void k_append(
   const int t0 = blockIdx.x * TOK_PER_BLOCK + (threadIdx.x >> 6) * (ROW_PAIRS * 2);
   // source row (b, t, h) of [n_sess][n_tok][kvh][HD]
   const float* src = (which ? xv : xk) + ((size_t)b * n_tok * kvh + h) * HD + sub * 4;
-  const size_t drow0 = (size_t)h * s.cap + len;   // destination row of token 0
 
   float4 x[ROW_PAIRS];
 #pragma unroll
@@ -146,8 +170,10 @@ __global__ __launch_bounds__(APPEND_THREADS) void k_append(
 #pragma unroll
   for (int p = 0; p < ROW_PAIRS; ++p) {
     const int t = t0 + 2 * p + half;
-    const bool store = t < n_tok;
-    const size_t row = drow0 + t;
+    const long long r = t < n_tok ? rm.row(s, b, h, len + t) : -1;
+    if (t < n_tok && r < 0 && sub == 0) flag(status, KV_DEV_BAD_PAGE);
+    const bool store = r >= 0;
+    const size_t row = store ? (size_t)r : 0;
     if constexpr (FMT != KV_FMT_F16) {   // int8: the Q8 arrays, and the K8V4 K
       float a = fmaxf(fmaxf(fabsf(x[p].x), fabsf(x[p].y)), fmaxf(fabsf(x[p].z), fabsf(x[p].w)));
       a = max16(a);                                  // group max: all 16 lanes of the group
@@ -183,19 +209,21 @@ __global__ __launch_bounds__(APPEND_THREADS) void k_append(
 
 hipError_t launch_append(int fmt, int kvh, const kv_session* d_tab, const int32_t* d_len,
                          int n_sess, int n_tok, const float* d_k, const float* d_v,
-                         int32_t* d_status, hipStream_t st) {
+                         int32_t* d_status, hipStream_t st, const int32_t* d_pages,
+                         int page_stride) {
   const long long bx = ((long long)n_tok + TOK_PER_BLOCK - 1) / TOK_PER_BLOCK;
   if (bx > 0x7FFFFFFFLL || 2LL * kvh > 65535 || n_sess > 65535) return hipErrorInvalidValue;
   dim3 grid((unsigned)bx, 2 * kvh, n_sess), block(APPEND_THREADS);
+  const RowMap rm{d_pages, page_stride};
   if (fmt == KV_FMT_Q8)
     hipLaunchKernelGGL(k_append<KV_FMT_Q8>, grid, block, 0, st, d_tab, d_len, n_tok, kvh, d_k,
-                       d_v, d_status);
+                       d_v, d_status, rm);
   else if (fmt == KV_FMT_K8V4)
     hipLaunchKernelGGL(k_append<KV_FMT_K8V4>, grid, block, 0, st, d_tab, d_len, n_tok, kvh, d_k,
-                       d_v, d_status);
+                       d_v, d_status, rm);
   else
     hipLaunchKernelGGL(k_append<KV_FMT_F16>, grid, block, 0, st, d_tab, d_len, n_tok, kvh, d_k,
-                       d_v, d_status);
+                       d_v, d_status, rm);
   return hipGetLastError();
 }
 

@@ -147,9 +147,11 @@ __device__ __forceinline__ void flag(int32_t* status, int bits) {
 // ---------------------------------------------------------------------------
 // Launchers (validated arguments only; return hipError_t of the launch)
 // ---------------------------------------------------------------------------
+// d_pages: NULL for contiguous sessions, else the page tables of paged ones
 hipError_t launch_append(int fmt, int kvh, const kv_session* d_tab, const int32_t* d_len,
                          int n_sess, int n_tok, const float* d_k, const float* d_v,
-                         int32_t* d_status, hipStream_t st);
+                         int32_t* d_status, hipStream_t st, const int32_t* d_pages = nullptr,
+                         int page_stride = 0);
 
 // host-side checks shared by the entry points (KV_OK or a negative KV_ERR_*)
 int check_shape(const kv_shape* s);

@@ -8,6 +8,7 @@
 // page slots on the device (a session whose cap is 64 x slots); its bookkeeping lives
 // in caller-owned host memory: which (session, page) each slot holds, and CLOCK
 // replacement (a reference bit per slot and a sweeping hand).  Host code only.
+#include <algorithm>
 #include <cstring>
 
 #include "kvq8_internal.h"
@@ -147,6 +148,40 @@ int kv_window_map(const kv_shape* h_shape, void* h_state, const kv_session* h_st
       hipMemcpyAsync(d_pages, h_pages, (size_t)n_pages * sizeof(int32_t), hipMemcpyHostToDevice,
                      static_cast<hipStream_t>(stream)) != hipSuccess)
     return KV_ERR_HIP;
+  return KV_OK;
+}
+
+int kv_window_writeback(const kv_shape* h_shape, void* h_state, const kv_session* h_store,
+                        int sess_id, int row0, int n_rows, const kv_session* h_pool,
+                        const int32_t* h_pages, void* stream) {
+  int rc = check_shape(h_shape);
+  if (rc) return rc;
+  if ((rc = check_session(h_shape, h_store)) || (rc = check_session(h_shape, h_pool))) return rc;
+  if (h_state == nullptr || header(h_state)->magic != kWindowMagic) return KV_ERR_WINDOW;
+  if (sess_id < 0 || row0 < 0 || n_rows < 0) return KV_ERR_ARG;
+  if (n_rows > 0 && h_pages == nullptr) return KV_ERR_ARG;
+  if ((long long)row0 + n_rows > h_store->cap) return KV_ERR_RANGE;
+  if (n_rows == 0) return KV_OK;
+  const int n_slots = header(h_state)->n_slots;
+  if ((long long)h_pool->cap < (long long)n_slots * KV_PAGE_ROWS) return KV_ERR_RANGE;
+  const WinSlot* sl = slots(h_state);
+  const int p0 = row0 / KV_PAGE_ROWS, p1 = (row0 + n_rows - 1) / KV_PAGE_ROWS;
+  // every page the rows touch must be the session's, in the slot its table names
+  for (int p = p0; p <= p1; ++p)
+    if (!resident(sl, n_slots, h_pages[p], sess_id, p)) return KV_ERR_WINDOW;
+  // runs of rows in consecutive pages of consecutive slots, one copy per array each
+  int r = row0;
+  const int end = row0 + n_rows;
+  while (r < end) {
+    const int p = r / KV_PAGE_ROWS;
+    int q = p;
+    while ((q + 1) * KV_PAGE_ROWS < end && h_pages[q + 1] == h_pages[q] + 1) ++q;
+    const int r1 = std::min(end, (q + 1) * KV_PAGE_ROWS);
+    const int pool_row = h_pages[p] * KV_PAGE_ROWS + (r - p * KV_PAGE_ROWS);
+    rc = copy_rows(h_shape, h_pool, pool_row, h_store, r, r1 - r, stream, hipMemcpyDeviceToHost);
+    if (rc) return rc;
+    r = r1;
+  }
   return KV_OK;
 }
 

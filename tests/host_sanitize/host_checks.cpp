@@ -27,7 +27,7 @@ static int g_launches = 0;
 
 namespace kvq8 {
 hipError_t launch_append(int, int, const kv_session*, const int32_t*, int, int, const float*,
-                         const float*, int32_t*, hipStream_t) {
+                         const float*, int32_t*, hipStream_t, const int32_t*, int) {
   ++g_launches;
   return hipSuccess;
 }
@@ -127,6 +127,15 @@ static void argument_errors() {
                   st, nullptr) == KV_ERR_ALIGN);
   CHECK(kv_append(&ok, P<kv_session>(0), P<int32_t>(66), 1, 1, P<float>(0x100), P<float>(0x200),
                   st, nullptr) == KV_ERR_ALIGN);
+  // paged append
+  CHECK(kv_append_paged(&ok, P<kv_session>(0), nullptr, 4, P<int32_t>(64), 1, 1, P<float>(0x100),
+                        P<float>(0x200), st, nullptr) == KV_ERR_ARG);
+  CHECK(kv_append_paged(&ok, P<kv_session>(0), P<int32_t>(0x500), 0, P<int32_t>(64), 1, 1,
+                        P<float>(0x100), P<float>(0x200), st, nullptr) == KV_ERR_ARG);
+  CHECK(kv_append_paged(&ok, P<kv_session>(0), P<int32_t>(0x502), 4, P<int32_t>(64), 1, 1,
+                        P<float>(0x100), P<float>(0x200), st, nullptr) == KV_ERR_ALIGN);
+  CHECK(kv_append_paged(&ok, P<kv_session>(0), P<int32_t>(0x500), 4, P<int32_t>(64), 1, 1,
+                        P<float>(0x108), P<float>(0x200), st, nullptr) == KV_ERR_ALIGN);
   // decode
   CHECK(kv_decode_attn(&ok, P<kv_session>(0), P<int32_t>(64), 1, 100, P<float>(0x100), 0.1f,
                        P<float>(0x200), nullptr, 0, st, nullptr) == KV_ERR_WORKSPACE);
@@ -344,6 +353,39 @@ static void window_map_errors() {
   }
 }
 
+// kv_window_writeback: pages not resident for the session, or rows beyond the store,
+// are refused before anything is enqueued
+static void window_writeback_errors() {
+  const kv_shape sh{KV_FMT_Q8, 2, 8, 128};
+  const int n_slots = 8;
+  std::vector<unsigned char> state(kv_window_bytes(n_slots));
+  CHECK(kv_window_init(state.data(), state.size(), n_slots) == KV_OK);
+  kv_session store = fake(KV_FMT_Q8, 64 * 4, A);
+  kv_session pool = fake(KV_FMT_Q8, 64 * n_slots, A + 0x10000000);
+  std::vector<int32_t> pages(4, -1), missed(4);
+  int misses = -1;
+  CHECK(kv_window_plan(state.data(), 3, 2, pages.data(), missed.data(), &misses) == KV_OK);
+  CHECK(misses == 2);
+  // page 2 not mapped; another session's id; rows past the store; a null table
+  CHECK(kv_window_writeback(&sh, state.data(), &store, 3, 100, 40, &pool, pages.data(), nullptr) ==
+        KV_ERR_WINDOW);
+  CHECK(kv_window_writeback(&sh, state.data(), &store, 4, 0, 1, &pool, pages.data(), nullptr) ==
+        KV_ERR_WINDOW);
+  CHECK(kv_window_writeback(&sh, state.data(), &store, 3, 250, 7, &pool, pages.data(), nullptr) ==
+        KV_ERR_RANGE);
+  CHECK(kv_window_writeback(&sh, state.data(), &store, 3, 0, 1, &pool, nullptr, nullptr) ==
+        KV_ERR_ARG);
+  std::vector<int32_t> garbage = {1 << 30, -5, 7, 0};
+  CHECK(kv_window_writeback(&sh, state.data(), &store, 3, 0, 70, &pool, garbage.data(), nullptr) ==
+        KV_ERR_WINDOW);
+  CHECK(kv_window_writeback(&sh, state.data(), &store, 3, 5, 0, &pool, pages.data(), nullptr) ==
+        KV_OK);
+  // mapped rows: the copy itself fails without a GPU
+  const int rc = kv_window_writeback(&sh, state.data(), &store, 3, 60, 10, &pool, pages.data(),
+                                     nullptr);
+  CHECK(rc == KV_ERR_HIP || rc == KV_OK);
+}
+
 int main() {
   // Fake pointers reach the runtime's copy calls; with a GPU present a copy could be
   // enqueued on them, so this driver runs on machines without one only.
@@ -356,6 +398,7 @@ int main() {
   image_fuzz();
   window_plan_fuzz();
   window_map_errors();
+  window_writeback_errors();
   if (g_fail) {
     std::fprintf(stderr, "%d checks failed\n", g_fail);
     return 1;

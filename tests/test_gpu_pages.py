@@ -251,3 +251,63 @@ def test_streamed_window_interleaved_without_sync(fmt):
         n = lens[s]
         y_res = decode(sh, [res[s]], [n], q, max_len)
         assert np.array_equal(out.cpu().numpy(), y_res), s
+
+
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_paged_append_equals_resident(fmt):
+    """kv_append_paged writes exactly the rows kv_append writes, into the slots the page
+    tables name: three sessions in one call, appends that start mid-page and cross pages,
+    every other pool row left as it was; a table entry outside the pool skips its rows
+    (flagged), and a session whose pages cannot hold the append is skipped (flagged)."""
+    kvh, n_tok = 4, 150
+    lens = [0, 100, 1000]
+    stride = 20                          # 1280 cells per session
+    sh = shape(fmt, kvh, kvh)
+    n_slots = 3 * stride + 4
+    perm = np.random.default_rng(90 + fmt).permutation(n_slots).astype(np.int32)
+    table = perm[:3 * stride].reshape(3, stride).copy()
+    pool = kq.Session(fmt, kvh, n_slots * P, fill=0x5A)
+    res = [kq.Session(fmt, kvh, stride * P, fill=0x5A) for _ in lens]
+    xk = kvsynth.kv_tokens(91, 0, 3 * n_tok, kvh, 128, "K", True).reshape(3, n_tok, kvh, 128)
+    xv = kvsynth.kv_tokens(91, 0, 3 * n_tok, kvh, 128, "V", True).reshape(3, n_tok, kvh, 128)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ln = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    dk = torch.from_numpy(np.ascontiguousarray(xk)).to(DEV)
+    dv = torch.from_numpy(np.ascontiguousarray(xv)).to(DEV)
+    kq.kv_append_paged(sh, kq.session_table([pool.entry()] * 3), torch.from_numpy(table).to(DEV),
+                       stride, ln, 3, n_tok, dk, dv, status)
+    kq.kv_append(sh, kq.session_table([s.entry() for s in res]), ln, 3, n_tok, dk, dv, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    touched = np.zeros(n_slots * P, bool)
+    for b, n in enumerate(lens):
+        for c in range(n, n + n_tok):
+            prow = int(table[b, c // P]) * P + c % P
+            touched[prow] = True
+            for a, d in zip(res[b].tensors(), pool.tensors()):
+                assert torch.equal(a[:, c], d[:, prow]), (b, c)
+    untouched = torch.from_numpy(np.flatnonzero(~touched)).to(DEV)
+    for d in pool.tensors():
+        assert bool((d.view(torch.uint8).view(kvh, n_slots * P, -1)[:, untouched] == 0x5A).all())
+    # a page outside the pool: its rows skipped and flagged, the other rows written
+    bad = table.copy()
+    bad[1, 2] = n_slots + 9                     # cells 128 .. 191 of session 1
+    pool2 = kq.Session(fmt, kvh, n_slots * P, fill=0x5A)
+    status.zero_()
+    kq.kv_append_paged(sh, kq.session_table([pool2.entry()] * 3), torch.from_numpy(bad).to(DEV),
+                       stride, ln, 3, n_tok, dk, dv, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == kq.KV_DEV_BAD_PAGE
+    for a, d in zip(pool.tensors(), pool2.tensors()):
+        row = int(table[1, 1]) * P + 100 % P    # cell 100 of session 1, a good page
+        assert torch.equal(a[:, row], d[:, row])
+    # more cells than the pages hold: the session is skipped whole
+    status.zero_()
+    pool3 = kq.Session(fmt, kvh, n_slots * P, fill=0x5A)
+    ln3 = torch.tensor([stride * P - 10], dtype=torch.int32, device=DEV)
+    kq.kv_append_paged(sh, kq.session_table([pool3.entry()]), torch.from_numpy(table[:1].copy()).to(DEV),
+                       stride, ln3, 1, 11, dk[:1, :11].contiguous(), dv[:1, :11].contiguous(), status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == kq.KV_DEV_RANGE
+    for d in pool3.tensors():
+        assert bool((d.view(torch.uint8) == 0x5A).all())
