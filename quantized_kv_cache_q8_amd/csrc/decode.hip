@@ -23,10 +23,9 @@
 //   written as one (o, lse) per query head and split (o normalised, lse in log2).
 //   Offsets are 32-bit, from per-head base pointers (a head holds at most 2^24
 //   cells).
-// k_decode_pair (the int8-K formats): the same splits, with the K logits on the
-//   matrix cores and the waves in pairs, one streaming K and one streaming V per
-//   SIMD (described at the kernel).  k_decode_split serves FP16 (and the int8
-//   formats when KVQ8_DEC_PAIR is 0).
+// k_decode_pair / k_decode_pair_mv (the int8-K formats): the same splits, with the
+//   K logits on the matrix cores and the waves in pairs, one streaming K and one
+//   streaming V per SIMD (described at the kernels).  k_decode_split serves FP16.
 // k_decode_merge: out = sum_j 2^(lse_j - L) o_j with L = log2 sum_j 2^lse_j.
 //
 // Dequantised values are exact in fp32 (a 7-bit code times an 11-bit fp16
@@ -416,7 +415,7 @@ __device__ __forceinline__ void fold_stage(float (&x)[U][G]) {
   }
 }
 
-// The int8 K pass on the matrix cores.  The logits of G query heads against 16
+// The int8 K pass on the matrix cores (the pair kernels).  The logits of G query heads against 16
 // tokens are a small integer product per 64-dim scale group: the query, in log2
 // units, is split per (head, group) into three int8 levels,
 //   q = s (a + b / 254 + c / 254^2),  s = max|q| / 127 over the group,
@@ -428,17 +427,12 @@ __device__ __forceinline__ void fold_stage(float (&x)[U][G]) {
 // the three level sums of head l / 16 and token l % 16 and turns them into one logit.
 // Any assignment of dims to k-slots is a valid contraction as long as A and B use
 // the same one: lane l's byte j of both operands is dim 64 * group + 16 * (l / 16) + j.
-#ifndef KVQ8_DEC_KMFMA
-#define KVQ8_DEC_KMFMA 1
-#endif
 // 8-token steps per K batch of the matrix-core pass (two batches alternate)
 #ifndef KVQ8_DEC_UK_Q8
 #define KVQ8_DEC_UK_Q8 8
 #endif
 template <int G>
 __host__ __device__ constexpr int k_batch_rows() { return G >= 8 ? 4 : KVQ8_DEC_UK_Q8; }
-template <int FMT>
-__host__ __device__ constexpr bool kmfma() { return KVQ8_DEC_KMFMA && FMT != KV_FMT_F16; }
 constexpr int QLEV = 3;
 constexpr float QBASE_INV = 1.f / 254.f;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -510,10 +504,8 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     const float* __restrict__ q, float qscale, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, int S, const int32_t* __restrict__ pages, int page_stride) {
   constexpr int CH0 = ch0<FMT, G>(), CH1 = ch1<FMT, G>();
-  constexpr int UK = k_batch_rows<G>();
+  static_assert(FMT == KV_FMT_F16, "the int8-K formats take the pair kernels");
   static_assert(CH0 % (2 * U) == 0 && CH1 % (2 * U) == 0, "a chunk holds whole pairs of load batches");
-  static_assert(!kmfma<FMT>() || (CH0 % (2 * UK) == 0 && CH1 % (2 * UK) == 0),
-                "a chunk holds whole pairs of K batches");
   static_assert(CH0 >= KVQ8_DEC_MIN_STEPS && (!GROUPED || CH1 >= KVQ8_DEC_MIN_STEPS),
                 "a short session's waves (at most KVQ8_DEC_MIN_STEPS steps) fit the logits budget");
   const int s_idx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -547,91 +539,30 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
   float* l_l = m_l + DEC_WAVES * G;              // [waves][G]
   float* junk = l_l + DEC_WAVES * G + (threadIdx.x >> 6) * 64;  // discarded stores
 
-  constexpr int EB = FMT == KV_FMT_F16 ? 2 : 1;   // bytes per value
   const size_t hrow = (size_t)h * (size_t)ss.cap;  // the head's first row
-  const char* kb = static_cast<const char*>(ss.k) + hrow * HD * EB;
-  constexpr int VB = FMT == KV_FMT_K8V4 ? HD / 2 : HD * EB;   // bytes per V row
-  constexpr int VSC = FMT == KV_FMT_K8V4 ? NQ4 : NGRP;          // V scales per row
-  const char* vb = static_cast<const char*>(ss.v) + hrow * VB;
-  const char* ksb = reinterpret_cast<const char*>(ss.k_scale) + hrow * NGRP * 2;
-  const char* vsb = reinterpret_cast<const char*>(ss.v_scale) + hrow * VSC * 2;
+  const char* kb = static_cast<const char*>(ss.k) + hrow * HD * 2;
+  const char* vb = static_cast<const char*>(ss.v) + hrow * HD * 2;
+  const char* nsc = nullptr;   // FP16: no scale arrays
   float m[G], l[G], acc[G][16];
-  float accw[G];  // K8V4: the V-pass weights summed (takes the + 8 of the nibbles out)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = -INFINITY;
     l[g] = 0.f;
-    accw[g] = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[g][i] = 0.f;
   }
 
   if (n_steps > 0) {
     const int hsel = head_map<G>(c);
-    constexpr bool MF = kmfma<FMT>();
-    float qv[G][16];  // slot g: head g ^ hsel (the vector K pass)
-    if constexpr (!MF) {
+    float qv[G][16];  // slot g: head g ^ hsel
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float* qp = q + ((long long)b * nqh + h * G + (g ^ hsel)) * HD;
+    for (int g = 0; g < G; ++g) {
+      const float* qp = q + ((long long)b * nqh + h * G + (g ^ hsel)) * HD;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const u32x4 v = ldg128(qp + lane_dim<FMT>(c, 4 * k));   // 4 consecutive dims
+      for (int k = 0; k < 4; ++k) {
+        const u32x4 v = ldg128(qp + lane_dim<FMT>(c, 4 * k));   // 4 consecutive dims
 #pragma unroll
-          for (int e = 0; e < 4; ++e) qv[g][4 * k + e] = as_f32(v[e]) * qscale;
-        }
-      }
-    }
-    // matrix-core K pass: A operands (per block of 4 heads and group) and the level
-    // scales of the head whose logits this lane receives
-    constexpr int NHB = G > 4 ? 2 : 1;
-    i32x4 aq[MF ? NHB : 1][NGRP];
-    float qs[MF ? NHB : 1][NGRP][QLEV];
-    if constexpr (MF) {
-      const int m = lane & 15, kq = lane >> 4;
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) {
-        const int ga = hb * 4 + (m >> 2), lev = m & 3;   // this lane's A row: head, level
-#pragma unroll
-        for (int grp = 0; grp < NGRP; ++grp) {
-          const float* qp =
-              q + ((long long)b * nqh + h * G + min(ga, G - 1)) * HD + grp * 64 + kq * 16;
-          float x[16];
-          float mx = 0.f;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const u32x4 v = ldg128(qp + 4 * k);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              x[4 * k + e] = as_f32(v[e]) * qscale;
-              mx = fmaxf(mx, fabsf(x[4 * k + e]));
-            }
-          }
-          // lanes m, m + 16, m + 32, m + 48 hold the group's 64 dims
-          mx = fmaxf(mx, shfl_xor(mx, 16));
-          mx = fmaxf(mx, shfl_xor(mx, 32));
-          float sl[QLEV];
-          sl[0] = mx > 0.f ? mx / 127.f : 1.f;   // an all-zero group: any s, levels 0
-#pragma unroll
-          for (int l = 1; l < QLEV; ++l) sl[l] = sl[l - 1] * QBASE_INV;
-          const bool live = ga < G && lev < QLEV;
-          uint32_t wd[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float rr = x[i];
-            int a = 0;
-#pragma unroll
-            for (int l = 0; l < QLEV; ++l) {
-              const int al = q_level(rr, sl[l]);
-              a = l == lev ? al : a;
-            }
-            wd[i >> 2] |= (uint32_t)((live ? a : 0) & 0xFF) << (8 * (i & 3));
-          }
-          aq[hb][grp] = i32x4{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
-          // lane 4 * kq holds row 4 * kq (head hb * 4 + kq, level 0): its scales
-#pragma unroll
-          for (int l = 0; l < QLEV; ++l) qs[hb][grp][l] = __shfl(sl[l], 4 * kq, 64);
-        }
+        for (int e = 0; e < 4; ++e) qv[g][4 * k + e] = as_f32(v[e]) * qscale;
       }
     }
     // U x G independent dot products, interleaved so that no FMA waits on the one
@@ -660,14 +591,6 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
       constexpr int N1 = G > 1 ? G / 2 : 1, N2 = N1 > 1 ? N1 / 2 : 1, N3 = N2 > 1 ? N2 / 2 : 1;
       fold_stage<DPP_QUAD_XOR1, U, G, G>(part);
       fold_stage<DPP_QUAD_XOR2, U, G, N1>(part);
-      if constexpr (FMT != KV_FMT_F16) {  // lanes c .. c^3 share a scale group
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const float sc = cur.scale(u);
-#pragma unroll
-          for (int k = 0; k < N2; ++k) part[u][k] *= sc;
-        }
-      }
       fold_stage<DPP_ROW_HALF_MIRROR, U, G, N2>(part);
       static_assert(N3 == 1, "three stages reduce up to 8 heads");
       // lanes c < G of each row hold distinct heads and write them; the others
@@ -678,66 +601,19 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
         *dst = part[u][0];
       }
     };
-    // matrix-core K step: per block of 16 tokens, per group of 4 heads, one product
-    // per scale group; lane l turns the level sums of (head, token l % 16) into the
-    // logit, sum over groups of K scale x (A s0 + B s1 + C s2)
-    auto kstep_m = [&](const KBatch<UK>& cur, int it0) __attribute__((always_inline)) {
-      if constexpr (MF) {
-#pragma unroll
-        for (int j = 0; j < UK / 2; ++j) {
-#pragma unroll
-          for (int hb = 0; hb < NHB; ++hb) {
-            float v = 0.f;
-#pragma unroll
-            for (int grp = 0; grp < NGRP; ++grp) {
-              const u32x4& bw = cur.w[j][grp];
-              const i32x4 bk = i32x4{(int)bw[0], (int)bw[1], (int)bw[2], (int)bw[3]};
-              const i32x4 d =
-                  __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[hb][grp], bk, i32x4{0, 0, 0, 0}, 0, 0, 0);
-              const float lv = fmaf((float)d[2], qs[hb][grp][2],
-                                    fmaf((float)d[1], qs[hb][grp][1], (float)d[0] * qs[hb][grp][0]));
-              v = fmaf(lv, h2f(cur.sc[j][grp]), v);
-            }
-            const int g = hb * 4 + (lane >> 4);
-            float* dst = g < G ? lg + ((it0 + 2 * j) * 8 + (lane & 15)) * G + g : junk + lane;
-            *dst = v;
-          }
-        }
-      }
-    };
     auto vstep = [&](const Batch<FMT, U>& cur, int it0, int n_it) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int it = it0 + u;
-        const float sc = cur.scale(u);
         // p is 0 for tokens past the end (their logits were stored as -inf); slots
         // past n_it hold stale LDS (in bounds: CH0, CH1 are multiples of 2U) and are zeroed
         float w[G];
         load_p<G>(lg + (it * 8 + r) * G, w);
 #pragma unroll
-        for (int g = 0; g < G; ++g) w[g] *= sc;
-        if constexpr (FMT == KV_FMT_K8V4) {
+        for (int i = 0; i < 16; ++i) {
+          const float vf = cur.ch[u].get(i);
 #pragma unroll
-          for (int g = 0; g < G; ++g) accw[g] += w[g];
-          // even and odd nibbles of each word moved into byte lanes: each value is
-          // then one byte-to-float conversion
-          const u32x4& cw = cur.ch[u].w;
-          const uint32_t nb[4] = {nibble_bytes(cw[0]), nibble_bytes(cw[0] >> 4),
-                                  nibble_bytes(cw[1]), nibble_bytes(cw[1] >> 4)};
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const uint32_t src = nb[2 * (i >> 3) + (i & 1)];
-            const float vf = (float)((src >> (8 * ((i & 7) >> 1))) & 0xFFu);   // code + 8
-#pragma unroll
-            for (int g = 0; g < G; ++g) acc[g][i] = fmaf(w[g], vf, acc[g][i]);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float vf = cur.ch[u].get(i);
-#pragma unroll
-            for (int g = 0; g < G; ++g) acc[g][i] = fmaf(w[g], vf, acc[g][i]);
-          }
+          for (int g = 0; g < G; ++g) acc[g][i] = fmaf(w[g], vf, acc[g][i]);
         }
       }
     };
@@ -771,7 +647,6 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
         const float f = exp2f(m[g] - mn);   // 0 on the first chunk (m = -inf)
         m[g] = mn;
         l[g] *= f;
-        accw[g] *= f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[g][i] *= f;
       }
@@ -788,62 +663,37 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     };
     auto vpass = [&](int s0, int s1) __attribute__((always_inline)) {
       for (int it0 = s0; it0 < s1; it0 += 2 * U) {
-        B.template load<true>(vb, vsb, gw, W, it0 + U, len, r, c, kclamp, pm);
+        B.template load<true>(vb, nsc, gw, W, it0 + U, len, r, c, kclamp, pm);
         vstep(A, it0, n_it);
-        if (it0 + 2 * U < s1) A.template load<true>(vb, vsb, gw, W, it0 + 2 * U, len, r, c, kclamp, pm);
+        if (it0 + 2 * U < s1) A.template load<true>(vb, nsc, gw, W, it0 + 2 * U, len, r, c, kclamp, pm);
         vstep(B, it0 + U, n_it);
       }
     };
-    if constexpr (MF) {
-      // ---- K pass on the matrix cores ------------------------------------------
-      KBatch<UK> KA, KB;
-      KA.load(kb, ksb, gw, W, 0, len, lane, kclamp, pm);
-      for (int it0 = 0; it0 < n_it; it0 += 2 * UK) {
-        KB.load(kb, ksb, gw, W, it0 + UK, len, lane, kclamp, pm);
-        kstep_m(KA, it0);
-        if (it0 + 2 * UK < n_it) KA.load(kb, ksb, gw, W, it0 + 2 * UK, len, lane, kclamp, pm);
-        kstep_m(KB, it0 + UK);
-      }
-      // the first V batch after the loop: its registers are then not live across it
-      A.template load<true>(vb, vsb, gw, W, 0, len, r, c, kclamp, pm);
-      wave_lds_fence();
-      softmax(0, n_it, (n_it + 2 * U - 1) / (2 * U) * (2 * U));
-      wave_lds_fence();
-      // ---- V pass ---------------------------------------------------------------
-      vpass(0, n_it);
-    } else {
-      // ---- K pass ---------------------------------------------------------------
-      A.template load<false>(kb, ksb, gw, W, 0, len, r, c, kclamp, pm);
-      for (int it0 = 0; it0 < n_it; it0 += 2 * U) {
-        B.template load<false>(kb, ksb, gw, W, it0 + U, len, r, c, kclamp, pm);
-        kstep(A, 0, it0, n_it);
-        if (it0 + 2 * U < n_it)
-          A.template load<false>(kb, ksb, gw, W, it0 + 2 * U, len, r, c, kclamp, pm);
-        else
-          A.template load<true>(vb, vsb, gw, W, 0, len, r, c, kclamp, pm);
-        kstep(B, 0, it0 + U, n_it);
-      }
-      wave_lds_fence();
-      softmax(0, n_it, (n_it + 2 * U - 1) / (2 * U) * (2 * U));
-      wave_lds_fence();
-      // ---- V pass ---------------------------------------------------------------
-      vpass(0, n_it);
+    // ---- K pass -----------------------------------------------------------------
+    A.template load<false>(kb, nsc, gw, W, 0, len, r, c, kclamp, pm);
+    for (int it0 = 0; it0 < n_it; it0 += 2 * U) {
+      B.template load<false>(kb, nsc, gw, W, it0 + U, len, r, c, kclamp, pm);
+      kstep(A, 0, it0, n_it);
+      if (it0 + 2 * U < n_it)
+        A.template load<false>(kb, nsc, gw, W, it0 + 2 * U, len, r, c, kclamp, pm);
+      else
+        A.template load<true>(vb, nsc, gw, W, 0, len, r, c, kclamp, pm);
+      kstep(B, 0, it0 + U, n_it);
     }
+    wave_lds_fence();
+    softmax(0, n_it, (n_it + 2 * U - 1) / (2 * U) * (2 * U));
+    wave_lds_fence();
+    // ---- V pass -----------------------------------------------------------------
+    vpass(0, n_it);
 #pragma unroll
     for (int g = 0; g < G; ++g) l[g] = wave_sum(l[g]);
-    if constexpr (FMT == KV_FMT_K8V4) {  // sum_t w_t (n - 8) = sum_t w_t n - 8 sum_t w_t
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[g][i] = fmaf(-8.f, accw[g], acc[g][i]);
-    }
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[g][i] = sum_rows8(acc[g][i]);
   }
 
-  // ---- combine the 4 wave partials of the workgroup --------------------------
+  // ---- combine the 8 wave partials of the workgroup --------------------------
   if (r == 0) {
 #pragma unroll
     for (int g = 0; g < G; ++g)
@@ -891,9 +741,6 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
 //   barrier per chunk hands a buffer from the K wave to the V wave and back.  Each
 //   wave keeps one kind of load in flight all the time, and the V wave's arithmetic
 //   overlaps the K wave's loads on the same SIMD.
-#ifndef KVQ8_DEC_PAIR
-#define KVQ8_DEC_PAIR 1
-#endif
 #ifndef KVQ8_DEC_PAIR_CH
 #define KVQ8_DEC_PAIR_CH 16
 #endif
@@ -1230,50 +1077,65 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
   }
 }
 
-// k_decode_pair_mv: the q8 format (1, 2 or 4 query heads per kv head) with both
+// k_decode_pair_mv: the int8-K formats with 1, 2 or 4 query heads per kv head, both
 //   products on the matrix cores, in the pairs of k_decode_pair.
 //   K wave: the logits as in k_decode_pair; then, per 64-token block (8 steps), the
-//     weights w = p * (V scale of the token's 64-dim group), each split into two bf16
+//     weights w = p * (V scale of the token's group of dims), each split into two bf16
 //     values, hi = w truncated to bf16 and lo = (w - hi) rounded to bf16
 //     (|w - hi - lo| <= 2^-16 |w|), written to LDS in the layout of an MFMA A operand:
-//     16 rows (64-dim group, head, hi / lo) by the block's 64 tokens.
-//   V wave: stages the block's V rows in an LDS tile as loaded and reads them back
-//     transposed (ds_read_b64_tr_b8: 16 lanes receive one dim each, 8 tokens per
-//     read); the int8 codes become bf16 exactly (an integer of at most 7 bits is the
-//     upper half of its fp32 value), and one v_mfma_f32_16x16x32_bf16 per 16 dims and
-//     32 tokens accumulates the rows' products in fp32.  The block's 64 tokens are the
-//     k-slots of both operands in the same order.  Lane (q, i) of a 16-dim tile holds
-//     rows 4q .. 4q + 3; the tiles of group 0 use rows 0 .. 7, those of group 1 rows
-//     8 .. 15, so each tile's other half is discarded.
+//     a table of 16 rows (two groups of dims, 4 heads, hi / lo) by the block's 64
+//     tokens.  Q8 has two 64-dim groups: one table.  K8V4 has four 32-dim groups of
+//     its rotated V: two tables, groups 0-1 and 2-3.
+//   V wave: stages the block's V rows in an LDS tile as signed bytes (Q8: the codes as
+//     loaded; K8V4: each nibble n made the byte n - 8, two per input byte, so the tile
+//     holds the codes of the rotated row in dim order) and reads them back transposed
+//     (ds_read_b64_tr_b8: 16 lanes receive one dim each, 8 tokens per read); a code of
+//     at most 7 bits becomes bf16 exactly (the upper half of its fp32 value), and one
+//     v_mfma_f32_16x16x32_bf16 per 16 dims and 32 tokens accumulates the rows'
+//     products in fp32.  The block's 64 tokens are the k-slots of both operands in the
+//     same order.  Lane (q, i) of a 16-dim tile holds rows 4q .. 4q + 3 of its table;
+//     the tile's dims belong to one group, whose rows (0 .. 7 or 8 .. 15) are kept.
+//     K8V4 leaves its output in the rotated basis; the merge undoes the rotation.
 //   Against the vector V pass this moves the 64 FMAs a lane spends per step and 4
-//   heads onto the matrix cores; the V wave keeps 12 conversions per 8 codes.
-#ifndef KVQ8_DEC_MV
-#define KVQ8_DEC_MV 1   // 0: the int8 decode keeps the vector V pass
-#endif
+//   heads onto the matrix cores; the V wave keeps 12 conversions per 8 codes (K8V4:
+//   plus 9 bit operations per 8 nibbles).
 #ifndef KVQ8_DEC_MV_CH
 #define KVQ8_DEC_MV_CH 16
 #endif
-constexpr int MV_CH = KVQ8_DEC_MV_CH;  // steps per chunk
+constexpr int MV_CH = KVQ8_DEC_MV_CH;  // steps per chunk (Q8)
 constexpr int MV_BLK = 8;              // steps per 64-token block
 constexpr int MV_PITCH = 144;          // bytes per V tile row (16-byte aligned rows)
 constexpr int MV_AROW = 32;            // weight-table bytes per token (16 bf16 rows)
 static_assert(MV_CH % (2 * MV_BLK) == 0, "a chunk holds whole pairs of blocks");
 
-template <int G>
+// steps per chunk: K8V4's two weight tables per block take one-block chunks, so that
+// two workgroups still share a CU's LDS
+template <int FMT>
+__host__ __device__ constexpr int mv_chunk() { return FMT == KV_FMT_K8V4 ? MV_BLK : MV_CH; }
+template <int FMT>
+__host__ __device__ constexpr int mv_tables() { return FMT == KV_FMT_K8V4 ? 2 : 1; }
+template <int FMT, int G>
 __host__ __device__ constexpr size_t mv_pair_bytes() {
   // logits of one chunk, the weight tables of two chunks, the rescale factors of two
   // chunks, the V tile
-  return (size_t)MV_CH * 8 * G * 4 + 2 * (size_t)MV_CH * 8 * MV_AROW + 2 * 4 * 4 +
-         64 * MV_PITCH;
+  return (size_t)mv_chunk<FMT>() * 8 * G * 4 +
+         2 * (size_t)mv_chunk<FMT>() * 8 * MV_AROW * mv_tables<FMT>() + 2 * 4 * 4 + 64 * MV_PITCH;
 }
-template <int G>
+template <int FMT, int G>
 __host__ __device__ constexpr size_t mv_lds_bytes() {
-  return PAIRS * mv_pair_bytes<G>() + DEC_WAVES * 64 * 4;
+  return PAIRS * mv_pair_bytes<FMT, G>() + DEC_WAVES * 64 * 4;
 }
-static_assert(mv_pair_bytes<4>() % 16 == 0 && mv_pair_bytes<2>() % 16 == 0 &&
-                  mv_pair_bytes<1>() % 16 == 0, "pair regions keep 16-byte alignment");
-static_assert(PAIRS * mv_pair_bytes<1>() >= sizeof(float) * (PAIRS * 4 * HD + 2 * PAIRS * 4),
+static_assert(mv_pair_bytes<KV_FMT_Q8, 4>() % 16 == 0 && mv_pair_bytes<KV_FMT_Q8, 2>() % 16 == 0 &&
+                  mv_pair_bytes<KV_FMT_Q8, 1>() % 16 == 0 &&
+                  mv_pair_bytes<KV_FMT_K8V4, 4>() % 16 == 0 &&
+                  mv_pair_bytes<KV_FMT_K8V4, 2>() % 16 == 0 &&
+                  mv_pair_bytes<KV_FMT_K8V4, 1>() % 16 == 0,
+              "pair regions keep 16-byte alignment");
+static_assert(PAIRS * mv_pair_bytes<KV_FMT_K8V4, 1>() >=
+                  sizeof(float) * (PAIRS * 4 * HD + 2 * PAIRS * 4),
               "the final partials fit in the pair regions");
+static_assert(mv_lds_bytes<KV_FMT_Q8, 4>() <= 80 * 1024 && mv_lds_bytes<KV_FMT_K8V4, 4>() <= 80 * 1024,
+              "two workgroups share a CU's 160 KB of LDS");
 
 // max(a, b) in one instruction (the median of a, b and +inf; no NaN quieting)
 __device__ __forceinline__ float max2(float a, float b) {
@@ -1315,17 +1177,31 @@ __device__ __forceinline__ bf16x8 codes_bf16(i32x2 c) {
   }
   return __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
 }
-template <int G, int PG, int SP>
+// 8 nibbles (a 32-bit word: value j in bits 4j .. 4j + 3, stored as code + 8) as 8
+// signed bytes code = n - 8 in value order (two words).  Per byte, n + 0x78 <= 0x87
+// carries into no other byte, and flipping bit 7 of it gives n - 8 in two's complement.
+__device__ __forceinline__ void nibbles_to_codes(uint32_t x, uint32_t& o0, uint32_t& o1) {
+  const uint32_t lo = nibble_bytes(x), hi = nibble_bytes(x >> 4);   // values 0,2,4,6 / 1,3,5,7
+  o0 = (__builtin_amdgcn_perm(hi, lo, 0x05010400u) + 0x78787878u) ^ 0x80808080u;
+  o1 = (__builtin_amdgcn_perm(hi, lo, 0x07030602u) + 0x78787878u) ^ 0x80808080u;
+}
+template <int FMT, int G, int PG, int SP>
 __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_PAIR_WPE)))
 void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restrict__ lens,
                       int max_len, int kvh, const float* __restrict__ q, float qscale,
                       float* __restrict__ ws_o, float* __restrict__ ws_lse, int S,
                       const int32_t* __restrict__ pages, int page_stride) {
-  constexpr int FMT = KV_FMT_Q8;
+  static_assert(FMT == KV_FMT_Q8 || FMT == KV_FMT_K8V4, "int8 K codes");
   static_assert(G <= 4, "one block of 4 heads");
-  constexpr int UK = k_batch_rows<G>();
-  static_assert(MV_CH % (2 * UK) == 0, "a chunk holds whole pairs of K batches");
-  constexpr int NCB = MV_CH / MV_BLK;            // blocks per chunk
+  constexpr bool K4 = FMT == KV_FMT_K8V4;
+  constexpr int CHK = mv_chunk<FMT>();           // steps per chunk
+  constexpr int UK = CHK / 2;                    // steps per K batch: two per chunk
+  constexpr int NT = mv_tables<FMT>();           // weight tables per block
+  static_assert(CHK % MV_BLK == 0 && (UK == MV_BLK || 2 * UK == MV_BLK),
+                "a chunk is whole blocks; a K batch is a block or half of one");
+  constexpr int NCB = CHK / MV_BLK;              // blocks per chunk
+  constexpr int VROW = K4 ? HD / 2 : HD;         // bytes per V row
+  constexpr int VSC = K4 ? NQ4 : NGRP;           // V scales per row
   const int s_idx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int nqh = kvh * G;
   const kv_session ss = tab[b];
@@ -1347,24 +1223,25 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
   const int NU = (J + SP - 1) / SP;
   const int nu = gw < NU ? (NU - 1 - gw) / W + 1 : 0;
   const int n_steps = nu ? min(SP * nu, J - SP * (gw + (nu - 1) * W) + SP * (nu - 1)) : 0;
-  // chunks: pair 0 holds the most units (a bound on every pair's steps)
+  // steps the pairs run through: pair 0 holds the most units (a bound on every pair's
+  // steps), rounded to whole pairs of blocks (whole chunks; the V wave takes blocks in
+  // pairs)
   const int n_first = s_idx * PAIRS < NU ? SP * ((NU - 1 - s_idx * PAIRS) / W + 1) : 0;
-  const int n_chunks = (n_first + MV_CH - 1) / MV_CH;
+  const int total = (n_first + 2 * MV_BLK - 1) / (2 * MV_BLK) * (2 * MV_BLK);
   const int kmax = max(n_steps - 1, 0);
-  const int total = n_chunks * MV_CH;
   // paged (PG: the page map's registers, 0 for a contiguous session): this pair's
   // steps -> pool slots; steps past the session's end read its last step
   std::conditional_t<PG != 0, PageMap<PG ? PG : 4, SP>, NoPages> pm{};
   if constexpr (PG != 0) pm.init(pages, page_stride, b, gw, W, n_steps, ss.cap / KV_PAGE_ROWS, len, lane);
 
   extern __shared__ float smem[];
-  uint8_t* reg = reinterpret_cast<uint8_t*>(smem) + (size_t)pr * mv_pair_bytes<G>();
-  float* lc = reinterpret_cast<float*>(reg);                               // [CH*8][G]
-  uint8_t* at = reg + (size_t)MV_CH * 8 * G * 4;                           // [2][CH*8][AROW]
-  float* fb = reinterpret_cast<float*>(at + 2 * MV_CH * 8 * MV_AROW);       // [2][4]
-  uint8_t* tile = reinterpret_cast<uint8_t*>(fb + 8);                      // [64][PITCH]
+  uint8_t* reg = reinterpret_cast<uint8_t*>(smem) + (size_t)pr * mv_pair_bytes<FMT, G>();
+  float* lc = reinterpret_cast<float*>(reg);                            // [CHK*8][G]
+  uint8_t* at = reg + (size_t)CHK * 8 * G * 4;                          // [2][CHK/8][NT][64][AROW]
+  float* fb = reinterpret_cast<float*>(at + 2 * CHK * 8 * MV_AROW * NT);  // [2][4]
+  uint8_t* tile = reinterpret_cast<uint8_t*>(fb + 8);                   // [64][PITCH]
   float* junk = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem) +
-                                         PAIRS * mv_pair_bytes<G>()) + wave * 64;
+                                         PAIRS * mv_pair_bytes<FMT, G>()) + wave * 64;
   // after the loops every pair region is free: the partials reuse them
   float* o_l = smem;                         // [pairs][G][HD]
   float* m_l = o_l + PAIRS * G * HD;         // [pairs][G]
@@ -1372,9 +1249,16 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
 
   const size_t hrow = (size_t)h * (size_t)ss.cap;
   const char* kb = static_cast<const char*>(ss.k) + hrow * HD;
-  const char* vb = static_cast<const char*>(ss.v) + hrow * HD;
+  const char* vb = static_cast<const char*>(ss.v) + hrow * VROW;
   const char* ksb = reinterpret_cast<const char*>(ss.k_scale) + hrow * NGRP * 2;
-  const char* vsb = reinterpret_cast<const char*>(ss.v_scale) + hrow * NGRP * 2;
+  const char* vsb = reinterpret_cast<const char*>(ss.v_scale) + hrow * VSC * 2;
+  // the pool row (contiguous: the row) of token 64 bl + lane of the chunk starting at
+  // step ch CHK: row lane % 8 of its step
+  auto chunk_row = [&](int ch, int bl) __attribute__((always_inline)) {
+    const int st = ch * CHK + bl * 8 + (lane >> 3);
+    if constexpr (PG != 0) return pm.lane_row(pm.block(ch * CHK + bl * 8), st, gw, W, lane & 7);
+    else return (uint32_t)min(step_g<SP>(gw, min(st, kmax), W) * 8 + (lane & 7), len - 1);
+  };
 
   if (kw) {
     // ================= K wave ===================================================
@@ -1429,14 +1313,14 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
       }
     }
     // the K scales of the batch's tokens come from the chunk's scale words: token
-    // n = lane % 16 of block j is lane 16 j + n of the chunk's 64-token block kr / 8
-    // (ksw: the scale word of the block holding the batch, kr its first step)
-    static_assert(2 * UK == MV_CH && UK * 8 == 64, "a chunk is two K batches, one per block");
+    // n = lane % 16 of 16-token piece j of the batch (first step kr of its chunk) is
+    // lane 8 kr + 16 j + n (mod 64) of its 64-token block (ksw: that block's word)
     auto kstep = [&](const KBatch<UK, SP, false>& cur, int kr, uint32_t ksw)
         __attribute__((always_inline)) {
 #pragma unroll
       for (int j = 0; j < UK / 2; ++j) {
-        const uint32_t kw2 = (uint32_t)__shfl((int)ksw, 16 * j + (lane & 15), 64);
+        const uint32_t kw2 =
+            (uint32_t)__shfl((int)ksw, ((8 * kr) & 63) + 16 * j + (lane & 15), 64);
         const float ks[NGRP] = {h2f((uint16_t)(kw2 & 0xFFFFu)), h2f((uint16_t)(kw2 >> 16))};
         float v = 0.f;
 #pragma unroll
@@ -1454,111 +1338,124 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         *dst = v;
       }
     };
-    // The scale words of a chunk: lane l of block bl holds both 64-dim group scales
-    // (4 bytes) of token 64 bl + l of the chunk, one 32-bit load per lane and block.
-    auto chunk_scales = [&](const char* sb, int ch, uint32_t (&dst)[NCB]) __attribute__((always_inline)) {
+    // the K scale words of a chunk: lane l of block bl holds both 64-dim group scales
+    // (4 bytes) of token 64 bl + l of the chunk, one 32-bit load per lane and block
+    uint32_t ksn[NCB], ksx[NCB] = {};   // this chunk's and the next one's
+    auto k_scales = [&](int ch, uint32_t (&dst)[NCB]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int bl = 0; bl < NCB; ++bl)
+        dst[bl] = *(const KVQ8_GLOBAL uint32_t*)(ksb + chunk_row(ch, bl) * NGRP * 2);
+    };
+    // the V scales of a chunk, loaded as it starts: per lane and block the token's
+    // VSC fp16 scales
+    uint32_t svn[NCB][VSC / 2];
+    auto chunk_start = [&](int ch) __attribute__((always_inline)) {
 #pragma unroll
       for (int bl = 0; bl < NCB; ++bl) {
-        const int st = ch * MV_CH + bl * 8 + (lane >> 3);
-        uint32_t row;
-        if constexpr (PG != 0)
-          row = pm.lane_row(pm.block(ch * MV_CH + bl * 8), st, gw, W, lane & 7);
-        else
-          row = (uint32_t)min(step_g<SP>(gw, min(st, kmax), W) * 8 + (lane & 7), len - 1);
-        dst[bl] = *(const KVQ8_GLOBAL uint32_t*)(sb + row * NGRP * 2);
+        const uint32_t row = chunk_row(ch, bl);
+        if constexpr (K4) {
+          const u32x2 t = *(const KVQ8_GLOBAL u32x2*)(vsb + row * VSC * 2);
+          svn[bl][0] = t[0];
+          svn[bl][1] = t[1];
+        } else {
+          svn[bl][0] = *(const KVQ8_GLOBAL uint32_t*)(vsb + row * VSC * 2);
+        }
       }
+      if ((ch + 1) * CHK < total) k_scales(ch + 1, ksx);
+    };
+    // the chunk's softmax, then per block the weight tables; a barrier hands them over
+    auto chunk_end = [&](int ch) __attribute__((always_inline)) {
+#pragma unroll
+      for (int bl = 0; bl < NCB; ++bl) ksn[bl] = ksx[bl];
+      wave_lds_fence();
+      const int c0 = ch * CHK;
+      const int nl = max(0, min(n_steps, c0 + CHK) - c0) * 8;
+      float mc[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) mc[g] = -INFINITY;
+#pragma unroll
+      for (int bl = 0; bl < NCB; ++bl) {
+        const int tl = bl * 64 + lane;
+        const int t = step_g<SP>(gw, c0 + (tl >> 3), W) * 8 + (tl & 7);
+        if (tl < nl && t < len) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) mc[g] = max2(mc[g], lc[tl * G + g]);
+        }
+      }
+      float* fc = fb + (ch & 1) * 4;
+      float cm[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) cm[g] = wave_max_dpp(mc[g]);
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float mn = max2(m[g], cm[g]);
+        const float f = mn == -INFINITY ? 1.f : exp2f(m[g] - mn);
+        m[g] = mn;
+        l[g] *= f;
+        if (lane == g) fc[g] = f;
+      }
+      uint8_t* atc = at + (ch & 1) * CHK * 8 * MV_AROW * NT;
+#pragma unroll
+      for (int bl = 0; bl < NCB; ++bl) {
+        const int tl = bl * 64 + lane;
+        const int st = c0 + (tl >> 3);
+        const int t = step_g<SP>(gw, st, W) * 8 + (tl & 7);
+        const bool ok = tl < nl && t < len;
+        float sv[VSC];
+#pragma unroll
+        for (int k = 0; k < VSC / 2; ++k) {
+          sv[2 * k] = h2f((uint16_t)(svn[bl][k] & 0xFFFFu));
+          sv[2 * k + 1] = h2f((uint16_t)(svn[bl][k] >> 16));
+        }
+        // the weights w = p * s_v and their bf16 split: hi = w truncated to bf16, lo =
+        // the rest rounded to bf16 (|w - hi - lo| <= 2^-16 |w|)
+        float p4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float p = 0.f;
+          if (g < G) {
+            p = ok ? exp2f(lc[tl * G + g] - m[g]) : 0.f;
+            l[g] += p;
+          }
+          p4[g] = p;
+        }
+        // A operand layout: table grp / 2, row m = 8 (grp % 2) + 2 head + part, token
+        // k = lane = 8 g8 + j at byte (g8 16 + (m ^ g8)) 16 + 2 j of the table's 2 KB
+        const int g8 = lane >> 3, jt = lane & 7;
+#pragma unroll
+        for (int grp = 0; grp < VSC; ++grp) {
+          uint8_t* atb = atc + ((size_t)bl * NT + (grp >> 1)) * 64 * MV_AROW;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float w = p4[g] * sv[grp];
+            const uint32_t wb = __builtin_bit_cast(uint32_t, w);
+            const uint32_t hib = wb & 0xFFFF0000u;
+            const float lo = w - __builtin_bit_cast(float, hib);
+            const uint16_t lob = __builtin_bit_cast(uint16_t, (__bf16)lo);
+            const int m0 = 8 * (grp & 1) + 2 * g;
+            *reinterpret_cast<uint16_t*>(atb + (g8 * 16 + (m0 ^ g8)) * 16 + 2 * jt) =
+                (uint16_t)(hib >> 16);
+            *reinterpret_cast<uint16_t*>(atb + (g8 * 16 + ((m0 + 1) ^ g8)) * 16 + 2 * jt) = lob;
+          }
+        }
+      }
+      __syncthreads();
     };
     KBatch<UK, SP, false> KA, KB;
-    uint32_t svn[NCB];   // the chunk's V scales, loaded as it starts
-    uint32_t ksn[NCB], ksx[NCB] = {};   // the K scales of this chunk and of the next
     if (total > 0) {
-      chunk_scales(ksb, 0, ksn);
+      k_scales(0, ksn);
       KA.load(kb, ksb, gw, W, 0, len, lane, kmax, pm);
     }
-    for (int k0 = 0; k0 < total; k0 += 2 * UK) {
-      const int ch = k0 / MV_CH, kr = k0 - ch * MV_CH;
-      if (kr == 0) {
-        chunk_scales(vsb, ch, svn);
-        if (k0 + MV_CH < total) chunk_scales(ksb, ch + 1, ksx);
-      }
+    // one chunk per iteration, two K batches of it (the second's scale word is that of
+    // its block: the chunk's second block for Q8, the same block for K8V4)
+    for (int k0 = 0; k0 < total; k0 += CHK) {
+      const int ch = k0 / CHK;
+      chunk_start(ch);
       KB.load(kb, ksb, gw, W, k0 + UK, len, lane, kmax, pm);
-      kstep(KA, kr, ksn[0]);
+      kstep(KA, 0, ksn[0]);
       KA.load(kb, ksb, gw, W, k0 + 2 * UK, len, lane, kmax, pm);
-      kstep(KB, kr + UK, ksn[1]);
-      if (kr + 2 * UK == MV_CH) {
-#pragma unroll
-        for (int bl = 0; bl < NCB; ++bl) ksn[bl] = ksx[bl];
-        wave_lds_fence();
-        // the chunk's softmax, then per block the weight table
-        const int c0 = ch * MV_CH;
-        const int nl = max(0, min(n_steps, c0 + MV_CH) - c0) * 8;
-        float mc[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) mc[g] = -INFINITY;
-#pragma unroll
-        for (int bl = 0; bl < NCB; ++bl) {
-          const int tl = bl * 64 + lane;
-          const int t = step_g<SP>(gw, c0 + (tl >> 3), W) * 8 + (tl & 7);
-          if (tl < nl && t < len) {
-#pragma unroll
-            for (int g = 0; g < G; ++g) mc[g] = max2(mc[g], lc[tl * G + g]);
-          }
-        }
-        float* fc = fb + (ch & 1) * 4;
-        float cm[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) cm[g] = wave_max_dpp(mc[g]);
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float mn = max2(m[g], cm[g]);
-          const float f = mn == -INFINITY ? 1.f : exp2f(m[g] - mn);
-          m[g] = mn;
-          l[g] *= f;
-          if (lane == g) fc[g] = f;
-        }
-        uint8_t* atc = at + (ch & 1) * MV_CH * 8 * MV_AROW;
-#pragma unroll
-        for (int bl = 0; bl < NCB; ++bl) {
-          const int tl = bl * 64 + lane;
-          const int st = c0 + (tl >> 3);
-          const int t = step_g<SP>(gw, st, W) * 8 + (tl & 7);
-          const bool ok = tl < nl && t < len;
-          const uint32_t svw = svn[bl];
-          const float sv[NGRP] = {h2f((uint16_t)(svw & 0xFFFFu)), h2f((uint16_t)(svw >> 16))};
-          // the weights w = p * s_v and their bf16 split: hi = w truncated to bf16, lo =
-          // the rest rounded to bf16 (|w - hi - lo| <= 2^-16 |w|)
-          float w[4][NGRP];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            float p = 0.f;
-            if (g < G) {
-              p = ok ? exp2f(lc[tl * G + g] - m[g]) : 0.f;
-              l[g] += p;
-            }
-#pragma unroll
-            for (int grp = 0; grp < NGRP; ++grp) w[g][grp] = p * sv[grp];
-          }
-          // A operand layout: row m = 8 grp + 2 head + part, token k = lane = 8 g8 + j
-          // at byte (g8 16 + (m ^ g8)) 16 + 2 j of the block's 2 KB
-          uint8_t* atb = atc + (size_t)bl * 64 * MV_AROW;
-          const int g8 = lane >> 3, jt = lane & 7;
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-#pragma unroll
-            for (int grp = 0; grp < NGRP; ++grp) {
-              const uint32_t wb = __builtin_bit_cast(uint32_t, w[g][grp]);
-              const uint32_t hib = wb & 0xFFFF0000u;
-              const float lo = w[g][grp] - __builtin_bit_cast(float, hib);
-              const uint16_t lob = __builtin_bit_cast(uint16_t, (__bf16)lo);
-              const int m0 = 8 * grp + 2 * g;
-              *reinterpret_cast<uint16_t*>(atb + (g8 * 16 + (m0 ^ g8)) * 16 + 2 * jt) =
-                  (uint16_t)(hib >> 16);
-              *reinterpret_cast<uint16_t*>(atb + (g8 * 16 + ((m0 + 1) ^ g8)) * 16 + 2 * jt) = lob;
-            }
-          }
-        }
-        __syncthreads();
-      }
+      kstep(KB, UK, ksn[(8 * UK) / 64]);
+      chunk_end(ch);
     }
     __syncthreads();   // the V wave's last chunk
 #pragma unroll
@@ -1574,28 +1471,33 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
     // ================= V wave ===================================================
     const int qv = lane >> 4, iv = lane & 15;
     // D tile jd (dims 16 jd ..): lane (qv, iv) holds rows 4 qv .. 4 qv + 3 of dim
-    // 16 jd + iv, rows m = 8 grp + 2 head + part; heads ha, ha + 1 of this lane
+    // 16 jd + iv of its table, rows m = 8 (group % 2) + 2 head + part; heads ha, ha + 1
     const int ha = 2 * (qv & 1);
     f32x4 acc[8];
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) acc[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto vload = [&](u32x4 (&vw)[MV_BLK], int blk) __attribute__((always_inline)) {
+    // a lane's 16 dims of one row of a step: Q8 the 16 codes, K8V4 8 bytes of nibbles
+    using VW = std::conditional_t<K4, u32x2, u32x4>;
+    auto vload = [&](VW (&vw)[MV_BLK], int blk) __attribute__((always_inline)) {
       int pv = 0;
       if constexpr (PG != 0) pv = pm.block(blk * MV_BLK);   // the block's 8 steps share it
 #pragma unroll
       for (int u = 0; u < MV_BLK; ++u) {
+        const char* base = vb;
+        uint32_t row;
         if constexpr (PG != 0) {
           int pb, lim;
           pm.step(pv, blk * MV_BLK + u, gw, W, pb, lim);
-          vw[u] = ldkv(vb + (size_t)pb * HD, (uint32_t)min(r, lim) * HD + c * 16);
+          base += (size_t)pb * VROW;
+          row = (uint32_t)min(r, lim);
         } else {
-          const uint32_t row =
-              (uint32_t)min(step_g<SP>(gw, min(blk * MV_BLK + u, kmax), W) * 8 + r, len - 1);
-          vw[u] = ldkv(vb, row * HD + c * 16);
+          row = (uint32_t)min(step_g<SP>(gw, min(blk * MV_BLK + u, kmax), W) * 8 + r, len - 1);
         }
+        if constexpr (K4) vw[u] = ldkv64(base, row * VROW + c * 8);
+        else vw[u] = ldkv(base, row * VROW + c * 16);
       }
     };
-    auto vblock = [&](const u32x4 (&vw)[MV_BLK], int blk) __attribute__((always_inline)) {
+    auto vblock = [&](const VW (&vw)[MV_BLK], int blk) __attribute__((always_inline)) {
       const int ch = blk / NCB, bl = blk - ch * NCB;
       if (bl == 0) {
         if (ch > 0) __syncthreads();   // the K wave's chunk ch
@@ -1609,27 +1511,41 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
           acc[jd][3] *= fc;
         }
       }
-      // the block's rows, token u * 8 + r, as loaded
+      // the block's rows, token u * 8 + r, as signed codes in dim order
 #pragma unroll
-      for (int u = 0; u < MV_BLK; ++u)
-        *reinterpret_cast<u32x4*>(tile + (u * 8 + r) * MV_PITCH + c * 16) = vw[u];
+      for (int u = 0; u < MV_BLK; ++u) {
+        u32x4 cw;
+        if constexpr (K4) {
+          uint32_t o[4];
+          nibbles_to_codes(vw[u][0], o[0], o[1]);
+          nibbles_to_codes(vw[u][1], o[2], o[3]);
+          cw = u32x4{o[0], o[1], o[2], o[3]};
+        } else {
+          cw = vw[u];
+        }
+        *reinterpret_cast<u32x4*>(tile + (u * 8 + r) * MV_PITCH + c * 16) = cw;
+      }
       wave_lds_fence();
-      const uint8_t* atb = at + (ch & 1) * MV_CH * 8 * MV_AROW + bl * 64 * MV_AROW;
+      const uint8_t* atb = at + (ch & 1) * CHK * 8 * MV_AROW * NT + bl * NT * 64 * MV_AROW;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int g8 = 4 * hh + qv;   // tokens 8 g8 .. 8 g8 + 7 of the block
-        const bf16x8 aw = *reinterpret_cast<const bf16x8*>(atb + (g8 * 16 + (iv ^ g8)) * 16);
+        bf16x8 aw[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          aw[t] = *reinterpret_cast<const bf16x8*>(atb + t * 64 * MV_AROW + (g8 * 16 + (iv ^ g8)) * 16);
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) {
           // B: the codes of tokens 8 g8 + 0 .. 7, dim 16 jd + iv, as bf16 (exact)
           const i32x2 cb = lds_tr8(tile + (8 * g8 + (iv >> 1)) * MV_PITCH + 16 * jd + 8 * (iv & 1));
-          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, codes_bf16(cb), acc[jd], 0, 0, 0);
+          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[K4 ? jd >> 2 : 0], codes_bf16(cb),
+                                                            acc[jd], 0, 0, 0);
         }
       }
       wave_lds_fence();
     };
     const int nblk = total / MV_BLK;
-    u32x4 VA[MV_BLK], VB[MV_BLK];
+    VW VA[MV_BLK], VB[MV_BLK];
     if (nblk > 0) vload(VA, 0);
     __syncthreads();   // the K wave's first chunk
     for (int blk = 0; blk < nblk; blk += 2) {
@@ -1641,7 +1557,10 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
     if (nblk > 0) __syncthreads();   // frees the K wave's last buffers
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) {
-      if ((qv >> 1) == (jd >> 2)) {   // this lane's rows are of the tile's group
+      // the tile's dims belong to group jd / 4 (Q8) or jd / 2 (K8V4); its rows are
+      // 0 .. 7 or 8 .. 15 of the table
+      const int half = K4 ? (jd >> 1) & 1 : jd >> 2;
+      if ((qv >> 1) == half) {
         if (ha < G) o_l[(pr * G + ha) * HD + jd * 16 + iv] = acc[jd][0] + acc[jd][1];
         if (ha + 1 < G) o_l[(pr * G + ha + 1) * HD + jd * 16 + iv] = acc[jd][2] + acc[jd][3];
       }
@@ -1808,11 +1727,12 @@ constexpr int batch_rows() {
   return FMT != KV_FMT_F16 ? (G >= 8 ? 2 : KVQ8_DEC_U_Q8) : KVQ8_DEC_U_F16;
 }
 
+// the int8-K formats take the pair kernels
 template <int FMT>
-constexpr bool use_pair() { return KVQ8_DEC_PAIR && FMT != KV_FMT_F16; }
-// the q8 format with 1, 2 or 4 query heads per kv head: V products on the matrix cores
+constexpr bool use_pair() { return FMT != KV_FMT_F16; }
+// the int8-K formats with 1, 2 or 4 query heads per kv head: V products on the matrix cores
 template <int FMT, int G>
-constexpr bool use_mv() { return KVQ8_DEC_MV && use_pair<FMT>() && FMT == KV_FMT_Q8 && G <= 4; }
+constexpr bool use_mv() { return FMT != KV_FMT_F16 && G <= 4; }
 
 
 // Split workgroups of one kernel instance that fit on the current device at once
@@ -1827,8 +1747,8 @@ int resident_splits() {
   int per_cu = 0, cus = 0;
   hipError_t e;
   if constexpr (use_mv<FMT, G>())
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_pair_mv<G, 0, MV_SP>, DEC_THREADS,
-                                                     mv_lds_bytes<G>());
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_pair_mv<FMT, G, 0, MV_SP>,
+                                                     DEC_THREADS, mv_lds_bytes<FMT, G>());
   else if constexpr (use_pair<FMT>())
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
         &per_cu, k_decode_pair<FMT, G, batch_rows<FMT, G>(), 0>, DEC_THREADS, pair_lds_bytes<G>());
@@ -1876,7 +1796,7 @@ hipError_t launch_split(const kv_session* tab, const int32_t* lens, int n_sess, 
     const long long per_pair = (J + (long long)PAIRS * plan.S - 1) / ((long long)PAIRS * plan.S);
     const bool one = n_sess == 1;
 #define KVQ8_MV_LAUNCH(P, SPV)                                                                 \
-  hipLaunchKernelGGL((k_decode_pair_mv<G, P, SPV>), grid, block, mv_lds_bytes<G>(), st, tab, lens, \
+  hipLaunchKernelGGL((k_decode_pair_mv<FMT, G, P, SPV>), grid, block, (mv_lds_bytes<FMT, G>()), st, tab, lens, \
                      max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages, page_stride)
     if constexpr (!PG) {
       if (one) KVQ8_MV_LAUNCH(0, MV_SP);
@@ -1964,7 +1884,7 @@ DecodePlan decode_plan(int fmt, int kvh, int nqh, int n_sess, int max_len) {
   if (CH0 <= 0) CH0 = 1;  // unsupported G: rejected before any launch
   const long long P = (long long)kvh * n_sess;
   long long S0, Smax;
-  if (q8 && KVQ8_DEC_PAIR) {
+  if (q8) {
     // pairs take any number of steps (in chunks): aim at most PAIR_TARGET_STEPS per
     // pair, and at least PAIR_MIN_STEPS
     S0 = std::max(1LL, (J + PAIRS * PAIR_TARGET_STEPS - 1) / (PAIRS * PAIR_TARGET_STEPS));
