@@ -387,6 +387,22 @@ def _time_calls(torch, calls, reps):
     return [float(np.mean([a.elapsed_time(b) for a, b in e])) * 1e-3 for e in ev]
 
 
+def _time_loop(torch, calls, reps):
+    """Mean seconds per call of the callables in calls run back to back, reps rounds,
+    with one pair of HIP events around the whole run (no per-call events between
+    launches)."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        for f in calls:
+            f()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / (reps * len(calls))
+
+
 def side_configs(kq, torch, steps=10, warmup=3):
     """The smaller workloads: the 64-session int8 batch (session lengths uniform on
     [1024, 65536], one session table; a step is one batched 1-token append and one
@@ -476,19 +492,22 @@ def side_configs(kq, torch, steps=10, warmup=3):
         o = torch.empty((1, NQH, HD), device="cuda")
         calls = [lambda t=t: kq.kv_decode_attn(sh, t, ld, 1, ctx, q, sm, o, ws) for t in tabs]
         _time_calls(torch, calls, warmup)
-        ts = _time_calls(torch, calls, steps)
-        t = float(np.mean(ts))
+        # back to back over the 4 copies (as a model's layers run): the rate; and with
+        # events around each call, which adds each launch's gap
+        t = _time_loop(torch, calls, steps)
+        t_each = float(np.mean(_time_calls(torch, calls, steps)))
         nb = decode_bytes(fmt, ctx)
         name = {F16: "F16", Q8: "int8", K8V4: "K8V4 (int8 K, rotated 4-bit V)"}[fmt]
-        out[key] = {"workload": f"{name} cache, {ctx} cells, 4 copies in turn",
+        out[key] = {"workload": f"{name} cache, {ctx} cells, 4 copies in turn, back to back",
                     "decode_us": t * 1e6, "decode_bytes": nb,
                     "decode_GB_s": nb / t / 1e9, "decode_frac_hbm": nb / t / 1e9 / HBM_PEAK_GBS,
+                    "decode_us_events_each": t_each * 1e6,
                     "bulk_append_cells_per_s": ctx / app}
         # the same copy every call: a layer that fits the 256 MB last-level cache stays
         # in it (what one layer decoded in a loop would see); rotated above is the rate
         hot = [lambda: kq.kv_decode_attn(sh, tabs[0], ld, 1, ctx, q, sm, o, ws)]
         _time_calls(torch, hot, warmup)
-        th = float(np.mean(_time_calls(torch, hot, steps)))
+        th = _time_loop(torch, hot, 4 * steps)
         out[key]["hot_decode_us"] = th * 1e6
         out[key]["hot_decode_GB_s"] = nb / th / 1e9
         # a decode step's one-token append (quantise-on-write for int8), per call
@@ -499,7 +518,7 @@ def side_configs(kq, torch, steps=10, warmup=3):
                                                  stream=kvsynth.S_V_NEW)[None]).cuda()
         app1 = [lambda t=t: kq.kv_append(sh, t, ld1, 1, 1, x1k, x1v) for t in tabs]
         _time_calls(torch, app1, warmup)
-        out[key]["step_append_us"] = float(np.mean(_time_calls(torch, app1, steps))) * 1e6
+        out[key]["step_append_us"] = _time_loop(torch, app1, steps) * 1e6
         log(f"{key}: decode {t * 1e6:.1f} us = {nb / t / 1e9:.0f} GB/s (hot {th * 1e6:.1f} us); "
             f"one-token append {out[key]['step_append_us']:.1f} us")
         if fmt == Q8:

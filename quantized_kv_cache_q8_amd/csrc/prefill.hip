@@ -160,14 +160,24 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) s[kb][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // K fragments (16 = 4 k-steps x 4 key blocks) read from LDS one k-step (4 reads)
+    // ahead of the products that use them; the scheduling barrier keeps the compiler
+    // from moving each read back next to its use, so LDS latency hides behind MFMAs
+    auto kfrag = [&](int i) __attribute__((always_inline)) {
+      const int ks = i >> 2, kb = i & 3;
+      return *reinterpret_cast<const half8*>(&KsC[(16 * kb + l16) * KSTR + 32 * ks + 8 * g4]);
+    };
+    half8 kf[5];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int i = 0; i < 4; ++i) kf[i] = kfrag(i);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const half8 a = *reinterpret_cast<const half8*>(&KsC[(16 * kb + l16) * KSTR + 32 * ks + 8 * g4]);
+    for (int i = 0; i < 16; ++i) {
+      if (i + 4 < 16) kf[(i + 4) % 5] = kfrag(i + 4);
+      __builtin_amdgcn_sched_barrier(0);
+      const half8 a = kf[i % 5];
+      const int ks = i >> 2, kb = i & 3;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) s[kb][rb] = mfma(a, qf[rb][ks], s[kb][rb]);
-      }
+      for (int rb = 0; rb < 2; ++rb) s[kb][rb] = mfma(a, qf[rb][ks], s[kb][rb]);
     }
 
     // ---- online softmax (log2 units) -----------------------------------------
@@ -247,19 +257,28 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
     }
 
     // ---- O^T += V^T P^T -------------------------------------------------------
+    // V^T fragments (16 = 2 key halves x 8 dim blocks) read two ahead of their products,
+    // held in place by the scheduling barrier as above
+    auto vfrag = [&](int i) __attribute__((always_inline)) {
+      const int ks2 = i >> 3, db = i & 7;
+      const _Float16* vp = &VtC[(16 * db + l16) * VSTR + 32 * ks2 + 4 * g4];
+      const uint2 lo = *reinterpret_cast<const uint2*>(vp);
+      const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
+      return __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    };
+    half8 vf[3];
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
+    for (int i = 0; i < 2; ++i) vf[i] = vfrag(i);
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const _Float16* vp = &VtC[(16 * db + l16) * VSTR + 32 * ks2 + 4 * g4];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
-        const half8 a = __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    for (int i = 0; i < 16; ++i) {
+      if (i + 2 < 16) vf[(i + 2) % 3] = vfrag(i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      const half8 a = vf[i % 3];
+      const int ks2 = i >> 3, db = i & 7;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          o[rb][db] = mfma(a, pf[rb][ks2], o[rb][db]);
-          o[rb][db] = mfma(a, pl[rb][ks2], o[rb][db]);
-        }
+      for (int rb = 0; rb < 2; ++rb) {
+        o[rb][db] = mfma(a, pf[rb][ks2], o[rb][db]);
+        o[rb][db] = mfma(a, pl[rb][ks2], o[rb][db]);
       }
     }
 
