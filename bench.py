@@ -246,7 +246,7 @@ CALIB_BYTES = 3 << 28   # 768 MiB: a size no other copy in the probe has
 def traffic_probe(kq, torch, seed):
     """Kernels for counter collection (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE): a
     plain device-to-device copy of CALIB_BYTES (the calibration), then per format
-    one 262144-cell layer: bulk append and 3 decodes."""
+    (FP16, int8, K8V4) one 262144-cell layer: bulk append and 3 decodes."""
     import kvsynth
     a = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
@@ -259,7 +259,7 @@ def traffic_probe(kq, torch, seed):
     xv = torch.from_numpy(kvsynth.kv_tokens(seed, 0, CTX, KVH, HD, "V", True)[None]).cuda()
     q = torch.from_numpy(kvsynth.queries(seed, 0, 1, NQH, HD)).cuda()
     out = torch.empty((1, NQH, HD), device="cuda")
-    for fmt in (F16, Q8):
+    for fmt in (F16, Q8, K8V4):
         sh = kq.make_shape(fmt, KVH, NQH, HD)
         s = kq.Session(fmt, KVH, CTX)
         tab = kq.session_table([s.entry()])
@@ -306,12 +306,11 @@ def traffic_summary(fetch_dir, write_dir, command):
         "write_KiB": float(np.mean([write[i][1] for i in calib])),
         "fetch_factor": f_fac, "write_factor": w_fac}}
     ids = sorted(fetch)
-    for fmt, key in ((F16, "decode_f16"), (Q8, "decode_int8")):
+    for fmt, key in ((F16, "decode_f16"), (Q8, "decode_int8"), (K8V4, "decode_k8v4")):
         # one kv_decode_attn call = one split kernel (k_decode_split for FP16,
-        # k_decode_pair_mv for int8 at 1, 2 or 4 query heads per kv head, else
-        # k_decode_pair) then one k_decode_merge<fmt>
-        tags = (f"k_decode_split<{fmt},", f"k_decode_pair<{fmt},") + \
-            (("k_decode_pair_mv<",) if fmt == Q8 else ())
+        # k_decode_pair_mv for the int8-K formats at 1, 2 or 4 query heads per kv head,
+        # else k_decode_pair) then one k_decode_merge<fmt>
+        tags = (f"k_decode_split<{fmt},", f"k_decode_pair<{fmt},", f"k_decode_pair_mv<{fmt},")
         splits = [i for i in ids if any(t in fetch[i][0] for t in tags)]
         per = []
         for i in splits:
@@ -327,7 +326,7 @@ def traffic_summary(fetch_dir, write_dir, command):
                     "bytes_per_launch": float(per[:, 2].mean()),
                     "algorithmic_bytes_per_launch": decode_bytes(fmt, CTX),
                     "ratio_to_algorithmic": float(per[:, 2].mean()) / decode_bytes(fmt, CTX)}
-    for fmt, key in ((F16, "append_f16"), (Q8, "append_int8")):
+    for fmt, key in ((F16, "append_f16"), (Q8, "append_int8"), (K8V4, "append_k8v4")):
         a = [i for i in ids if f"k_append<{fmt}>" in fetch[i][0]]
         fk = float(np.mean([fetch[i][1] for i in a]))
         wk = float(np.mean([write[i][1] for i in a]))
