@@ -150,11 +150,14 @@ size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_le
  *     levels, q = s (a + b/254 + c/254^2) with s = max|q| / 127 over the group
  *     (residual at most s / (2 * 254^2)); each level's dot product with the codes
  *     is an exact integer (matrix cores), combined with the K scales in fp32.
- *   V of Q8 with G <= 4: each softmax weight times its V scale is carried as two
- *     bf16 values, hi + lo, with |w - hi - lo| <= 2^-16 |w|; codes times hi and lo
- *     are summed in fp32 on the matrix cores.  An output element then lies within
- *     2^-16 A of the exact weighted sum, A = sum_t w_t |V_td| / sum_t w_t, plus fp32
- *     rounding.  V of Q8 with G = 8 and of K8V4: fp32 vector sums.
+ *   V with G <= 4 (Q8 and K8V4): each softmax weight times its V scale (per 64
+ *     dims for Q8, per 32 for K8V4) is carried as two bf16 values, hi + lo, with
+ *     |w - hi - lo| <= 2^-16 |w|; codes times hi and lo are summed in fp32 on the
+ *     matrix cores.  A Q8 output element then lies within 2^-16 A of the exact
+ *     weighted sum, A = sum_t w_t |V_td| / sum_t w_t, plus fp32 rounding.  K8V4 sums
+ *     the rotated values u = code * d and applies H / 128 in fp32 after the merge,
+ *     so its bound is 2^-16 times the mean over dims of A taken over |u|.
+ *   V with G = 8: fp32 vector sums.
  *   d_q   : fp32 [n_sess][n_q_heads][head_dim];  d_out : fp32 [n_sess][n_q_heads][head_dim]
  *   n_sess : 1 .. 65535.
  *   max_len : host upper bound of every d_len[b] (sizes the grid); a session over it

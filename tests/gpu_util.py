@@ -119,7 +119,9 @@ def sm_scale(hd=128):
 # group's largest query value, and the rest is fp32 rounding of products and sums
 # (together measured under 0.5 x 2^-16 A_d on every decode test).  FID_C = 2^-14
 # leaves 4x the weight-split term; a two-level query split or a single bf16 weight
-# (2^-8 A_d) lands far outside.
+# (2^-8 A_d) lands far outside.  K8V4 sums the rotated values u = code * d with the
+# same weight split and applies H / 128 after the merge, which averages the rotated
+# sums' errors over the dims: its A_d is the mean over dims of the attention over |u|.
 FID_C = 2.0 ** -14
 FID_ABS = 1e-6
 
