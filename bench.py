@@ -11,10 +11,12 @@ of it (distinct addresses, so no cache level holds more than a sliver of them).
 One step = for each format, for each of the 48 layers: kv_append of one new token
 (quantise-on-write or FP16 store) and kv_decode_attn over the cache.  The timed
 region holds exactly `--steps` steps between two device synchronisations; the
-metric is the decode's algorithmic K/V bytes per step / step time.  Each
-kv_decode_attn call is also bracketed by HIP events on the launch stream for the
-per-kernel roofline.  Side measurements (not in the step): bulk append rate, and
-the 4096-token prompt chunk at position 131072 of an int8 cache.
+metric is the decode's algorithmic K/V bytes per step / step time.  The per-call
+roofline times the 48 layers' decode calls of one format captured as a HIP graph
+(HIP events around each replay on its stream); the same calls launched eagerly with
+events around each one are reported beside it.  Side measurements (not in the
+step): bulk append rate, the smaller workloads, and the 4096-token prompt chunk at
+position 131072 of an int8 cache.
 
 Prints progress to stderr and ONE JSON line to stdout.
 """
@@ -184,6 +186,41 @@ def graph_steps(kq, torch, model, n_warm, n_steps, len0, q, xk_new, xv_new, ws):
     assert int(lens_w.item()) == len0 + n_warm + n_steps
     assert torch.isfinite(out).all().item()
     return t1 - t0
+
+
+def graph_call_times(kq, torch, model, length, q, ws, reps):
+    """Per-call duration of kv_decode_attn as a captured step runs it: for each format,
+    the 48 layers' decode calls over `length` cells captured as one HIP graph (no
+    appends), replayed `reps` times with HIP events around each replay on the graph's
+    stream.  Returns seconds per call (split and merge kernels and the gaps between
+    them, without the host's launch cost)."""
+    out = torch.empty((1, NQH, HD), device="cuda")
+    res = {}
+    for fmt, m in model.items():
+        lens_d = torch.full((1,), length, dtype=torch.int32, device="cuda")
+        stream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            with torch.cuda.graph(graph, stream=stream):
+                for li in range(LAYERS):
+                    kq.kv_decode_attn(m["shape"], m["tabs"][li], lens_d, 1, CTX, q[li],
+                                      1 / math.sqrt(HD), out, ws[fmt])
+        torch.cuda.synchronize()
+        evs = []
+        with torch.cuda.stream(stream):
+            graph.replay()   # untimed
+            for _ in range(reps):
+                e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                e[0].record(stream)
+                graph.replay()
+                e[1].record(stream)
+                evs.append(e)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all().item()
+        res[fmt] = float(np.mean([a.elapsed_time(b) * 1e-3 for a, b in evs])) / LAYERS
+        del graph
+    return res
 
 
 def prefill_side(kq, torch, seed, steps, warmup):
@@ -850,11 +887,16 @@ def main():
     eager_value = bytes_total / (t1 - t0) / 1e9
     log(f"eager steps: {eager_step_s * 1e3:.2f} ms per step, {eager_value:.0f} GB/s")
 
+    # the decode calls alone, as a captured step runs them (over the full context)
+    log("graph of the 48 decode calls per format: per-call durations")
+    g_call = graph_call_times(kq, torch, model, CTX, q, ws, reps=n_steps)
+
     roof = {}
     for fmt in (F16, Q8):
         durs = [a.elapsed_time(b) * 1e-3 for a, b in events[fmt]]
-        avg = float(np.mean(durs))
-        per_launch = float(np.mean([decode_bytes(fmt, length + s + 1) for s in range(n_steps)]))
+        avg_eager = float(np.mean(durs))
+        avg = g_call[fmt]
+        per_launch = float(decode_bytes(fmt, CTX))
         ach = per_launch / avg / 1e9
         key = "decode_f16" if fmt == F16 else "decode_int8"
         roof[fmt] = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -863,12 +905,20 @@ def main():
                      "kernel": ("k_decode_split" if fmt == F16 else "k_decode_pair_mv") +
                                " + k_decode_merge (one kv_decode_attn call)",
                      "avg_us": avg * 1e6, "algorithmic_bytes_per_launch": per_launch,
+                     "timing": "HIP events around replays of a HIP graph of the 48 layers' "
+                               "decode calls over 262144 cells (the launch form of the step), "
+                               "per call",
+                     "avg_us_eager_events": avg_eager * 1e6,
+                     "achieved_eager_events": float(np.mean(
+                         [decode_bytes(fmt, length + s + 1) for s in range(n_steps)])) /
+                         avg_eager / 1e9,
                      "tokens_per_s_48_layers": 1.0 / (avg * LAYERS)}
         if fmt == Q8:
             roof[fmt]["note"] = ("both products on the matrix cores (K logits as int8, the V "
                                  "sums as bf16 with fp32 accumulation); the kernel is bound by "
                                  "the HBM stream")
-        log(f"fmt={fmt}: {avg * 1e6:.1f} us/layer, {ach:.0f} GB/s ({ach / HBM_PEAK_GBS:.1%})")
+        log(f"fmt={fmt}: {avg * 1e6:.1f} us per call in the graph ({ach:.0f} GB/s, "
+            f"{ach / HBM_PEAK_GBS:.1%}); {avg_eager * 1e6:.1f} us by events around eager calls")
     dominant = F16 if roof[F16]["avg_us"] >= roof[Q8]["avg_us"] else Q8
     del model
     torch.cuda.empty_cache()
