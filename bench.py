@@ -439,6 +439,45 @@ def _time_loop(torch, calls, reps):
     return e0.elapsed_time(e1) * 1e-3 / (reps * len(calls))
 
 
+def _time_graph(torch, calls, reps):
+    """Mean seconds per call of the callables in calls captured once, in order, as a
+    HIP graph and replayed reps times (HIP events around each replay on the graph's
+    stream): the calls as a captured step runs them, without the host's launches."""
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            for f in calls:
+                f()
+    torch.cuda.synchronize()
+    evs = []
+    with torch.cuda.stream(stream):
+        graph.replay()   # untimed
+        for _ in range(reps):
+            e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            e[0].record(stream)
+            graph.replay()
+            e[1].record(stream)
+            evs.append(e)
+    torch.cuda.synchronize()
+    del graph
+    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3 / len(calls)
+
+
+def _stream_us(kq, torch, nbytes, reps=10):
+    """Microseconds per kv_probe_stream_read over nbytes, four buffers in turn."""
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bufs = [torch.ones(nbytes, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    calls = [lambda b=b: kq.kv_probe_stream_read(b, sink) for b in bufs]
+    for f in calls:
+        f()
+    t = _time_loop(torch, calls, reps)
+    del bufs
+    torch.cuda.empty_cache()
+    return t * 1e6
+
+
 def side_configs(kq, torch, steps=10, warmup=3):
     """The smaller workloads: the 64-session int8 batch (session lengths uniform on
     [1024, 65536], one session table; a step is one batched 1-token append and one
@@ -485,6 +524,10 @@ def side_configs(kq, torch, steps=10, warmup=3):
         lens_w += 1
         lens_d += 1
     assert torch.isfinite(o).all().item()
+    # the batched decode alone as a captured step runs it (lengths as they ended)
+    t_g = _time_graph(torch, [lambda: kq.kv_decode_attn(sh, tab, lens_d, n_sess, max_len, q, sm,
+                                                        o, ws)], steps)
+    read_g = decode_bytes(Q8, int(lens_d.sum().item()))
     out["batched64_int8"] = {
         "workload": "64 int8 sessions, lengths uniform on [1024, 65536] (sum "
                     f"{sum(lens)}), one session table; a step = batched 1-token append + "
@@ -492,6 +535,8 @@ def side_configs(kq, torch, steps=10, warmup=3):
         "decode_us": float(np.mean(t_dec)) * 1e6,
         "decode_GB_s": read / sum(t_dec) / 1e9,
         "decode_frac_hbm": read / sum(t_dec) / 1e9 / HBM_PEAK_GBS,
+        "decode_us_graph": t_g * 1e6,
+        "decode_frac_hbm_graph": read_g / t_g / 1e9 / HBM_PEAK_GBS,
         "append_us": float(np.mean(t_app)) * 1e6,
         "append_cells_per_s": n_sess / float(np.mean(t_app))}
     log(f"batched64 int8: decode {out['batched64_int8']['decode_us']:.1f} us = "
@@ -532,12 +577,15 @@ def side_configs(kq, torch, steps=10, warmup=3):
         # events around each call, which adds each launch's gap
         t = _time_loop(torch, calls, steps)
         t_each = float(np.mean(_time_calls(torch, calls, steps)))
+        t_graph = _time_graph(torch, calls, steps)
         nb = decode_bytes(fmt, ctx)
         name = {F16: "F16", Q8: "int8", K8V4: "K8V4 (int8 K, rotated 4-bit V)"}[fmt]
         out[key] = {"workload": f"{name} cache, {ctx} cells, 4 copies in turn, back to back",
                     "decode_us": t * 1e6, "decode_bytes": nb,
                     "decode_GB_s": nb / t / 1e9, "decode_frac_hbm": nb / t / 1e9 / HBM_PEAK_GBS,
                     "decode_us_events_each": t_each * 1e6,
+                    "decode_us_graph": t_graph * 1e6,
+                    "decode_frac_hbm_graph": nb / t_graph / 1e9 / HBM_PEAK_GBS,
                     "bulk_append_cells_per_s": ctx / app}
         # the same copy every call: a layer that fits the 256 MB last-level cache stays
         # in it (what one layer decoded in a loop would see); rotated above is the rate
@@ -555,12 +603,15 @@ def side_configs(kq, torch, steps=10, warmup=3):
         app1 = [lambda t=t: kq.kv_append(sh, t, ld1, 1, 1, x1k, x1v) for t in tabs]
         _time_calls(torch, app1, warmup)
         out[key]["step_append_us"] = _time_loop(torch, app1, steps) * 1e6
-        log(f"{key}: decode {t * 1e6:.1f} us = {nb / t / 1e9:.0f} GB/s (hot {th * 1e6:.1f} us); "
-            f"one-token append {out[key]['step_append_us']:.1f} us")
+        log(f"{key}: decode {t * 1e6:.1f} us = {nb / t / 1e9:.0f} GB/s (graph {t_graph * 1e6:.1f} us, "
+            f"hot {th * 1e6:.1f} us); one-token append {out[key]['step_append_us']:.1f} us")
         if fmt == Q8:
             out["row_moves_int8"] = row_moves(kq, torch, sh, copies[0], copies[1], ctx)
         del copies, tabs, ws
         torch.cuda.empty_cache()
+        # a plain streaming read of the same bytes (four buffers in turn, back to back)
+        out[key]["stream_ceiling_us"] = _stream_us(kq, torch, nb, steps)
+        out[key]["vs_stream_ceiling"] = out[key]["stream_ceiling_us"] / (t * 1e6)
     out.update(paged_and_streamed(kq, torch, steps, warmup))
     return out
 

@@ -199,7 +199,7 @@ size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_le
   if (check_shape(h_shape) || n_sess < 1 || n_sess > KV_DEC_MAX_SESS || max_len < 0) return 0;
   const DecodePlan p =
       decode_plan(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, n_sess, max_len);
-  return p.ws_o_bytes + p.ws_lse_bytes;
+  return p.total();
 }
 
 int kv_decode_attn(const kv_shape* h_shape, const kv_session* d_tab, const int32_t* d_len,
@@ -216,7 +216,7 @@ int kv_decode_attn(const kv_shape* h_shape, const kv_session* d_tab, const int32
   if (d_ws == nullptr) return KV_ERR_WORKSPACE;
   const DecodePlan p =
       decode_plan(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, n_sess, max_len);
-  if (ws_bytes < p.ws_o_bytes + p.ws_lse_bytes) return KV_ERR_WORKSPACE;
+  if (ws_bytes < p.total()) return KV_ERR_WORKSPACE;
   return hip_status(launch_decode(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, d_tab,
                                   d_len, n_sess, max_len, d_q, sm_scale, d_out, d_ws, p, d_status,
                                   static_cast<hipStream_t>(stream)));
@@ -235,7 +235,7 @@ int kv_decode_attn_static(const kv_shape* h_shape, const kv_session* d_tab, cons
     return KV_ERR_ALIGN;
   const DecodePlan p =
       decode_plan(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, n_sess, max_len);
-  if (p.ws_o_bytes + p.ws_lse_bytes > (size_t)KV_DECODE_STATIC_WS_BYTES) return KV_ERR_WORKSPACE;
+  if (p.total() > (size_t)KV_DECODE_STATIC_WS_BYTES) return KV_ERR_WORKSPACE;
   void* ws = static_workspace();
   if (ws == nullptr) return KV_ERR_HIP;
   return hip_status(launch_decode(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, d_tab,
@@ -263,7 +263,7 @@ int kv_decode_attn_paged(const kv_shape* h_shape, const kv_session* d_tab,
   if (d_ws == nullptr) return KV_ERR_WORKSPACE;
   const DecodePlan p =
       decode_plan(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, n_sess, max_len);
-  if (ws_bytes < p.ws_o_bytes + p.ws_lse_bytes) return KV_ERR_WORKSPACE;
+  if (ws_bytes < p.total()) return KV_ERR_WORKSPACE;
   return hip_status(launch_decode(h_shape->fmt, h_shape->n_kv_heads, h_shape->n_q_heads, d_tab,
                                   d_len, n_sess, max_len, d_q, sm_scale, d_out, d_ws, p, d_status,
                                   static_cast<hipStream_t>(stream), d_pages, page_stride));

@@ -502,16 +502,20 @@ __global__ __launch_bounds__(DEC_THREADS)
 __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int kvh,
     const float* __restrict__ q, float qscale, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, int S, const int32_t* __restrict__ pages, int page_stride) {
+    float* __restrict__ ws_lse, int S, const int32_t* __restrict__ pages, int page_stride,
+    const int32_t* __restrict__ sid) {
   constexpr int CH0 = ch0<FMT, G>(), CH1 = ch1<FMT, G>();
   static_assert(FMT == KV_FMT_F16, "the int8-K formats take the pair kernels");
   static_assert(CH0 % (2 * U) == 0 && CH1 % (2 * U) == 0, "a chunk holds whole pairs of load batches");
   static_assert(CH0 >= KVQ8_DEC_MIN_STEPS && (!GROUPED || CH1 >= KVQ8_DEC_MIN_STEPS),
                 "a short session's waves (at most KVQ8_DEC_MIN_STEPS steps) fit the logits budget");
-  const int s_idx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int s_idx = blockIdx.x, h = blockIdx.y, rk = blockIdx.z;
   const int nqh = kvh * G;
-  const kv_session ss = tab[b];
-  const int len = lens[b];
+  // tab, lens: the call's sessions, or ranked longest first with sid the session of
+  // each rank (batches)
+  const kv_session ss = tab[rk];
+  const int len = lens[rk];
+  const int b = sid != nullptr ? sid[rk] : rk;
   if (session_bad(ss, FMT) || len < 0 || len > ss.cap || len > max_len) return;  // merge flags
   const int J = (len + 7) >> 3;                  // 8-token steps of this session
   const int Jf = lead_steps<FMT>(J);             // steps of group 0 (>= those of group 1)
@@ -771,16 +775,20 @@ template <int FMT, int G, int U, int PG>
 __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >= 8 ? 2 : KVQ8_DEC_PAIR_WPE))) void k_decode_pair(
     const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int max_len, int kvh,
     const float* __restrict__ q, float qscale, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, int S, const int32_t* __restrict__ pages, int page_stride) {
+    float* __restrict__ ws_lse, int S, const int32_t* __restrict__ pages, int page_stride,
+    const int32_t* __restrict__ sid) {
   static_assert(FMT != KV_FMT_F16, "the pair kernel reads int8 K codes");
   constexpr int UK = k_batch_rows<G>();
   static_assert(PAIR_CH % (2 * UK) == 0 && PAIR_CH % (2 * U) == 0,
                 "a chunk holds whole pairs of K and of V batches");
   constexpr int NHB = G > 4 ? 2 : 1;
-  const int s_idx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int s_idx = blockIdx.x, h = blockIdx.y, rk = blockIdx.z;
   const int nqh = kvh * G;
-  const kv_session ss = tab[b];
-  const int len = lens[b];
+  // tab, lens: the call's sessions, or ranked longest first with sid the session of
+  // each rank (batches)
+  const kv_session ss = tab[rk];
+  const int len = lens[rk];
+  const int b = sid != nullptr ? sid[rk] : rk;
   // workgroup-uniform exits only (the loop below has barriers)
   if (session_bad(ss, FMT) || len < 0 || len > ss.cap || len > max_len) return;  // merge flags
   const int J = (len + 7) >> 3;
@@ -1190,7 +1198,8 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(KVQ
 void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restrict__ lens,
                       int max_len, int kvh, const float* __restrict__ q, float qscale,
                       float* __restrict__ ws_o, float* __restrict__ ws_lse, int S,
-                      const int32_t* __restrict__ pages, int page_stride) {
+                      const int32_t* __restrict__ pages, int page_stride,
+                      const int32_t* __restrict__ sid) {
   static_assert(FMT == KV_FMT_Q8 || FMT == KV_FMT_K8V4, "int8 K codes");
   static_assert(G <= 4, "one block of 4 heads");
   constexpr bool K4 = FMT == KV_FMT_K8V4;
@@ -1202,10 +1211,13 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
   constexpr int NCB = CHK / MV_BLK;              // blocks per chunk
   constexpr int VROW = K4 ? HD / 2 : HD;         // bytes per V row
   constexpr int VSC = K4 ? NQ4 : NGRP;           // V scales per row
-  const int s_idx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int s_idx = blockIdx.x, h = blockIdx.y, rk = blockIdx.z;
   const int nqh = kvh * G;
-  const kv_session ss = tab[b];
-  const int len = lens[b];
+  // tab, lens: the call's sessions, or ranked longest first with sid the session of
+  // each rank (batches)
+  const kv_session ss = tab[rk];
+  const int len = lens[rk];
+  const int b = sid != nullptr ? sid[rk] : rk;
   // workgroup-uniform exits only (the loops below have barriers)
   if (session_bad(ss, FMT) || len < 0 || len > ss.cap || len > max_len) return;  // merge flags
   const int J = (len + 7) >> 3;
@@ -1588,6 +1600,53 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
   }
 }
 
+// A batch's sessions ranked longest first, so that the split workgroups of the long
+// sessions, which hold the most steps each, are dispatched first and the short ones
+// fill in behind them (the grid's last dimension is the rank).  One workgroup: a
+// counting sort on ORD_BUCKETS length classes (len * (ORD_BUCKETS - 1) / max_len,
+// a length outside 0 .. max_len in the last class); within a class the order is
+// whatever the atomics give, which changes no output: a session's arithmetic
+// depends on its own length only.  Writes the ranked session table, lengths and
+// session index of each rank.
+constexpr int ORD_THREADS = 1024;
+constexpr int ORD_BUCKETS = ORD_THREADS;
+__global__ __launch_bounds__(ORD_THREADS) void k_session_order(
+    const kv_session* __restrict__ tab, const int32_t* __restrict__ lens, int n_sess,
+    int max_len, kv_session* __restrict__ stab, int32_t* __restrict__ slen,
+    int32_t* __restrict__ sid) {
+  __shared__ int cnt[2][ORD_BUCKETS];
+  const int t = threadIdx.x;
+  const long long span = max(max_len, 1);
+  auto cls = [&](int len) {   // 0: longest
+    const int k = len <= 0 || len > max_len ? 0 : (int)((long long)len * (ORD_BUCKETS - 1) / span);
+    return ORD_BUCKETS - 1 - k;
+  };
+  cnt[0][t] = 0;
+  __syncthreads();
+  for (int b = t; b < n_sess; b += ORD_THREADS) atomicAdd(&cnt[0][cls(lens[b])], 1);
+  __syncthreads();
+  // inclusive scan of the class counts (Hillis-Steele over the two buffers)
+  int src = 0;
+  for (int d = 1; d < ORD_BUCKETS; d *= 2) {
+    const int v = cnt[src][t] + (t >= d ? cnt[src][t - d] : 0);
+    cnt[src ^ 1][t] = v;
+    src ^= 1;
+    __syncthreads();
+  }
+  // the first rank of class t
+  const int first = t > 0 ? cnt[src][t - 1] : 0;
+  __syncthreads();
+  cnt[src][t] = first;
+  __syncthreads();
+  for (int b = t; b < n_sess; b += ORD_THREADS) {
+    const int len = lens[b];
+    const int r = atomicAdd(&cnt[src][cls(len)], 1);
+    stab[r] = tab[b];
+    slen[r] = len;
+    sid[r] = b;
+  }
+}
+
 // One workgroup of 256 threads per (session, query head).  Thread t holds dims
 // 4 (t % 32) .. + 3 of the splits j = t / 32 + 8 k (k = 0 .. 7) of a chunk of 64
 // splits; every wave also holds the chunk's 64 lse values, one per lane, and forms
@@ -1783,10 +1842,10 @@ int resident(int fmt, int G) {
 }
 
 template <int FMT, int G, bool PG>
-hipError_t launch_split(const kv_session* tab, const int32_t* lens, int n_sess, int max_len,
-                        int kvh, const float* q, float sm_scale, float* ws_o, float* ws_lse,
-                        const DecodePlan& plan, const int32_t* pages, int page_stride,
-                        hipStream_t st) {
+hipError_t launch_split(const kv_session* tab, const int32_t* lens, const int32_t* sid,
+                        int n_sess, int max_len, int kvh, const float* q, float sm_scale,
+                        float* ws_o, float* ws_lse, const DecodePlan& plan, const int32_t* pages,
+                        int page_stride, hipStream_t st) {
   constexpr int U = batch_rows<FMT, G>();
   static_assert(U == 1 || U == 2 || U == 4 || U == 8, "U must divide the group budgets / 2");
   dim3 grid(plan.S, kvh, n_sess), block(DEC_THREADS);
@@ -1797,7 +1856,7 @@ hipError_t launch_split(const kv_session* tab, const int32_t* lens, int n_sess, 
     const bool one = n_sess == 1;
 #define KVQ8_MV_LAUNCH(P, SPV)                                                                 \
   hipLaunchKernelGGL((k_decode_pair_mv<FMT, G, P, SPV>), grid, block, (mv_lds_bytes<FMT, G>()), st, tab, lens, \
-                     max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages, page_stride)
+                     max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages, page_stride, sid)
     if constexpr (!PG) {
       if (one) KVQ8_MV_LAUNCH(0, MV_SP);
       else KVQ8_MV_LAUNCH(0, 1);
@@ -1813,7 +1872,7 @@ hipError_t launch_split(const kv_session* tab, const int32_t* lens, int n_sess, 
     if constexpr (!PG) {
       hipLaunchKernelGGL((k_decode_pair<FMT, G, U, 0>), grid, block, pair_lds_bytes<G>(), st, tab,
                          lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S, pages,
-                         page_stride);
+                         page_stride, sid);
     } else {
       // the page map in 2 registers when no pair has more than 128 steps, else in 4
       // with V batches of at most 2 steps, so the V wave stays within its registers.
@@ -1829,16 +1888,16 @@ hipError_t launch_split(const kv_session* tab, const int32_t* lens, int n_sess, 
       if (per_pair <= 128)
         hipLaunchKernelGGL((k_decode_pair<FMT, G, U, 2>), grid, block, pair_lds_bytes<G>(), st,
                            tab, lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S,
-                           pages, page_stride);
+                           pages, page_stride, sid);
       else
         hipLaunchKernelGGL((k_decode_pair<FMT, G, U4, 4>), grid, block, pair_lds_bytes<G>(), st,
                            tab, lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S,
-                           pages, page_stride);
+                           pages, page_stride, sid);
     }
   } else {
     hipLaunchKernelGGL((k_decode_split<FMT, G, U, PG ? 4 : 0>), grid, block, split_lds_bytes<G>(),
                        st, tab, lens, max_len, kvh, q, sm_scale * LOG2E, ws_o, ws_lse, plan.S,
-                       pages, page_stride);
+                       pages, page_stride, sid);
   }
   return hipGetLastError();
 }
@@ -1846,13 +1905,27 @@ hipError_t launch_split(const kv_session* tab, const int32_t* lens, int n_sess, 
 template <int FMT, int G>
 hipError_t launch_g(const kv_session* tab, const int32_t* lens, int n_sess, int max_len, int kvh,
                     const float* q, float sm_scale, float* out, float* ws_o, float* ws_lse,
-                    const DecodePlan& plan, int32_t* status, const int32_t* pages,
+                    void* ws_ord, const DecodePlan& plan, int32_t* status, const int32_t* pages,
                     int page_stride, hipStream_t st) {
+  // a batch runs its sessions longest first: the split kernels read the ranked copy
+  const kv_session* stab = tab;
+  const int32_t* slen = lens;
+  const int32_t* sid = nullptr;
+  if (plan.ws_ord_bytes != 0) {
+    kv_session* rt = static_cast<kv_session*>(ws_ord);
+    int32_t* rl = reinterpret_cast<int32_t*>(rt + n_sess);
+    int32_t* ri = rl + n_sess;
+    hipLaunchKernelGGL(k_session_order, dim3(1), dim3(ORD_THREADS), 0, st, tab, lens, n_sess,
+                       max_len, rt, rl, ri);
+    stab = rt;
+    slen = rl;
+    sid = ri;
+  }
   hipError_t e = pages != nullptr
-                     ? launch_split<FMT, G, true>(tab, lens, n_sess, max_len, kvh, q, sm_scale, ws_o,
-                                                  ws_lse, plan, pages, page_stride, st)
-                     : launch_split<FMT, G, false>(tab, lens, n_sess, max_len, kvh, q, sm_scale,
-                                                   ws_o, ws_lse, plan, nullptr, 0, st);
+                     ? launch_split<FMT, G, true>(stab, slen, sid, n_sess, max_len, kvh, q, sm_scale,
+                                                  ws_o, ws_lse, plan, pages, page_stride, st)
+                     : launch_split<FMT, G, false>(stab, slen, sid, n_sess, max_len, kvh, q,
+                                                   sm_scale, ws_o, ws_lse, plan, nullptr, 0, st);
   if (e != hipSuccess) return e;
   const int n_rows = n_sess * kvh * G;
   hipLaunchKernelGGL((k_decode_merge<FMT>), dim3(n_rows), dim3(MERGE_THREADS), 0, st, tab, lens,
@@ -1907,6 +1980,9 @@ DecodePlan decode_plan(int fmt, int kvh, int nqh, int n_sess, int max_len) {
   const size_t rows = (size_t)n_sess * nqh * p.S;
   p.ws_o_bytes = (rows * HD * sizeof(float) + 255) & ~(size_t)255;
   p.ws_lse_bytes = (rows * sizeof(float) + 255) & ~(size_t)255;
+  p.ws_ord_bytes = n_sess > 1
+                       ? ((size_t)n_sess * (sizeof(kv_session) + 2 * sizeof(int32_t)) + 255) & ~(size_t)255
+                       : 0;
   return p;
 }
 
@@ -1935,11 +2011,12 @@ hipError_t launch_decode(int fmt, int kvh, int nqh, const kv_session* d_tab,
                          int page_stride) {
   float* ws_o = static_cast<float*>(d_ws);
   float* ws_lse = reinterpret_cast<float*>(static_cast<char*>(d_ws) + plan.ws_o_bytes);
+  void* ws_ord = static_cast<char*>(d_ws) + plan.ws_o_bytes + plan.ws_lse_bytes;
   const int G = nqh / kvh;
 #define KVQ8_DEC(F, GG)                                                                          \
   if (fmt == F && G == GG)                                                                       \
     return launch_g<F, GG>(d_tab, d_len, n_sess, max_len, kvh, d_q, sm_scale, d_out, ws_o, ws_lse, \
-                           plan, d_status, d_pages, page_stride, st);
+                           ws_ord, plan, d_status, d_pages, page_stride, st);
   KVQ8_DEC(KV_FMT_K8V4, 1)
   KVQ8_DEC(KV_FMT_K8V4, 2)
   KVQ8_DEC(KV_FMT_K8V4, 4)

@@ -166,6 +166,10 @@ int copy_rows(const kv_shape* h_shape, const kv_session* h_src, int src_row0,
 struct DecodePlan {
   int S;      // splits (workgroups) per (session, kv head): grid x
   size_t ws_o_bytes, ws_lse_bytes;
+  // a batch's sessions ranked longest first (0 for one session): the session table,
+  // lengths and session indices in that order
+  size_t ws_ord_bytes;
+  size_t total() const { return ws_o_bytes + ws_lse_bytes + ws_ord_bytes; }
 };
 // depends on the arguments and on how many split workgroups the current device
 // holds at once (queried once per device)

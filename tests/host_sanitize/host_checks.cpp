@@ -36,6 +36,7 @@ DecodePlan decode_plan(int, int, int nqh, int n_sess, int) {
   p.S = 4;
   p.ws_o_bytes = ((size_t)n_sess * nqh * p.S * HD * 4 + 255) & ~(size_t)255;
   p.ws_lse_bytes = ((size_t)n_sess * nqh * p.S * 4 + 255) & ~(size_t)255;
+  p.ws_ord_bytes = n_sess > 1 ? ((size_t)n_sess * 48 + 255) & ~(size_t)255 : 0;
   return p;
 }
 hipError_t launch_decode(int, int, int, const kv_session*, const int32_t*, int, int, const float*,
