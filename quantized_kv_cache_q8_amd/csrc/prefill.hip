@@ -18,8 +18,9 @@
 //   accumulators (as hi + lo fp16 parts, two products), using one consistent
 //   assignment of keys to MFMA k-slots for both operands, so no data moves
 //   between lanes.
-// K is staged row-major with a 288-byte row pitch, V transposed with a 136-byte
-// pitch, both free of LDS bank conflicts on the fragment reads.  Tiles alternate
+// K is staged row-major with a 288-byte row pitch, V transposed with a 160-byte
+// pitch and its key columns permuted so that the 8 keys a lane needs for one V
+// fragment are adjacent: every fragment is one 16-byte LDS read.  Tiles alternate
 // between two LDS buffers: the next tile's global loads are in flight while the
 // current tile computes, and one barrier per tile suffices.
 // Workgroups are numbered so that consecutive ones take different kv heads: the
@@ -37,7 +38,7 @@ constexpr int PF_ROWS = 256;    // (query, head) rows per workgroup
 constexpr int PF_THREADS = 512; // 8 waves x 32 rows
 constexpr int BK = 64;     // keys per tile
 constexpr int KSTR = 144;  // K row pitch in halves (288 B)
-constexpr int VSTR = 68;   // V^T row pitch in halves (136 B)
+constexpr int VSTR = 80;   // V^T row pitch in halves (160 B)
 constexpr float LOG2E_F = 1.4426950408889634f;
 constexpr float PF_PRE = 15.0f;  // log2 scale of p (p <= 2^15)
 
@@ -110,7 +111,8 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
 
   // ---- staging: K tile row-major, V tile transposed --------------------------
   // K: 1024 chunks of 8 halves, 2 per thread.  V: thread holds keys 2kq, 2kq + 1 of
-  // dims 8dq .. 8dq + 7.
+  // dims 8dq .. 8dq + 7.  V^T column of key k (within its half of 32 keys, kk):
+  // 8 (kk % 16 / 4) + 4 (kk / 16) + kk % 4, the order of the P^T k-slots below.
   uint4 kreg[2], vreg[2];
   const int kq = tid & 31, dq = tid >> 5;
   auto gload = [&](int tile) {
@@ -136,10 +138,12 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
     }
     const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
     const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
+    const int kk = 2 * kq;
+    const int col = (kk & 32) + 8 * ((kk & 15) >> 2) + 4 * ((kk >> 4) & 1) + (kk & 3);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {  // dims 2e and 2e+1 of the octet, keys 2kq and 2kq + 1
-      *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * dq + 2 * e) * VSTR + 2 * kq]) = pack_lo(w0[e], w1[e]);
-      *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * dq + 2 * e + 1) * VSTR + 2 * kq]) = pack_hi(w0[e], w1[e]);
+      *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * dq + 2 * e) * VSTR + col]) = pack_lo(w0[e], w1[e]);
+      *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * dq + 2 * e + 1) * VSTR + col]) = pack_hi(w0[e], w1[e]);
     }
   };
 
@@ -261,10 +265,9 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
     // held in place by the scheduling barrier as above
     auto vfrag = [&](int i) __attribute__((always_inline)) {
       const int ks2 = i >> 3, db = i & 7;
-      const _Float16* vp = &VtC[(16 * db + l16) * VSTR + 32 * ks2 + 4 * g4];
-      const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-      const uint2 hi = *reinterpret_cast<const uint2*>(vp + 16);
-      return __builtin_bit_cast(half8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+      // k-slots (g4, 0 .. 7) of k-step ks2: keys 4 g4 .. + 3 and 16 + 4 g4 .. + 3 of the
+      // half, adjacent in the permuted columns
+      return *reinterpret_cast<const half8*>(&VtC[(16 * db + l16) * VSTR + 32 * ks2 + 8 * g4]);
     };
     half8 vf[3];
 #pragma unroll
