@@ -1185,13 +1185,25 @@ __device__ __forceinline__ bf16x8 codes_bf16(i32x2 c) {
   }
   return __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
 }
-// 8 nibbles (a 32-bit word: value j in bits 4j .. 4j + 3, stored as code + 8) as 8
-// signed bytes code = n - 8 in value order (two words).  Per byte, n + 0x78 <= 0x87
-// carries into no other byte, and flipping bit 7 of it gives n - 8 in two's complement.
-__device__ __forceinline__ void nibbles_to_codes(uint32_t x, uint32_t& o0, uint32_t& o1) {
-  const uint32_t lo = nibble_bytes(x), hi = nibble_bytes(x >> 4);   // values 0,2,4,6 / 1,3,5,7
-  o0 = (__builtin_amdgcn_perm(hi, lo, 0x05010400u) + 0x78787878u) ^ 0x80808080u;
-  o1 = (__builtin_amdgcn_perm(hi, lo, 0x07030602u) + 0x78787878u) ^ 0x80808080u;
+// K8V4 in the matrix-core V pass: 8 nibbles n (one 32-bit word, value j in bits
+// 4j .. 4j + 3) as the bytes 0x80 | n << 3 in value order (two words), the low byte of
+// the bf16 value 16 + n (0x4180 + 8 n): the bf16 operand is then one byte permute per
+// two values, and the pass sums w (16 + n) = w (24 + code), from which the weights'
+// own sum times 24 is taken out.
+__device__ __forceinline__ void nibbles_to_biased(uint32_t x, uint32_t& o0, uint32_t& o1) {
+  const uint32_t lo = ((x << 3) & 0x78787878u) | 0x80808080u;   // values 0, 2, 4, 6
+  const uint32_t hi = ((x >> 1) & 0x78787878u) | 0x80808080u;   // values 1, 3, 5, 7
+  o0 = __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+  o1 = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+}
+// 8 biased bytes b (the bytes of c, in order) as the bf16 values 0x41 << 8 | b
+__device__ __forceinline__ bf16x8 biased_bf16(i32x2 c) {
+  uint32_t o[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d)
+    o[d] = __builtin_amdgcn_perm(0x41414141u, (uint32_t)(d < 2 ? c.x : c.y),
+                                 (d & 1) ? 0x04030402u : 0x04010400u);
+  return __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
 }
 template <int FMT, int G, int PG, int SP>
 __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_PAIR_WPE)))
@@ -1488,6 +1500,10 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
     f32x4 acc[8];
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) acc[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // K8V4: 24 times the sum of each table row's weights (rows as in acc)
+    f32x4 wsum[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) wsum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     // a lane's 16 dims of one row of a step: Q8 the 16 codes, K8V4 8 bytes of nibbles
     using VW = std::conditional_t<K4, u32x2, u32x4>;
     auto vload = [&](VW (&vw)[MV_BLK], int blk) __attribute__((always_inline)) {
@@ -1522,6 +1538,15 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
           acc[jd][2] *= fc;
           acc[jd][3] *= fc;
         }
+        if constexpr (K4) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            wsum[t][0] *= fa;
+            wsum[t][1] *= fa;
+            wsum[t][2] *= fc;
+            wsum[t][3] *= fc;
+          }
+        }
       }
       // the block's rows, token u * 8 + r, as signed codes in dim order
 #pragma unroll
@@ -1529,8 +1554,8 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         u32x4 cw;
         if constexpr (K4) {
           uint32_t o[4];
-          nibbles_to_codes(vw[u][0], o[0], o[1]);
-          nibbles_to_codes(vw[u][1], o[2], o[3]);
+          nibbles_to_biased(vw[u][0], o[0], o[1]);
+          nibbles_to_biased(vw[u][1], o[2], o[3]);
           cw = u32x4{o[0], o[1], o[2], o[3]};
         } else {
           cw = vw[u];
@@ -1548,10 +1573,19 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
           aw[t] = *reinterpret_cast<const bf16x8*>(atb + t * 64 * MV_AROW + (g8 * 16 + (iv ^ g8)) * 16);
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) {
-          // B: the codes of tokens 8 g8 + 0 .. 7, dim 16 jd + iv, as bf16 (exact)
+          // B: the codes of tokens 8 g8 + 0 .. 7, dim 16 jd + iv, as bf16 (exact; K8V4:
+          // 16 + n)
           const i32x2 cb = lds_tr8(tile + (8 * g8 + (iv >> 1)) * MV_PITCH + 16 * jd + 8 * (iv & 1));
-          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[K4 ? jd >> 2 : 0], codes_bf16(cb),
-                                                            acc[jd], 0, 0, 0);
+          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              aw[K4 ? jd >> 2 : 0], K4 ? biased_bf16(cb) : codes_bf16(cb), acc[jd], 0, 0, 0);
+        }
+        if constexpr (K4) {
+          // 24 per weight: B = 24.0 in every slot
+          const bf16x8 b24 = __builtin_bit_cast(bf16x8, u32x4{0x41C041C0u, 0x41C041C0u,
+                                                              0x41C041C0u, 0x41C041C0u});
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            wsum[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[t], b24, wsum[t], 0, 0, 0);
         }
       }
       wave_lds_fence();
@@ -1572,9 +1606,11 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
       // the tile's dims belong to group jd / 4 (Q8) or jd / 2 (K8V4); its rows are
       // 0 .. 7 or 8 .. 15 of the table
       const int half = K4 ? (jd >> 1) & 1 : jd >> 2;
+      f32x4 a = acc[jd];
+      if constexpr (K4) a -= wsum[jd >> 2];   // w (24 + code) - 24 w
       if ((qv >> 1) == half) {
-        if (ha < G) o_l[(pr * G + ha) * HD + jd * 16 + iv] = acc[jd][0] + acc[jd][1];
-        if (ha + 1 < G) o_l[(pr * G + ha + 1) * HD + jd * 16 + iv] = acc[jd][2] + acc[jd][3];
+        if (ha < G) o_l[(pr * G + ha) * HD + jd * 16 + iv] = a[0] + a[1];
+        if (ha + 1 < G) o_l[(pr * G + ha + 1) * HD + jd * 16 + iv] = a[2] + a[3];
       }
     }
   }
