@@ -132,7 +132,9 @@ int kv_append_paged(const kv_shape* h_shape, const kv_session* d_tab, const int3
                     int page_stride, const int32_t* d_len, int n_sess, int n_tok,
                     const float* d_k_new, const float* d_v_new, int32_t* d_status, void* stream);
 
-/* Workspace for kv_decode_attn: split-K partials.  Depends on its arguments and on
+/* Workspace for kv_decode_attn: split-K partials and, for more than one session, the
+ * session table, lengths and indices ranked longest first (a batch's long sessions
+ * are started first; the outputs do not depend on the order).  Depends on its arguments and on
  * the current HIP device (the split count follows that device's occupancy); query
  * it with the device current that kv_decode_attn will run on.  0 on invalid
  * arguments (n_sess outside 1 .. 65535). */
