@@ -257,9 +257,10 @@ __device__ __forceinline__ int step_g(int gw, int k, int W) {
   else return SP * (gw + (k / SP) * W) + (k % SP);
 }
 #ifndef KVQ8_DEC_MV_SP
-#define KVQ8_DEC_MV_SP 4
+#define KVQ8_DEC_MV_SP 8
 #endif
-// steps per unit dealt to a wave of k_decode_pair_mv for one session (a batch of
+// steps per unit dealt to a wave of k_decode_pair_mv for one session: 8 steps, 64
+// tokens, one page of a paged session and 8 KB of int8 codes per array (a batch of
 // ragged sessions takes single steps: its short sessions split more evenly)
 constexpr int MV_SP = KVQ8_DEC_MV_SP;
 // Paged sessions: the rows of a step (8 consecutive tokens, 8-aligned) lie in one
