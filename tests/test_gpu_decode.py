@@ -301,3 +301,55 @@ def test_batch_composition_bitwise(fmt):
         check_close(single, want, f"single session {i}")
         check_fidelity(base[i], want, absv, f"batched session {i}")
         check_fidelity(single, want, absv, f"single session {i}")
+
+
+@pytest.mark.parametrize("fmt", [F16, Q8])
+def test_many_sessions_ranked(fmt):
+    """1500 sessions in one call, more than the 1024 threads of the workgroup that ranks
+    a batch by length (its loops take two passes), with many equal lengths: views into
+    one pool of 128-cell slots, lengths 1 .. 128.  Each session's output is bitwise the
+    same with the table in reverse order, and sampled sessions match the oracle."""
+    kvh, nqh, n, slot = 1, 4, 1500, 128
+    r = np.random.default_rng(123)
+    lens = r.integers(1, slot + 1, size=n)
+    lens[:4] = [1, slot, slot, 1]
+    say(f"many sessions fmt={fmt}: fill {n * slot} cells")
+    pool, ref = filled(fmt, kvh, n * slot, n * slot, 4242, outliers=True)
+    row_bytes = 2 * 128 if fmt == F16 else 128
+    sc_bytes = 0 if fmt == F16 else 2 * (128 // 64)
+
+    def view(b):
+        o = int(b) * slot
+        k, v = pool.k.data_ptr() + o * row_bytes, pool.v.data_ptr() + o * row_bytes
+        ks = None if fmt == F16 else pool.k_scale.data_ptr() + o * sc_bytes
+        vs = None if fmt == F16 else pool.v_scale.data_ptr() + o * sc_bytes
+        return kq.kv_session(k, v, ks, vs, slot, 0)
+
+    sh = shape(fmt, kvh, nqh)
+    q = kvsynth.queries(124, 0, n, nqh, 128)
+
+    def run(order):
+        tab = kq.session_table([view(b) for b in order])
+        lt = to_dev(lens[order].astype(np.int32))
+        ws = kq.kv_decode_workspace(sh, n, slot, DEV)
+        out = torch.full((n, nqh, 128), float("nan"), device=DEV)
+        kq.kv_decode_attn(sh, tab, lt, n, slot, to_dev(q[order].astype(np.float32)), sm_scale(),
+                          out, ws)
+        torch.cuda.synchronize()
+        res = np.empty((n, nqh, 128))
+        res[order] = out.cpu().numpy()
+        return res
+
+    say("many sessions: decode, then the table reversed")
+    got = run(np.arange(n))
+    rev = run(np.arange(n)[::-1].copy())
+    assert np.array_equal(got, rev), "a session's output depends on its place in the table"
+    for b in sorted({0, 1, 2, 3, 700, 1024, 1499} | set(r.integers(0, n, size=5).tolist())):
+        sub = oracle.Cache(fmt, kvh, slot, 128)
+        sub.k, sub.v = ref.k[:, b * slot:(b + 1) * slot], ref.v[:, b * slot:(b + 1) * slot]
+        if fmt != F16:
+            sub.k_scale = ref.k_scale[:, b * slot:(b + 1) * slot]
+            sub.v_scale = ref.v_scale[:, b * slot:(b + 1) * slot]
+        want, absv = oracle_decode(sub, q[b], int(lens[b]), sm_scale(), with_abs=True)
+        check_close(got[b], want, f"session {b} (len {lens[b]})")
+        check_fidelity(got[b], want, absv, f"session {b}")
