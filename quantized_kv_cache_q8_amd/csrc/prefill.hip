@@ -18,11 +18,15 @@
 //   accumulators (as hi + lo fp16 parts, two products), using one consistent
 //   assignment of keys to MFMA k-slots for both operands, so no data moves
 //   between lanes.
-// K is staged row-major with a 288-byte row pitch, V transposed with a 160-byte
-// pitch and its key columns permuted so that the 8 keys a lane needs for one V
-// fragment are adjacent: every fragment is one 16-byte LDS read.  Tiles alternate
-// between two LDS buffers: the next tile's global loads are in flight while the
-// current tile computes, and one barrier per tile suffices.
+// K and V tiles go from global memory straight to LDS (global_load_lds_dwordx4: a
+// wave's instruction fills 1 KB, lane L the 16-byte slot L), both row-major (a key
+// per 256-byte row) with the 16-byte chunks of row r XOR-swizzled by r mod 16, so the
+// fragment reads spread over the banks.  K fragments are 16-byte reads; V^T
+// fragments come from two transposing reads (ds_read_b64_tr_b16: within 16 lanes,
+// lane i receives element i mod 4 of the 8-byte pieces addressed by lanes 4e + i / 4,
+// e = 0 .. 3, so 16 lanes addressing 4 keys x 16 dims each receive one dim of the 4
+// keys).  Tiles alternate between two LDS buffers: the next tile's loads are in
+// flight while the current tile computes, and one barrier per tile suffices.
 // Workgroups are numbered so that consecutive ones take different kv heads: the
 // hardware deals workgroups round-robin to the 8 XCDs, so with 8 kv heads each
 // XCD's L2 serves the K/V of one head to every query block of that head.
@@ -37,8 +41,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int PF_ROWS = 256;    // (query, head) rows per workgroup
 constexpr int PF_THREADS = 512; // 8 waves x 32 rows
 constexpr int BK = 64;     // keys per tile
-constexpr int KSTR = 144;  // K row pitch in halves (288 B)
-constexpr int VSTR = 80;   // V^T row pitch in halves (160 B)
 constexpr float LOG2E_F = 1.4426950408889634f;
 constexpr float PF_PRE = 15.0f;  // log2 scale of p (p <= 2^15)
 
@@ -46,12 +48,8 @@ __device__ __forceinline__ floatx4 mfma(const half8& a, const half8& b, const fl
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {  // low halves of a, b
-  return (a & 0xFFFFu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {  // high halves of a, b
-  return (a >> 16) | (b & 0xFFFF0000u);
-}
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define KVQ8_LDSP(T, p) ((__attribute__((address_space(3))) T*)(p))
 
 template <int G>
 __global__ __launch_bounds__(PF_THREADS) void k_prefill(
@@ -70,8 +68,8 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
   const int q_last = min(q0 + BQ, n_tok) - 1;
   const int n_tiles = (pos0 + q_last + 1 + BK - 1) / BK;
 
-  __shared__ __attribute__((aligned(16))) _Float16 Ks[2][BK * KSTR];
-  __shared__ __attribute__((aligned(16))) _Float16 Vt[2][128 * VSTR];
+  __shared__ __attribute__((aligned(16))) _Float16 Ks[2][BK * HD];
+  __shared__ __attribute__((aligned(16))) _Float16 Vs[2][BK * HD];
 
   // ---- Q rows of this wave, fp16 (RNE), as B fragments of S^T = K Q^T ----------
   half8 qf[2][4];
@@ -109,54 +107,35 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
     for (int db = 0; db < 8; ++db) o[rb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- staging: K tile row-major, V tile transposed --------------------------
-  // K: 1024 chunks of 8 halves, 2 per thread.  V: thread holds keys 2kq, 2kq + 1 of
-  // dims 8dq .. 8dq + 7.  V^T column of key k (within its half of 32 keys, kk):
-  // 8 (kk % 16 / 4) + 4 (kk / 16) + kk % 4, the order of the P^T k-slots below.
-  uint4 kreg[2], vreg[2];
-  const int kq = tid & 31, dq = tid >> 5;
-  auto gload = [&](int tile) {
+  // ---- staging: K or V of a tile into an LDS buffer ---------------------------
+  // wave w's instruction u fills rows 8w + 4u .. + 3; slot (r, pc) holds chunk
+  // pc ^ (r & 15) of row r.  Keys past P read key P - 1 (masked: past every row's last
+  // key, and their weights are 0)
+  auto tload = [&](const uint16_t* src, _Float16* dst, int tile) {
     const int k0 = tile * BK;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int c = tid + PF_THREADS * u;
-      const int key = k0 + (c >> 4);
-      kreg[u] = key < P ? *reinterpret_cast<const uint4*>(k16 + ((long)h * stride + key) * HD +
-                                                          (c & 15) * 8)
-                        : make_uint4(0, 0, 0, 0);
-      const int vkey = k0 + 2 * kq + u;
-      vreg[u] = vkey < P ? *reinterpret_cast<const uint4*>(v16 + ((long)h * stride + vkey) * HD +
-                                                           8 * dq)
-                         : make_uint4(0, 0, 0, 0);
+      const int r = 8 * wave + 4 * u + (lane >> 4);
+      const int pc = lane & 15;
+      const int key = min(k0 + r, P - 1);
+      const uint16_t* gp = src + ((long)h * stride + key) * HD + 8 * (pc ^ (r & 15));
+      __builtin_amdgcn_global_load_lds(gp, KVQ8_LDSP(void, &dst[(8 * wave + 4 * u) * HD]), 16, 0, 0);
     }
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + PF_THREADS * u;
-      *reinterpret_cast<uint4*>(&Ks[buf][(c >> 4) * KSTR + (c & 15) * 8]) = kreg[u];
-    }
-    const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-    const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-    const int kk = 2 * kq;
-    const int col = (kk & 32) + 8 * ((kk & 15) >> 2) + 4 * ((kk >> 4) & 1) + (kk & 3);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {  // dims 2e and 2e+1 of the octet, keys 2kq and 2kq + 1
-      *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * dq + 2 * e) * VSTR + col]) = pack_lo(w0[e], w1[e]);
-      *reinterpret_cast<uint32_t*>(&Vt[buf][(8 * dq + 2 * e + 1) * VSTR + col]) = pack_hi(w0[e], w1[e]);
-    }
-  };
-
-  gload(0);
-  lstore(0);
+  tload(k16, Ks[0], 0);
+  tload(v16, Vs[0], 0);
+  __builtin_amdgcn_s_waitcnt(0);   // the direct loads count as loads
   __syncthreads();
   for (int tile = 0; tile < n_tiles; ++tile) {
     const int cur = tile & 1;
     const bool more = tile + 1 < n_tiles;
-    if (more) gload(tile + 1);
+    if (more) {   // buffers cur ^ 1 were last read in the previous tile, before its barrier
+      tload(k16, Ks[cur ^ 1], tile + 1);
+      tload(v16, Vs[cur ^ 1], tile + 1);
+    }
     const int k0 = tile * BK;
     const _Float16* KsC = Ks[cur];
-    const _Float16* VtC = Vt[cur];
+    const _Float16* VsC = Vs[cur];
 
     // ---- S^T = K Q^T --------------------------------------------------------
     floatx4 s[4][2];  // [kb][rb]: S^T[key = k0 + 16kb + 4*g4 + j][row = 16rb + l16]
@@ -169,7 +148,7 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
     // from moving each read back next to its use, so LDS latency hides behind MFMAs
     auto kfrag = [&](int i) __attribute__((always_inline)) {
       const int ks = i >> 2, kb = i & 3;
-      return *reinterpret_cast<const half8*>(&KsC[(16 * kb + l16) * KSTR + 32 * ks + 8 * g4]);
+      return *reinterpret_cast<const half8*>(&KsC[(16 * kb + l16) * HD + 8 * ((4 * ks + g4) ^ l16)]);
     };
     half8 kf[5];
 #pragma unroll
@@ -266,8 +245,16 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
     auto vfrag = [&](int i) __attribute__((always_inline)) {
       const int ks2 = i >> 3, db = i & 7;
       // k-slots (g4, 0 .. 7) of k-step ks2: keys 4 g4 .. + 3 and 16 + 4 g4 .. + 3 of the
-      // half, adjacent in the permuted columns
-      return *reinterpret_cast<const half8*>(&VtC[(16 * db + l16) * VSTR + 32 * ks2 + 8 * g4]);
+      // half.  Lane l16 = 4 e + q addresses key 32 ks2 + 4 g4 + e (then + 16), dims
+      // 16 db + 4q .. + 3, and receives dim 16 db + l16 of the four keys
+      const int e = l16 >> 2, q = l16 & 3;
+      const int c16 = 2 * db + (q >> 1);
+      const int r1 = 32 * ks2 + 4 * g4 + e, r2 = r1 + 16;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          KVQ8_LDSP(v4i16, &VsC[r1 * HD + 8 * (c16 ^ (r1 & 15)) + 4 * (q & 1)]));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          KVQ8_LDSP(v4i16, &VsC[r2 * HD + 8 * (c16 ^ (r2 & 15)) + 4 * (q & 1)]));
+      return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     half8 vf[3];
 #pragma unroll
@@ -285,9 +272,9 @@ __global__ __launch_bounds__(PF_THREADS) void k_prefill(
       }
     }
 
-    // the other buffer was last read in the previous tile, which every wave finished
-    // before the barrier that ended it
-    if (more) lstore(cur ^ 1);
+    // the next tile's direct loads have landed (they count as loads), then the barrier
+    // publishes them and frees this tile's buffers
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
