@@ -1095,19 +1095,21 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
 //     a table of 16 rows (two groups of dims, 4 heads, hi / lo) by the block's 64
 //     tokens.  Q8 has two 64-dim groups: one table.  K8V4 has four 32-dim groups of
 //     its rotated V: two tables, groups 0-1 and 2-3.
-//   V wave: stages the block's V rows in an LDS tile as signed bytes (Q8: the codes as
-//     loaded; K8V4: each nibble n made the byte n - 8, two per input byte, so the tile
-//     holds the codes of the rotated row in dim order) and reads them back transposed
-//     (ds_read_b64_tr_b8: 16 lanes receive one dim each, 8 tokens per read); a code of
-//     at most 7 bits becomes bf16 exactly (the upper half of its fp32 value), and one
-//     v_mfma_f32_16x16x32_bf16 per 16 dims and 32 tokens accumulates the rows'
-//     products in fp32.  The block's 64 tokens are the k-slots of both operands in the
-//     same order.  Lane (q, i) of a 16-dim tile holds rows 4q .. 4q + 3 of its table;
-//     the tile's dims belong to one group, whose rows (0 .. 7 or 8 .. 15) are kept.
-//     K8V4 leaves its output in the rotated basis; the merge undoes the rotation.
+//   V wave: stages the block's V rows in an LDS tile as bytes (Q8: the signed codes as
+//     loaded; K8V4: each nibble n made the byte 0x80 | n << 3, two per input byte, in
+//     dim order of the rotated row) and reads them back transposed (ds_read_b64_tr_b8:
+//     16 lanes receive one dim each, 8 tokens per read); a Q8 code of at most 7 bits
+//     becomes bf16 exactly (the upper half of its fp32 value), a K8V4 byte is the low
+//     byte of the bf16 value 16 + n; one v_mfma_f32_16x16x32_bf16 per 16 dims and 32
+//     tokens accumulates the rows' products in fp32 (K8V4 then takes out 24 times the
+//     weights' sums: 16 + n = 24 + code).  The block's 64 tokens are the k-slots of both
+//     operands in the same order.  Lane (q, i) of a 16-dim tile holds rows 4q .. 4q + 3
+//     of its table; the tile's dims belong to one group, whose rows (0 .. 7 or 8 .. 15)
+//     are kept.  K8V4 leaves its output in the rotated basis; the merge undoes the
+//     rotation.
 //   Against the vector V pass this moves the 64 FMAs a lane spends per step and 4
-//   heads onto the matrix cores; the V wave keeps 12 conversions per 8 codes (K8V4:
-//   plus 9 bit operations per 8 nibbles).
+//   heads onto the matrix cores; the V wave keeps 12 conversions per 8 Q8 codes, or 6
+//   bit operations and 6 byte permutes per 8 K8V4 values.
 #ifndef KVQ8_DEC_MV_CH
 #define KVQ8_DEC_MV_CH 16
 #endif
