@@ -617,9 +617,10 @@ def side_configs(kq, torch, steps=10, warmup=3):
 
 
 def paged_and_streamed(kq, torch, steps, warmup):
-    """Paged sessions and the streamed window, int8.
+    """Paged sessions and the streamed window.
 
-    paged_int8_ctx262144: the full 262144-cell single-session decode read through a
+    paged_int8_ctx262144, paged_f16_ctx262144: the full 262144-cell single-session
+    decode read through a
     page table: identity pages over the session itself, and a pool whose 4096 pages of
     64 cells sit at a seeded random permutation of its slots; set against the
     contiguous decode of the same cache (two caches in turn, each larger than the
@@ -637,51 +638,53 @@ def paged_and_streamed(kq, torch, steps, warmup):
     sh = kq.make_shape(Q8, KVH, NQH, HD)
     zero = torch.zeros(1, dtype=torch.int32, device="cuda")
 
-    # ---- paged decode at the full context ------------------------------------
+    # ---- paged decode at the full context, int8 and F16 -------------------------
     ctx, P = CTX, kq.KV_PAGE_ROWS
     npg = ctx // P
-    dk = torch.from_numpy(kvsynth.kv_tokens(seed, 0, ctx, KVH, HD, "K", True)[None]).cuda()
-    dv = torch.from_numpy(kvsynth.kv_tokens(seed, 0, ctx, KVH, HD, "V", True)[None]).cuda()
-    a = kq.Session(Q8, KVH, ctx)
-    kq.kv_append(sh, kq.session_table([a.entry()]), zero, 1, ctx, dk, dv)
-    del dk, dv
-    perm = torch.from_numpy(np.random.default_rng(seed).permutation(npg).astype(np.int32)).cuda()
-    b = kq.Session(Q8, KVH, ctx)
-    for ta, tb in zip(a.tensors(), b.tensors()):   # page p of a -> slot perm[p] of b
-        tb.view(KVH, npg, -1)[:, perm.long()] = ta.view(KVH, npg, -1)
-    ident = torch.arange(npg, dtype=torch.int32, device="cuda")
-    tab_a, tab_b = kq.session_table([a.entry()]), kq.session_table([b.entry()])
-    ld = torch.full((1,), ctx, dtype=torch.int32, device="cuda")
-    q = torch.from_numpy(kvsynth.queries(seed, 0, 1, NQH, HD)).cuda()
-    ws = kq.kv_decode_workspace(sh, 1, ctx)
-    o = [torch.empty((1, NQH, HD), device="cuda") for _ in range(3)]
-    st = torch.zeros(1, dtype=torch.int32, device="cuda")
-    calls = [lambda: kq.kv_decode_attn(sh, tab_a, ld, 1, ctx, q, sm, o[0], ws),
-             lambda: kq.kv_decode_attn_paged(sh, tab_b, perm, npg, ld, 1, ctx, q, sm, o[1], ws,
-                                             st),
-             lambda: kq.kv_decode_attn_paged(sh, tab_a, ident, npg, ld, 1, ctx, q, sm, o[2], ws,
-                                             st),
-             lambda: kq.kv_decode_attn_paged(sh, tab_b, perm, npg, ld, 1, ctx, q, sm, o[1], ws,
-                                             st)]
-    _time_calls(torch, calls, warmup)
-    t = _time_calls(torch, calls, steps)
-    torch.cuda.synchronize()
-    assert int(st.item()) == 0
-    assert torch.equal(o[0], o[1]) and torch.equal(o[0], o[2]), "paged decode differs"
-    nb = decode_bytes(Q8, ctx)
-    t_res, t_perm, t_id = t[0], (t[1] + t[3]) / 2, t[2]
-    out["paged_int8_ctx262144"] = {
-        "workload": "int8 cache, 262144 cells, 4096 pages of 64 cells; two caches in turn",
-        "resident_us": t_res * 1e6, "paged_identity_us": t_id * 1e6,
-        "paged_permuted_us": t_perm * 1e6, "decode_bytes": nb,
-        "paged_permuted_GB_s": nb / t_perm / 1e9,
-        "paged_permuted_frac_hbm": nb / t_perm / 1e9 / HBM_PEAK_GBS,
-        "paging_overhead": t_perm / t_res - 1.0,
-        "outputs_bitwise_equal": True}
-    log(f"paged int8 262144: resident {t_res * 1e6:.1f} us, identity pages {t_id * 1e6:.1f} us, "
-        f"permuted pages {t_perm * 1e6:.1f} us ({nb / t_perm / 1e9:.0f} GB/s)")
-    del a, b, tab_a, tab_b, ws, perm, ident
-    torch.cuda.empty_cache()
+    for fmt, key, name in ((Q8, "paged_int8_ctx262144", "int8"), (F16, "paged_f16_ctx262144", "F16")):
+        shf = kq.make_shape(fmt, KVH, NQH, HD)
+        dk = torch.from_numpy(kvsynth.kv_tokens(seed, 0, ctx, KVH, HD, "K", True)[None]).cuda()
+        dv = torch.from_numpy(kvsynth.kv_tokens(seed, 0, ctx, KVH, HD, "V", True)[None]).cuda()
+        a = kq.Session(fmt, KVH, ctx)
+        kq.kv_append(shf, kq.session_table([a.entry()]), zero, 1, ctx, dk, dv)
+        del dk, dv
+        perm = torch.from_numpy(np.random.default_rng(seed).permutation(npg).astype(np.int32)).cuda()
+        b = kq.Session(fmt, KVH, ctx)
+        for ta, tb in zip(a.tensors(), b.tensors()):   # page p of a -> slot perm[p] of b
+            tb.view(KVH, npg, -1)[:, perm.long()] = ta.view(KVH, npg, -1)
+        ident = torch.arange(npg, dtype=torch.int32, device="cuda")
+        tab_a, tab_b = kq.session_table([a.entry()]), kq.session_table([b.entry()])
+        ld = torch.full((1,), ctx, dtype=torch.int32, device="cuda")
+        q = torch.from_numpy(kvsynth.queries(seed, 0, 1, NQH, HD)).cuda()
+        ws = kq.kv_decode_workspace(shf, 1, ctx)
+        o = [torch.empty((1, NQH, HD), device="cuda") for _ in range(3)]
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        calls = [lambda: kq.kv_decode_attn(shf, tab_a, ld, 1, ctx, q, sm, o[0], ws),
+                 lambda: kq.kv_decode_attn_paged(shf, tab_b, perm, npg, ld, 1, ctx, q, sm, o[1],
+                                                 ws, st),
+                 lambda: kq.kv_decode_attn_paged(shf, tab_a, ident, npg, ld, 1, ctx, q, sm, o[2],
+                                                 ws, st),
+                 lambda: kq.kv_decode_attn_paged(shf, tab_b, perm, npg, ld, 1, ctx, q, sm, o[1],
+                                                 ws, st)]
+        _time_calls(torch, calls, warmup)
+        t = _time_calls(torch, calls, steps)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        assert torch.equal(o[0], o[1]) and torch.equal(o[0], o[2]), "paged decode differs"
+        nb = decode_bytes(fmt, ctx)
+        t_res, t_perm, t_id = t[0], (t[1] + t[3]) / 2, t[2]
+        out[key] = {
+            "workload": f"{name} cache, 262144 cells, 4096 pages of 64 cells; two caches in turn",
+            "resident_us": t_res * 1e6, "paged_identity_us": t_id * 1e6,
+            "paged_permuted_us": t_perm * 1e6, "decode_bytes": nb,
+            "paged_permuted_GB_s": nb / t_perm / 1e9,
+            "paged_permuted_frac_hbm": nb / t_perm / 1e9 / HBM_PEAK_GBS,
+            "paging_overhead": t_perm / t_res - 1.0,
+            "outputs_bitwise_equal": True}
+        log(f"paged {name} 262144: resident {t_res * 1e6:.1f} us, identity pages {t_id * 1e6:.1f} us, "
+            f"permuted pages {t_perm * 1e6:.1f} us ({nb / t_perm / 1e9:.0f} GB/s)")
+        del a, b, tab_a, tab_b, ws, perm, ident
+        torch.cuda.empty_cache()
 
     # ---- streamed window ------------------------------------------------------
     n, n_st, n_slots = 32768, 4, 1024
