@@ -423,6 +423,19 @@ def _time_calls(torch, calls, reps):
     return [float(np.mean([a.elapsed_time(b) for a, b in e])) * 1e-3 for e in ev]
 
 
+def _warm(torch, calls, ms=30.0):
+    """Untimed rounds of the callables until ms of wall time have passed: the clocks
+    settle at the load's level (a phase that left the GPU mostly idle, such as the
+    host-link copies before it, otherwise costs the first timed rounds several %)."""
+    t0 = time.perf_counter()
+    while True:
+        for f in calls:
+            f()
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= ms:
+            return
+
+
 def _time_loop(torch, calls, reps):
     """Mean seconds per call of the callables in calls run back to back, reps rounds,
     with one pair of HIP events around the whole run (no per-call events between
@@ -572,7 +585,7 @@ def side_configs(kq, torch, steps=10, warmup=3):
         ws = kq.kv_decode_workspace(sh, 1, ctx)
         o = torch.empty((1, NQH, HD), device="cuda")
         calls = [lambda t=t: kq.kv_decode_attn(sh, t, ld, 1, ctx, q, sm, o, ws) for t in tabs]
-        _time_calls(torch, calls, warmup)
+        _warm(torch, calls)
         # back to back over the 4 copies (as a model's layers run): the rate; and with
         # events around each call, which adds each launch's gap
         t = _time_loop(torch, calls, steps)
@@ -590,7 +603,7 @@ def side_configs(kq, torch, steps=10, warmup=3):
         # the same copy every call: a layer that fits the 256 MB last-level cache stays
         # in it (what one layer decoded in a loop would see); rotated above is the rate
         hot = [lambda: kq.kv_decode_attn(sh, tabs[0], ld, 1, ctx, q, sm, o, ws)]
-        _time_calls(torch, hot, warmup)
+        _warm(torch, hot)
         th = _time_loop(torch, hot, 4 * steps)
         out[key]["hot_decode_us"] = th * 1e6
         out[key]["hot_decode_GB_s"] = nb / th / 1e9
@@ -601,7 +614,7 @@ def side_configs(kq, torch, steps=10, warmup=3):
         x1v = torch.from_numpy(kvsynth.kv_tokens(w["seed"], 0, 1, KVH, HD, "V", True,
                                                  stream=kvsynth.S_V_NEW)[None]).cuda()
         app1 = [lambda t=t: kq.kv_append(sh, t, ld1, 1, 1, x1k, x1v) for t in tabs]
-        _time_calls(torch, app1, warmup)
+        _warm(torch, app1, 10.0)
         out[key]["step_append_us"] = _time_loop(torch, app1, steps) * 1e6
         log(f"{key}: decode {t * 1e6:.1f} us = {nb / t / 1e9:.0f} GB/s (graph {t_graph * 1e6:.1f} us, "
             f"hot {th * 1e6:.1f} us); one-token append {out[key]['step_append_us']:.1f} us")
@@ -666,7 +679,7 @@ def paged_and_streamed(kq, torch, steps, warmup):
                                                  ws, st),
                  lambda: kq.kv_decode_attn_paged(shf, tab_b, perm, npg, ld, 1, ctx, q, sm, o[1],
                                                  ws, st)]
-        _time_calls(torch, calls, warmup)
+        _warm(torch, calls)
         t = _time_calls(torch, calls, steps)
         torch.cuda.synchronize()
         assert int(st.item()) == 0
