@@ -453,9 +453,11 @@ def _time_loop(torch, calls, reps):
 
 
 def _time_graph(torch, calls, reps):
-    """Mean seconds per call of the callables in calls captured once, in order, as a
-    HIP graph and replayed reps times (HIP events around each replay on the graph's
-    stream): the calls as a captured step runs them, without the host's launches."""
+    """Mean seconds per call of the callables in calls, in order, repeated to at least
+    32 calls and captured once as a HIP graph, replayed reps times (HIP events around
+    each replay on the graph's stream): the calls as a captured step runs them, without
+    the host's launches (the repetition spreads the graph's own launch over many calls)."""
+    calls = list(calls) * max(1, 32 // len(calls))
     stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
