@@ -254,7 +254,8 @@ template <int SP>
 __device__ __forceinline__ int step_g(int gw, int k, int W) {
   static_assert(SP == 1 || SP == 2 || SP == 4 || SP == 8, "steps dealt in units of 1, 2, 4 or 8");
   if constexpr (SP == 1) return gw + k * W;
-  else return SP * (gw + (k / SP) * W) + (k % SP);
+  // k >= 0: unsigned division and remainder are a shift and a mask
+  else return SP * (gw + (int)((unsigned)k / SP) * W) + (int)((unsigned)k % SP);
 }
 #ifndef KVQ8_DEC_MV_SP
 #define KVQ8_DEC_MV_SP 8
@@ -475,7 +476,9 @@ struct KBatch {
         const bool second = (n >> 3) != 0;
         row = (uint32_t)((second ? pb1 : pb0) + min(n & 7, second ? lim1 : lim0));
       } else {
-        row = (uint32_t)min(step_g<SP>(gw, (n >> 3) ? k1 : k0, W) * 8 + (n & 7), len - 1);
+        // both steps' rows from wave-uniform values, then the lane's choice
+        const int s0 = step_g<SP>(gw, k0, W), s1 = step_g<SP>(gw, k1, W);
+        row = (uint32_t)min(((n >> 3) ? s1 : s0) * 8 + (n & 7), len - 1);
       }
 #pragma unroll
       for (int grp = 0; grp < NGRP; ++grp) {
@@ -1116,7 +1119,11 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
 constexpr int MV_CH = KVQ8_DEC_MV_CH;  // steps per chunk (Q8)
 constexpr int MV_BLK = 8;              // steps per 64-token block
 constexpr int MV_PITCH = 144;          // bytes per V tile row (16-byte aligned rows)
-constexpr int MV_AROW = 32;            // weight-table bytes per token (16 bf16 rows)
+// a weight table: per 8-token group, its 16 rows of 8 bf16 (16 bytes each) and 16
+// bytes of padding, which keeps the K wave's 2-byte stores of one row free of bank
+// conflicts with addresses that are a per-lane base plus a constant
+constexpr int MV_TSTR = 16 * 16 + 16;  // bytes per 8-token group
+constexpr int MV_TBL = 8 * MV_TSTR;    // bytes per table (64 tokens)
 static_assert(MV_CH % (2 * MV_BLK) == 0, "a chunk holds whole pairs of blocks");
 
 // steps per chunk: K8V4's two weight tables per block take one-block chunks, so that
@@ -1130,11 +1137,13 @@ __host__ __device__ constexpr size_t mv_pair_bytes() {
   // logits of one chunk, the weight tables of two chunks, the rescale factors of two
   // chunks, the V tile
   return (size_t)mv_chunk<FMT>() * 8 * G * 4 +
-         2 * (size_t)mv_chunk<FMT>() * 8 * MV_AROW * mv_tables<FMT>() + 2 * 4 * 4 + 64 * MV_PITCH;
+         2 * (size_t)(mv_chunk<FMT>() / MV_BLK) * mv_tables<FMT>() * MV_TBL + 2 * 4 * 4 +
+         64 * MV_PITCH;
 }
 template <int FMT, int G>
 __host__ __device__ constexpr size_t mv_lds_bytes() {
-  return PAIRS * mv_pair_bytes<FMT, G>() + DEC_WAVES * 64 * 4;
+  // the logit stores of lanes past G heads go to a per-wave discard area (none for G = 4)
+  return PAIRS * mv_pair_bytes<FMT, G>() + (G < 4 ? DEC_WAVES * 64 * 4 : 0);
 }
 static_assert(mv_pair_bytes<KV_FMT_Q8, 4>() % 16 == 0 && mv_pair_bytes<KV_FMT_Q8, 2>() % 16 == 0 &&
                   mv_pair_bytes<KV_FMT_Q8, 1>() % 16 == 0 &&
@@ -1152,19 +1161,22 @@ static_assert(mv_lds_bytes<KV_FMT_Q8, 4>() <= 80 * 1024 && mv_lds_bytes<KV_FMT_K
 __device__ __forceinline__ float max2(float a, float b) {
   return __builtin_amdgcn_fmed3f(a, b, INFINITY);
 }
+// the bits of a float as a signed int of the same order (negative values have their
+// magnitude bits flipped; the map is its own inverse; -inf is the least value here)
+__device__ __forceinline__ int ord_bits(int i) { return i ^ ((i >> 31) & 0x7FFFFFFF); }
 // Max over the wave, returned wave-uniform, with cross-lane moves only: the four
 // in-row stages, then each row's lane 15 into the next row, lane 31 into rows 2 and 3;
-// lane 63 then holds the whole wave's max.
+// lane 63 then holds the whole wave's max.  The stages compare the values' ordered
+// bits as integers (a float max would first quiet each moved value).
 __device__ __forceinline__ float wave_max_dpp(float v) {
-  v = max2(v, dpp<DPP_QUAD_XOR1>(v));
-  v = max2(v, dpp<DPP_QUAD_XOR2>(v));
-  v = max2(v, dpp<DPP_ROW_HALF_MIRROR>(v));
-  v = max2(v, dpp<DPP_ROW_MIRROR>(v));
-  const int iv = __builtin_bit_cast(int, v);
-  v = max2(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iv, iv, 0x142, 0xA, 0xF, false)));
-  const int iw = __builtin_bit_cast(int, v);
-  v = max2(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(iw, iw, 0x143, 0xC, 0xF, false)));
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  int x = ord_bits(__builtin_bit_cast(int, v));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, DPP_QUAD_XOR1, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, DPP_QUAD_XOR2, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, DPP_ROW_HALF_MIRROR, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, DPP_ROW_MIRROR, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x142, 0xA, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x143, 0xC, 0xF, false));
+  return __builtin_bit_cast(float, ord_bits(__builtin_amdgcn_readlane(x, 63)));
 }
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 #define KVQ8_LDS __attribute__((address_space(3)))
@@ -1175,6 +1187,21 @@ __device__ __forceinline__ i32x2 lds_tr8(const uint8_t* p) {
 }
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// G consecutive floats of LDS in one read (16-byte aligned for G = 4, 8-byte for 2)
+template <int G>
+__device__ __forceinline__ void lds_floats(const float* p, float (&o)[G]) {
+  if constexpr (G == 4) {
+    const f32x4 t = *reinterpret_cast<const f32x4*>(p);
+    o[0] = t[0]; o[1] = t[1]; o[2] = t[2]; o[3] = t[3];
+  } else if constexpr (G == 2) {
+    const f32x2 t = *reinterpret_cast<const f32x2*>(p);
+    o[0] = t[0]; o[1] = t[1];
+  } else {
+    o[0] = p[0];
+  }
+}
 // 8 int8 codes (the bytes of c, in order) as 8 bf16, exactly: the upper half of each
 // code's fp32 value
 __device__ __forceinline__ bf16x8 codes_bf16(i32x2 c) {
@@ -1264,9 +1291,10 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
   extern __shared__ float smem[];
   uint8_t* reg = reinterpret_cast<uint8_t*>(smem) + (size_t)pr * mv_pair_bytes<FMT, G>();
   float* lc = reinterpret_cast<float*>(reg);                            // [CHK*8][G]
-  uint8_t* at = reg + (size_t)CHK * 8 * G * 4;                          // [2][CHK/8][NT][64][AROW]
-  float* fb = reinterpret_cast<float*>(at + 2 * CHK * 8 * MV_AROW * NT);  // [2][4]
+  uint8_t* at = reg + (size_t)CHK * 8 * G * 4;                          // [2][NCB][NT][TBL]
+  float* fb = reinterpret_cast<float*>(at + 2 * NCB * NT * MV_TBL);     // [2][4]
   uint8_t* tile = reinterpret_cast<uint8_t*>(fb + 8);                   // [64][PITCH]
+  // discarded logit stores of lanes past G heads (only G < 4 has such lanes)
   float* junk = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem) +
                                          PAIRS * mv_pair_bytes<FMT, G>()) + wave * 64;
   // after the loops every pair region is free: the partials reuse them
@@ -1281,10 +1309,15 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
   const char* vsb = reinterpret_cast<const char*>(ss.v_scale) + hrow * VSC * 2;
   // the pool row (contiguous: the row) of token 64 bl + lane of the chunk starting at
   // step ch CHK: row lane % 8 of its step
+  // Step sb + i of a wave, sb a multiple of 8 (so of SP) and i < 8, is its step sb
+  // plus step_g(0, i): the lane's part of the step (step i = lane / 8 of the 8 that
+  // start at sb) is one constant, the rest wave-uniform.
+  const int lane_step = step_g<SP>(0, lane >> 3, W);
   auto chunk_row = [&](int ch, int bl) __attribute__((always_inline)) {
     const int st = ch * CHK + bl * 8 + (lane >> 3);
     if constexpr (PG != 0) return pm.lane_row(pm.block(ch * CHK + bl * 8), st, gw, W, lane & 7);
-    else return (uint32_t)min(step_g<SP>(gw, min(st, kmax), W) * 8 + (lane & 7), len - 1);
+    // steps past the wave's own (masked tokens) read any row of the session
+    else return (uint32_t)min((step_g<SP>(gw, ch * CHK + bl * 8, W) + lane_step) * 8 + (lane & 7), len - 1);
   };
 
   if (kw) {
@@ -1397,72 +1430,83 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
       wave_lds_fence();
       const int c0 = ch * CHK;
       const int nl = max(0, min(n_steps, c0 + CHK) - c0) * 8;
+      // the lane's token of each block: whether it is one of the session's tokens,
+      // its logits (all heads, one read)
+      bool ok[NCB];
       float mc[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) mc[g] = -INFINITY;
 #pragma unroll
       for (int bl = 0; bl < NCB; ++bl) {
         const int tl = bl * 64 + lane;
-        const int t = step_g<SP>(gw, c0 + (tl >> 3), W) * 8 + (tl & 7);
-        if (tl < nl && t < len) {
+        const int t = (step_g<SP>(gw, c0 + bl * 8, W) + lane_step) * 8 + (lane & 7);
+        ok[bl] = tl < nl && t < len;
+        float lg[G];
+        lds_floats<G>(lc + tl * G, lg);
 #pragma unroll
-          for (int g = 0; g < G; ++g) mc[g] = max2(mc[g], lc[tl * G + g]);
-        }
+        for (int g = 0; g < G; ++g) mc[g] = max2(mc[g], ok[bl] ? lg[g] : -INFINITY);
       }
-      float* fc = fb + (ch & 1) * 4;
-      float cm[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) cm[g] = wave_max_dpp(mc[g]);
+      float f[G];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float mn = max2(m[g], cm[g]);
-        const float f = mn == -INFINITY ? 1.f : exp2f(m[g] - mn);
+        const float mn = max2(m[g], wave_max_dpp(mc[g]));
+        f[g] = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[g] - mn);
         m[g] = mn;
-        l[g] *= f;
-        if (lane == g) fc[g] = f;
+        l[g] *= f[g];
       }
-      uint8_t* atc = at + (ch & 1) * CHK * 8 * MV_AROW * NT;
+      if (lane == 0) {
+        float* fc = fb + (ch & 1) * 4;
+#pragma unroll
+        for (int g = 0; g < G; ++g) fc[g] = f[g];
+      }
+      // A operand layout: table grp / 2, row m = 8 (grp % 2) + 2 head + part; token
+      // 8 g8 + j of the block (lane 8 g8 + j) at byte g8 MV_TSTR + 16 m + 2 j.  Rows of
+      // heads past G are left as they are: they only reach rows of the product that
+      // are dropped.
+      uint8_t* atc = at + (ch & 1) * NCB * NT * MV_TBL + (lane >> 3) * MV_TSTR + 2 * (lane & 7);
 #pragma unroll
       for (int bl = 0; bl < NCB; ++bl) {
-        const int tl = bl * 64 + lane;
-        const int st = c0 + (tl >> 3);
-        const int t = step_g<SP>(gw, st, W) * 8 + (tl & 7);
-        const bool ok = tl < nl && t < len;
         float sv[VSC];
 #pragma unroll
         for (int k = 0; k < VSC / 2; ++k) {
           sv[2 * k] = h2f((uint16_t)(svn[bl][k] & 0xFFFFu));
           sv[2 * k + 1] = h2f((uint16_t)(svn[bl][k] >> 16));
         }
-        // the weights w = p * s_v and their bf16 split: hi = w truncated to bf16, lo =
-        // the rest rounded to bf16 (|w - hi - lo| <= 2^-16 |w|)
-        float p4[4];
+        // p = 2^(logit - max), 0 for a token past the session's end (whose logit slot
+        // may hold anything); results below 2^-126 flush to 0
+        float lg[G], p[G];
+        lds_floats<G>(lc + (bl * 64 + lane) * G, lg);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          float p = 0.f;
-          if (g < G) {
-            p = ok ? exp2f(lc[tl * G + g] - m[g]) : 0.f;
-            l[g] += p;
-          }
-          p4[g] = p;
+        for (int g = 0; g < G; ++g) {
+          const float e = __builtin_amdgcn_exp2f(lg[g] - m[g]);
+          p[g] = ok[bl] ? e : 0.f;
+          l[g] += p[g];
         }
-        // A operand layout: table grp / 2, row m = 8 (grp % 2) + 2 head + part, token
-        // k = lane = 8 g8 + j at byte (g8 16 + (m ^ g8)) 16 + 2 j of the table's 2 KB
-        const int g8 = lane >> 3, jt = lane & 7;
+        // the weights w = p * s_v and their bf16 split: hi = w truncated to bf16, lo =
+        // the rest rounded to bf16 (|w - hi - lo| <= 2^-16 |w|), two heads' lo at once
 #pragma unroll
         for (int grp = 0; grp < VSC; ++grp) {
-          uint8_t* atb = atc + ((size_t)bl * NT + (grp >> 1)) * 64 * MV_AROW;
+          uint8_t* atb = atc + (bl * NT + (grp >> 1)) * MV_TBL + 16 * 8 * (grp & 1);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const float w = p4[g] * sv[grp];
-            const uint32_t wb = __builtin_bit_cast(uint32_t, w);
-            const uint32_t hib = wb & 0xFFFF0000u;
-            const float lo = w - __builtin_bit_cast(float, hib);
-            const uint16_t lob = __builtin_bit_cast(uint16_t, (__bf16)lo);
-            const int m0 = 8 * (grp & 1) + 2 * g;
-            *reinterpret_cast<uint16_t*>(atb + (g8 * 16 + (m0 ^ g8)) * 16 + 2 * jt) =
-                (uint16_t)(hib >> 16);
-            *reinterpret_cast<uint16_t*>(atb + (g8 * 16 + ((m0 + 1) ^ g8)) * 16 + 2 * jt) = lob;
+          for (int g = 0; g < G; g += 2) {
+            uint32_t hib[2] = {0u, 0u};
+            float lo[2] = {0.f, 0.f};
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              if (g + e < G) {
+                const float w = p[g + e] * sv[grp];
+                hib[e] = __builtin_bit_cast(uint32_t, w) & 0xFFFF0000u;
+                lo[e] = w - __builtin_bit_cast(float, hib[e]);
+              }
+            }
+            const uint32_t lob =
+                __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo[0], lo[1]}, bf16x2));
+            *reinterpret_cast<uint16_t*>(atb + 16 * (2 * g)) = (uint16_t)(hib[0] >> 16);
+            *reinterpret_cast<uint16_t*>(atb + 16 * (2 * g + 1)) = (uint16_t)(lob & 0xFFFFu);
+            if (g + 1 < G) {
+              *reinterpret_cast<uint16_t*>(atb + 16 * (2 * g + 2)) = (uint16_t)(hib[1] >> 16);
+              *reinterpret_cast<uint16_t*>(atb + 16 * (2 * g + 3)) = (uint16_t)(lob >> 16);
+            }
           }
         }
       }
@@ -1497,6 +1541,10 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
   } else {
     // ================= V wave ===================================================
     const int qv = lane >> 4, iv = lane & 15;
+    // the lane's LDS bases: row iv of token group qv of a weight table; the tile bytes
+    // its transposing reads start at (token group qv, dims 8 (iv % 2) ..)
+    const uint8_t* a_lane = at + qv * MV_TSTR + iv * 16;
+    const uint8_t* t_lane = tile + (8 * qv + (iv >> 1)) * MV_PITCH + 8 * (iv & 1);
     // D tile jd (dims 16 jd ..): lane (qv, iv) holds rows 4 qv .. 4 qv + 3 of dim
     // 16 jd + iv of its table, rows m = 8 (group % 2) + 2 head + part; heads ha, ha + 1
     const int ha = 2 * (qv & 1);
@@ -1566,19 +1614,19 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         *reinterpret_cast<u32x4*>(tile + (u * 8 + r) * MV_PITCH + c * 16) = cw;
       }
       wave_lds_fence();
-      const uint8_t* atb = at + (ch & 1) * CHK * 8 * MV_AROW * NT + bl * NT * 64 * MV_AROW;
+      const uint8_t* atb = a_lane + ((ch & 1) * NCB + bl) * NT * MV_TBL;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int g8 = 4 * hh + qv;   // tokens 8 g8 .. 8 g8 + 7 of the block
+        // tokens 8 g8 .. 8 g8 + 7 of the block, g8 = 4 hh + qv
         bf16x8 aw[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          aw[t] = *reinterpret_cast<const bf16x8*>(atb + t * 64 * MV_AROW + (g8 * 16 + (iv ^ g8)) * 16);
+          aw[t] = *reinterpret_cast<const bf16x8*>(atb + t * MV_TBL + hh * 4 * MV_TSTR);
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) {
           // B: the codes of tokens 8 g8 + 0 .. 7, dim 16 jd + iv, as bf16 (exact; K8V4:
           // 16 + n)
-          const i32x2 cb = lds_tr8(tile + (8 * g8 + (iv >> 1)) * MV_PITCH + 16 * jd + 8 * (iv & 1));
+          const i32x2 cb = lds_tr8(t_lane + hh * 32 * MV_PITCH + 16 * jd);
           acc[jd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               aw[K4 ? jd >> 2 : 0], K4 ? biased_bf16(cb) : codes_bf16(cb), acc[jd], 0, 0, 0);
         }
