@@ -489,6 +489,41 @@ struct KBatch {
   }
 };
 
+// max(a, b) in one instruction (the median of a, b and +inf; no NaN quieting)
+__device__ __forceinline__ float max2(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, INFINITY);
+}
+// the bits of a float as a signed int of the same order (negative values have their
+// magnitude bits flipped; the map is its own inverse; -inf is the least value here)
+__device__ __forceinline__ int ord_bits(int i) { return i ^ ((i >> 31) & 0x7FFFFFFF); }
+// Max over the wave, returned wave-uniform, with cross-lane moves only: the four
+// in-row stages, then each row's lane 15 into the next row, lane 31 into rows 2 and 3;
+// lane 63 then holds the whole wave's max.  The stages compare the values' ordered
+// bits as integers (a float max would first quiet each moved value).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  int x = ord_bits(__builtin_bit_cast(int, v));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, DPP_QUAD_XOR1, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, DPP_QUAD_XOR2, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, DPP_ROW_HALF_MIRROR, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, DPP_ROW_MIRROR, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x142, 0xA, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x143, 0xC, 0xF, false));
+  return __builtin_bit_cast(float, ord_bits(__builtin_amdgcn_readlane(x, 63)));
+}
+// Sum over the wave, returned wave-uniform: the stages of wave_max_dpp with adds (a
+// row left out of a broadcast stage adds 0).
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp<DPP_QUAD_XOR1>(v);
+  v += dpp<DPP_QUAD_XOR2>(v);
+  v += dpp<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp<DPP_ROW_MIRROR>(v);
+  v += __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+  v += __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 // LDS of one split workgroup: per-wave logits (ch0 + ch1 = 2 ch_steps per pair of
 // waves sharing a SIMD, whatever the format), the wave partials (o, m, l) and one
 // discarded-store slot per lane
@@ -651,8 +686,8 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         // finite: every step of the wave holds a token below len
-        const float mn = fmaxf(m[g], wave_max(mc[g]));
-        const float f = exp2f(m[g] - mn);   // 0 on the first chunk (m = -inf)
+        const float mn = fmaxf(m[g], wave_max_dpp(mc[g]));
+        const float f = __builtin_amdgcn_exp2f(m[g] - mn);   // 0 on the first chunk (m = -inf)
         m[g] = mn;
         l[g] *= f;
 #pragma unroll
@@ -663,7 +698,8 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
         const bool ok = tl < s1 * 8 && t < len;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float p = ok ? exp2f(lg[tl * G + g] - m[g]) : 0.f;
+          // the bare exp2 (results below 2^-126 flush to 0)
+          const float p = ok ? __builtin_amdgcn_exp2f(lg[tl * G + g] - m[g]) : 0.f;
           lg[tl * G + g] = p;
           l[g] += p;
         }
@@ -694,7 +730,7 @@ __attribute__((amdgpu_waves_per_eu(KVQ8_DEC_WAVES_PER_EU))) void k_decode_split(
     // ---- V pass -----------------------------------------------------------------
     vpass(0, n_it);
 #pragma unroll
-    for (int g = 0; g < G; ++g) l[g] = wave_sum(l[g]);
+    for (int g = 0; g < G; ++g) l[g] = wave_sum_dpp(l[g]);
 #pragma unroll
     for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -947,9 +983,9 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
         float* fc = fb + (ch & 1) * G;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float mn = fmaxf(m[g], wave_max(mc[g]));
+          const float mn = fmaxf(m[g], wave_max_dpp(mc[g]));
           // 0 on the pair's first chunk (m = -inf); 1 while the pair has no token yet
-          const float f = mn == -INFINITY ? 1.f : exp2f(m[g] - mn);
+          const float f = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[g] - mn);
           m[g] = mn;
           l[g] *= f;
           if (lane == g) fc[g] = f;
@@ -959,7 +995,7 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
           const bool ok = tl < nl && t < len;
 #pragma unroll
           for (int g = 0; g < G; ++g) {
-            const float pv = ok ? exp2f(lc[tl * G + g] - m[g]) : 0.f;
+            const float pv = ok ? __builtin_amdgcn_exp2f(lc[tl * G + g] - m[g]) : 0.f;
             lc[tl * G + g] = pv;
             l[g] += pv;
           }
@@ -975,7 +1011,7 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
     }
     __syncthreads();   // the V wave's last chunk
 #pragma unroll
-    for (int g = 0; g < G; ++g) l[g] = wave_sum(l[g]);
+    for (int g = 0; g < G; ++g) l[g] = wave_sum_dpp(l[g]);
     if (lane == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -1157,27 +1193,6 @@ static_assert(PAIRS * mv_pair_bytes<KV_FMT_K8V4, 1>() >=
 static_assert(mv_lds_bytes<KV_FMT_Q8, 4>() <= 80 * 1024 && mv_lds_bytes<KV_FMT_K8V4, 4>() <= 80 * 1024,
               "two workgroups share a CU's 160 KB of LDS");
 
-// max(a, b) in one instruction (the median of a, b and +inf; no NaN quieting)
-__device__ __forceinline__ float max2(float a, float b) {
-  return __builtin_amdgcn_fmed3f(a, b, INFINITY);
-}
-// the bits of a float as a signed int of the same order (negative values have their
-// magnitude bits flipped; the map is its own inverse; -inf is the least value here)
-__device__ __forceinline__ int ord_bits(int i) { return i ^ ((i >> 31) & 0x7FFFFFFF); }
-// Max over the wave, returned wave-uniform, with cross-lane moves only: the four
-// in-row stages, then each row's lane 15 into the next row, lane 31 into rows 2 and 3;
-// lane 63 then holds the whole wave's max.  The stages compare the values' ordered
-// bits as integers (a float max would first quiet each moved value).
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  int x = ord_bits(__builtin_bit_cast(int, v));
-  x = max(x, __builtin_amdgcn_update_dpp(0, x, DPP_QUAD_XOR1, 0xF, 0xF, true));
-  x = max(x, __builtin_amdgcn_update_dpp(0, x, DPP_QUAD_XOR2, 0xF, 0xF, true));
-  x = max(x, __builtin_amdgcn_update_dpp(0, x, DPP_ROW_HALF_MIRROR, 0xF, 0xF, true));
-  x = max(x, __builtin_amdgcn_update_dpp(0, x, DPP_ROW_MIRROR, 0xF, 0xF, true));
-  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x142, 0xA, 0xF, false));
-  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x143, 0xC, 0xF, false));
-  return __builtin_bit_cast(float, ord_bits(__builtin_amdgcn_readlane(x, 63)));
-}
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 #define KVQ8_LDS __attribute__((address_space(3)))
 // transposing 8-byte LDS read: within each 16 lanes, lane i receives byte i % 8 of
@@ -1530,7 +1545,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
     }
     __syncthreads();   // the V wave's last chunk
 #pragma unroll
-    for (int g = 0; g < G; ++g) l[g] = wave_sum(l[g]);
+    for (int g = 0; g < G; ++g) l[g] = wave_sum_dpp(l[g]);
     if (lane == 0) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -1804,10 +1819,11 @@ __global__ __launch_bounds__(MERGE_THREADS) void k_decode_merge(
     if (j0 > 0) load_chunk(j0);
     const int n = min(MERGE_CHUNK, Sb - j0);   // workgroup-uniform
     const float fl = lane < n ? f : -INFINITY;
-    const float Mn = fmaxf(M, wave_max(fl));   // finite: the chunk holds split j0
-    const float w = lane < n ? exp2f(f - Mn) : 0.f;
-    const float alpha = exp2f(M - Mn);          // 0 on the first chunk (M = -inf)
-    L = fmaf(L, alpha, wave_sum(w));
+    const float Mn = fmaxf(M, wave_max_dpp(fl));   // finite: the chunk holds split j0
+    // the bare exp2: a split more than 126 below the max adds nothing
+    const float w = lane < n ? __builtin_amdgcn_exp2f(f - Mn) : 0.f;
+    const float alpha = __builtin_amdgcn_exp2f(M - Mn);   // 0 on the first chunk (M = -inf)
+    L = fmaf(L, alpha, wave_sum_dpp(w));
     acc.x *= alpha;
     acc.y *= alpha;
     acc.z *= alpha;
