@@ -1130,10 +1130,12 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
 //   K wave: the logits as in k_decode_pair; then, per 64-token block (8 steps), the
 //     weights w = p * (V scale of the token's group of dims), each split into two bf16
 //     values, hi = w truncated to bf16 and lo = (w - hi) rounded to bf16
-//     (|w - hi - lo| <= 2^-16 |w|), written to LDS in the layout of an MFMA A operand:
-//     a table of 16 rows (two groups of dims, 4 heads, hi / lo) by the block's 64
-//     tokens.  Q8 has two 64-dim groups: one table.  K8V4 has four 32-dim groups of
-//     its rotated V: two tables, groups 0-1 and 2-3.
+//     (|w - hi - lo| <= 2^-16 |w|), written to LDS as a table of 16 rows (two groups
+//     of dims, 4 heads, hi / lo) by the block's 64 tokens, token-major (a lane stores
+//     its token's rows of one group with one 16-byte store); the V wave reads it back
+//     as MFMA A operands with transposing 16-bit reads (ds_read_b64_tr_b16).  Q8 has
+//     two 64-dim groups: one table.  K8V4 has four 32-dim groups of its rotated V: two
+//     tables, groups 0-1 and 2-3.
 //   V wave: stages the block's V rows in an LDS tile as bytes (Q8: the signed codes as
 //     loaded; K8V4: each nibble n made the byte 0x80 | n << 3, two per input byte, in
 //     dim order of the rotated row) and reads them back transposed (ds_read_b64_tr_b8:
@@ -1155,11 +1157,8 @@ __global__ __launch_bounds__(DEC_THREADS) __attribute__((amdgpu_waves_per_eu(G >
 constexpr int MV_CH = KVQ8_DEC_MV_CH;  // steps per chunk (Q8)
 constexpr int MV_BLK = 8;              // steps per 64-token block
 constexpr int MV_PITCH = 144;          // bytes per V tile row (16-byte aligned rows)
-// a weight table: per 8-token group, its 16 rows of 8 bf16 (16 bytes each) and 16
-// bytes of padding, which keeps the K wave's 2-byte stores of one row free of bank
-// conflicts with addresses that are a per-lane base plus a constant
-constexpr int MV_TSTR = 16 * 16 + 16;  // bytes per 8-token group
-constexpr int MV_TBL = 8 * MV_TSTR;    // bytes per table (64 tokens)
+// a weight table: 64 tokens x 16 bf16 rows, token-major (32 bytes per token)
+constexpr int MV_TBL = 64 * 32;        // bytes per table
 static_assert(MV_CH % (2 * MV_BLK) == 0, "a chunk holds whole pairs of blocks");
 
 // steps per chunk: K8V4's two weight tables per block take one-block chunks, so that
@@ -1201,6 +1200,15 @@ __device__ __forceinline__ i32x2 lds_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((KVQ8_LDS i32x2*)(KVQ8_LDS uint8_t*)p);
 }
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+// two transposing 16-bit LDS reads (ds_read_b64_tr_b16: within each 16 lanes, lane i
+// receives element i % 4 of the 8 bytes addressed by lanes 4 e + i / 4, e = 0 .. 3)
+// joined as one 8-element bf16 operand, p0's four elements first
+__device__ __forceinline__ bf16x8 lds_tr16x2(const uint8_t* p0, const uint8_t* p1) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((KVQ8_LDS i16x4*)(KVQ8_LDS uint8_t*)p0);
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((KVQ8_LDS i16x4*)(KVQ8_LDS uint8_t*)p1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -1474,11 +1482,15 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
 #pragma unroll
         for (int g = 0; g < G; ++g) fc[g] = f[g];
       }
-      // A operand layout: table grp / 2, row m = 8 (grp % 2) + 2 head + part; token
-      // 8 g8 + j of the block (lane 8 g8 + j) at byte g8 MV_TSTR + 16 m + 2 j.  Rows of
-      // heads past G are left as they are: they only reach rows of the product that
-      // are dropped.
-      uint8_t* atc = at + (ch & 1) * NCB * NT * MV_TBL + (lane >> 3) * MV_TSTR + 2 * (lane & 7);
+      // Table layout (table grp / 2, row m = 8 (grp % 2) + 2 head + part): token
+      // t = 8 g8 + j of the block (lane t) keeps its 16 rows in 32 bytes at
+      // 256 g8 + 128 ((j / 4) ^ s) + 32 (j % 4), s = g8 % 2, rows 8 h .. 8 h + 7 in the
+      // 16-byte half h ^ s: one 16-byte store per token and group, and the 16 lanes of
+      // a store (or of a transposing read in the V wave) cover all 64 banks.  Rows of
+      // heads past G hold 0.
+      const int g8k = lane >> 3, jk = lane & 7, swk = g8k & 1;
+      uint8_t* atc = at + (ch & 1) * NCB * NT * MV_TBL + g8k * 256 + ((jk >> 2) ^ swk) * 128 +
+                     (jk & 3) * 32;
 #pragma unroll
       for (int bl = 0; bl < NCB; ++bl) {
         float sv[VSC];
@@ -1498,31 +1510,30 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
           l[g] += p[g];
         }
         // the weights w = p * s_v and their bf16 split: hi = w truncated to bf16, lo =
-        // the rest rounded to bf16 (|w - hi - lo| <= 2^-16 |w|), two heads' lo at once
+        // the rest rounded to bf16 (|w - hi - lo| <= 2^-16 |w|), two heads' lo at once;
+        // rows 2 g, 2 g + 1 of a group are one word: hi (w's upper half), lo
 #pragma unroll
         for (int grp = 0; grp < VSC; ++grp) {
-          uint8_t* atb = atc + (bl * NT + (grp >> 1)) * MV_TBL + 16 * 8 * (grp & 1);
+          uint32_t d[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
           for (int g = 0; g < G; g += 2) {
-            uint32_t hib[2] = {0u, 0u};
+            uint32_t wb[2] = {0u, 0u};
             float lo[2] = {0.f, 0.f};
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
               if (g + e < G) {
                 const float w = p[g + e] * sv[grp];
-                hib[e] = __builtin_bit_cast(uint32_t, w) & 0xFFFF0000u;
-                lo[e] = w - __builtin_bit_cast(float, hib[e]);
+                wb[e] = __builtin_bit_cast(uint32_t, w);
+                lo[e] = w - __builtin_bit_cast(float, wb[e] & 0xFFFF0000u);
               }
             }
             const uint32_t lob =
                 __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo[0], lo[1]}, bf16x2));
-            *reinterpret_cast<uint16_t*>(atb + 16 * (2 * g)) = (uint16_t)(hib[0] >> 16);
-            *reinterpret_cast<uint16_t*>(atb + 16 * (2 * g + 1)) = (uint16_t)(lob & 0xFFFFu);
-            if (g + 1 < G) {
-              *reinterpret_cast<uint16_t*>(atb + 16 * (2 * g + 2)) = (uint16_t)(hib[1] >> 16);
-              *reinterpret_cast<uint16_t*>(atb + 16 * (2 * g + 3)) = (uint16_t)(lob >> 16);
-            }
+            d[g] = __builtin_amdgcn_perm(lob, wb[0], 0x05040302u);
+            if (g + 1 < G) d[g + 1] = __builtin_amdgcn_perm(lob, wb[1], 0x07060302u);
           }
+          *reinterpret_cast<u32x4*>(atc + (bl * NT + (grp >> 1)) * MV_TBL + ((grp & 1) ^ swk) * 16) =
+              u32x4{d[0], d[1], d[2], d[3]};
         }
       }
       __syncthreads();
@@ -1556,9 +1567,13 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
   } else {
     // ================= V wave ===================================================
     const int qv = lane >> 4, iv = lane & 15;
-    // the lane's LDS bases: row iv of token group qv of a weight table; the tile bytes
-    // its transposing reads start at (token group qv, dims 8 (iv % 2) ..)
-    const uint8_t* a_lane = at + qv * MV_TSTR + iv * 16;
+    // the lane's LDS bases: the 8 bytes of a weight table its two transposing 16-bit
+    // reads address (lane 4 e + c of the 16: rows 4 c .. 4 c + 3 of the e-th token of
+    // tokens 8 g8 .. 8 g8 + 3, then of 8 g8 + 4 .. 8 g8 + 7, g8 = 4 hh + qv); the tile
+    // bytes its transposing 8-bit reads start at (token group qv, dims 8 (iv % 2) ..)
+    const int swv = qv & 1;
+    const uint8_t* a_lane = at + qv * 256 + (iv >> 2) * 32 + (((iv & 3) >> 1) ^ swv) * 16 + (iv & 1) * 8;
+    const int a_r0 = swv * 128, a_r1 = (swv ^ 1) * 128;
     const uint8_t* t_lane = tile + (8 * qv + (iv >> 1)) * MV_PITCH + 8 * (iv & 1);
     // D tile jd (dims 16 jd ..): lane (qv, iv) holds rows 4 qv .. 4 qv + 3 of dim
     // 16 jd + iv of its table, rows m = 8 (group % 2) + 2 head + part; heads ha, ha + 1
@@ -1636,7 +1651,7 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
         bf16x8 aw[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          aw[t] = *reinterpret_cast<const bf16x8*>(atb + t * MV_TBL + hh * 4 * MV_TSTR);
+          aw[t] = lds_tr16x2(atb + t * MV_TBL + hh * 1024 + a_r0, atb + t * MV_TBL + hh * 1024 + a_r1);
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) {
           // B: the codes of tokens 8 g8 + 0 .. 7, dim 16 jd + iv, as bf16 (exact; K8V4:
