@@ -1335,12 +1335,16 @@ void k_decode_pair_mv(const kv_session* __restrict__ tab, const int32_t* __restr
   // Step sb + i of a wave, sb a multiple of 8 (so of SP) and i < 8, is its step sb
   // plus step_g(0, i): the lane's part of the step (step i = lane / 8 of the 8 that
   // start at sb) is one constant, the rest wave-uniform.
+  // step_g grows with the step, so steps past the wave's last (masked tokens) clamp to
+  // that step's rows, which the wave reads anyway.
   const int lane_step = step_g<SP>(0, lane >> 3, W);
+  const int step_last = step_g<SP>(gw, kmax, W);
   auto chunk_row = [&](int ch, int bl) __attribute__((always_inline)) {
     const int st = ch * CHK + bl * 8 + (lane >> 3);
     if constexpr (PG != 0) return pm.lane_row(pm.block(ch * CHK + bl * 8), st, gw, W, lane & 7);
-    // steps past the wave's own (masked tokens) read any row of the session
-    else return (uint32_t)min((step_g<SP>(gw, ch * CHK + bl * 8, W) + lane_step) * 8 + (lane & 7), len - 1);
+    else
+      return (uint32_t)min(
+          min(step_g<SP>(gw, ch * CHK + bl * 8, W) + lane_step, step_last) * 8 + (lane & 7), len - 1);
   };
 
   if (kw) {
