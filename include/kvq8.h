@@ -146,6 +146,8 @@ size_t kv_decode_workspace_bytes(const kv_shape* h_shape, int n_sess, int max_le
  *   out[b][q] = sum_t softmax_t(sm_scale * q . K[h][t]) V[h][t],  t < d_len[b],
  * with K, V the dequantised cache values (code * scale, exact in fp32, or the
  * fp16 values).  Partials of each split of the context are merged by log-sum-exp.
+ * Softmax weights come from the hardware fp32 exp2 of the logit (in base 2) minus a
+ * running maximum; a weight below 2^-126 of that maximum counts as 0.
  * d_len[b] == 0 gives a zero row.  Arithmetic:
  *   F16: fp16 values widened to fp32; dot products, softmax and sums in fp32.
  *   int8 K (Q8, K8V4): the scaled query is split per 64-dim group into three int8
