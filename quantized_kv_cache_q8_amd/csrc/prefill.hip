@@ -21,7 +21,8 @@
 // K and V tiles go from global memory straight to LDS (global_load_lds_dwordx4: a
 // wave's instruction fills 1 KB, lane L the 16-byte slot L), both row-major (a key
 // per 256-byte row) with the 16-byte chunks of row r XOR-swizzled by r mod 16, so the
-// fragment reads spread over the banks.  K fragments are 16-byte reads; V^T
+// K fragment reads touch every bank once (the V^T reads below meet two-way bank
+// conflicts; a swizzle without them timed the same).  K fragments are 16-byte reads; V^T
 // fragments come from two transposing reads (ds_read_b64_tr_b16: within 16 lanes,
 // lane i receives element i mod 4 of the 8-byte pieces addressed by lanes 4e + i / 4,
 // e = 0 .. 3, so 16 lanes addressing 4 keys x 16 dims each receive one dim of the 4
